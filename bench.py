@@ -1,0 +1,241 @@
+"""Benchmark of the FP32 GEMM (C = A @ B, row-major, AB only) on one MI355X.
+
+Prints ONE JSON line on stdout: FP32 SGEMM TFLOP/s (2*M*N*K / t) of the
+headline 4096^3 workload (or --workload), with inputs resident in HBM, K
+back-to-back calls timed between two device synchronisations, plus:
+  * "roofline": per-launch kernel time from HIP events recorded on the
+    launch stream, against the MI355X FP32 matrix peak (157.3 TFLOP/s);
+  * "cpu_baseline": the FP64 CPU oracle timed on a bounded row sample of the
+    same product, on this host's cores.
+Details (every workload with --all, cold-cache timings, the plan, a
+torch.matmul context figure) go to stderr and to --detail FILE.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
+                       [--config N] [--sched N] [--all] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+PEAK_FP32_TFLOPS = 157.3          # MI355X dense FP32 (vector with packed FMA, or matrix)
+PEAK_HBM_GBS = 8000.0
+# The pages' own kernel at 4096^3 on an H100 (context, other hardware): "Beyond
+# Kernel 7", section "The confirmed result", k13f 2761.2 us = 49.8 TFLOP/s.
+PAGES_4096_TFLOPS = 49.8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--config", type=int, default=0)
+    ap.add_argument("--sched", type=int, default=0)
+    ap.add_argument("--all", action="store_true", help="also time every workload (details only)")
+    ap.add_argument("--cold", action="store_true", help="also time with caches flushed before each call")
+    ap.add_argument("--torch", action="store_true", help="also time torch.matmul (context)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--detail", default=None, help="write a detail JSON file")
+    return ap.parse_args()
+
+
+def ensure_library():
+    import fp32_sgemm_f32_amd as sg
+    if not os.path.exists(sg.LIB_PATH):
+        from fp32_sgemm_f32_amd import build
+        build.build()
+    sg.library()
+    return sg
+
+
+def time_calls(fn, stream, steps, warmup, flush=None):
+    """Per-call HIP-event times (ms) on `stream`, plus the total wall of the
+    back-to-back run between two synchronisations."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return per, wall
+
+
+def bench_workload(sg, w, args, dev, stream, cold=False, with_torch=False):
+    import torch
+    A, B = workloads.generate_workload(w)
+    Ad = torch.from_numpy(A).to(dev)
+    Bd = torch.from_numpy(B).to(dev)
+    Cd = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    del A, B
+
+    def call():
+        st = sg.sgemm_raw(w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), w.N, Cd.data_ptr(), w.N,
+                          stream.cuda_stream, args.config, args.sched)
+        if st != sg.OK:
+            raise sg.SgemmError(st)
+
+    # Sanity check before timing (the parity proof is the test suite): a
+    # sample of rows against an FP64 product on the device.
+    with torch.cuda.stream(stream):
+        call()
+    torch.cuda.synchronize()
+    rows = torch.arange(0, w.M, max(1, w.M // 64), device=dev)
+    ref = Ad[rows].double() @ Bd.double()
+    scale = Ad[rows].double().abs() @ Bd.double().abs()
+    err = (Cd[rows].double() - ref).abs()
+    sane = bool(torch.all(err <= 1e-5 * scale).item()) and bool(torch.isfinite(Cd).all().item())
+    del ref, scale, err
+
+    with torch.cuda.stream(stream):
+        per, wall = time_calls(call, stream, args.steps, args.warmup)
+    flops = w.flops
+    res = {
+        "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist, "seed": w.seed,
+        "sane": sane,
+        "steps": args.steps, "warmup": args.warmup,
+        "wall_s": wall,
+        "ms_per_step": wall / args.steps * 1e3,
+        "tflops": flops * args.steps / wall / 1e12,
+        "event_ms_median": statistics.median(per),
+        "event_ms_mean": statistics.fmean(per),
+        "event_ms_min": min(per),
+        "event_ms_p90": float(np.percentile(per, 90)),
+        "tflops_median": flops / (statistics.median(per) * 1e-3) / 1e12,
+        "plan": sg.plan(w.M, w.N, w.K, args.config, args.sched,
+                        num_cus=torch.cuda.get_device_properties(dev).multi_processor_count),
+    }
+    if cold:
+        flush_buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        with torch.cuda.stream(stream):
+            per_c, _ = time_calls(call, stream, max(20, args.steps // 2), 3,
+                                  flush=lambda: flush_buf.fill_(1.0))
+        res["cold_event_ms_median"] = statistics.median(per_c)
+        res["cold_tflops_median"] = flops / (statistics.median(per_c) * 1e-3) / 1e12
+        del flush_buf
+    if with_torch:
+        torch.backends.cuda.matmul.allow_tf32 = False
+        out = torch.empty_like(Cd)
+        with torch.cuda.stream(stream):
+            per_t, _ = time_calls(lambda: torch.matmul(Ad, Bd, out=out), stream, args.steps, args.warmup)
+        res["torch_matmul_event_ms_median"] = statistics.median(per_t)
+        res["torch_matmul_tflops_median"] = flops / (statistics.median(per_t) * 1e-3) / 1e12
+    del Ad, Bd, Cd
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, budget_s):
+    """The FP64 oracle on the first rows of the same product, until about
+    budget_s seconds of work; returns the TFLOP/s it sustains (2*rows*N*K per s)."""
+    import oracle
+    threads = oracle.default_threads()
+    A, B = workloads.generate_workload(w)
+    oracle._load()
+    rows_done, spent = 0, 0.0
+    step = max(threads, 32)
+    while rows_done < w.M and spent < budget_s:
+        r1 = min(w.M, rows_done + step)
+        t0 = time.perf_counter()
+        oracle.gemm(A[rows_done:r1], B, threads=threads)
+        spent += time.perf_counter() - t0
+        rows_done = r1
+    value = 2.0 * rows_done * w.N * w.K / spent / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows_done - 1} of the {w.M}x{w.N}x{w.K} product "
+                      f"({rows_done}x{w.N} outputs, full K), FP64 triple loop (also forms "
+                      f"sum|a*b|), {spent:.1f} s on {threads} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this GEMM has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    sg = ensure_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name}, {props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB")
+
+    w = workloads.WORKLOADS[args.workload]
+    head = bench_workload(sg, w, args, dev, stream, cold=args.cold, with_torch=args.torch)
+    log(json.dumps(head))
+    detail = {"headline": head, "device": props.name, "cus": props.multi_processor_count}
+    if args.all:
+        rest = []
+        for name, ww in workloads.WORKLOADS.items():
+            if name == w.name:
+                continue
+            r = bench_workload(sg, ww, args, dev, stream, cold=args.cold, with_torch=args.torch)
+            log(json.dumps(r))
+            rest.append(r)
+        detail["others"] = rest
+
+    achieved = w.flops / (head["event_ms_mean"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": None}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(json.dumps(cpu))
+    cfg_name = sg.CFG_NAMES[head["plan"]["config"]]
+    line = {
+        "metric": "FP32 SGEMM TFLOPS (2MNK/s)",
+        "value": round(head["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(head["tflops"] / PAGES_4096_TFLOPS, 3) if w.name == "sgemm_4096" else None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist, "seed": w.seed,
+                   "kernel": cfg_name, "sched": sg.SCHED_NAMES[head["plan"]["sched"]],
+                   "grid": head["plan"]["grid"], "parallelism": "single-gpu"},
+        "frac_of_fp32_peak": round(head["tflops"] / PEAK_FP32_TFLOPS, 4),
+        "median_event_tflops": round(head["tflops_median"], 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sane": head["sane"],
+    }
+    if args.detail:
+        detail["line"] = line
+        with open(args.detail, "w") as f:
+            json.dump(detail, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

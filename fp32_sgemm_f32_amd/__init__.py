@@ -1,0 +1,177 @@
+"""Python binding of libsgemm_f32 (include/sgemm_f32.h): FP32 GEMM C = A @ B.
+
+Argument marshalling only: every step of the product runs in the HIP
+library.  If the library has not been built, importing succeeds but every
+call raises (there is no fallback of any kind).  PyTorch is used only to
+hold device memory and to name the current HIP stream.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsgemm_f32.so")
+
+# Status codes (SGEMM_*).
+OK = 0
+ERR_SHAPE = 1
+ERR_LD = 2
+ERR_ALIGN = 3
+ERR_NULL = 4
+ERR_ALIAS = 5
+ERR_HIP = 6
+ERR_POINTER = 7
+ERR_CONFIG = 8
+
+# Kernel configurations (SGEMM_CFG_*).
+CFG_AUTO = 0
+CFG_MFMA_256x256x16 = 1
+CFG_MFMA_128x128x32 = 2
+CFG_MFMA_256x256x32 = 3
+CFG_MFMA_256x128x32 = 4
+CFG_VALU_128x128x8 = 5
+NUM_CFGS = 6
+CFG_NAMES = {
+    CFG_AUTO: "auto",
+    CFG_MFMA_256x256x16: "mfma_256x256x16",
+    CFG_MFMA_128x128x32: "mfma_128x128x32",
+    CFG_MFMA_256x256x32: "mfma_256x256x32",
+    CFG_MFMA_256x128x32: "mfma_256x128x32",
+    CFG_VALU_128x128x8: "valu_128x128x8",
+}
+
+# Schedules (SGEMM_SCHED_*).
+SCHED_AUTO = 0
+SCHED_DP = 1
+SCHED_STREAMK = 2
+SCHED_NAMES = {SCHED_AUTO: "auto", SCHED_DP: "dp", SCHED_STREAMK: "streamk"}
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status, where="sgemm_f32"):
+        self.status = status
+        hip = last_hip_error() if status == ERR_HIP else 0
+        msg = f"{where}: status {status} ({status_string(status)})"
+        if hip:
+            msg += f", hipError {hip}"
+        super().__init__(msg)
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "config", "sched", "tile_m", "tile_n", "tile_k", "threads", "tiles_m", "tiles_n",
+        "iters_per_tile", "dp_tiles", "sk_tiles", "grid", "sk_grid", "xcd_remap", "group_m")] + [
+        ("sk_iters", ctypes.c_longlong), ("workspace_bytes", ctypes.c_longlong)]
+
+
+_lib = None
+
+
+def library():
+    """The loaded ctypes library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python fp32_sgemm_f32_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i, p, vp = ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+    lib.sgemm_f32.restype = i
+    lib.sgemm_f32.argtypes = [i, i, i, p, i, p, i, p, i, vp]
+    lib.sgemm_f32_ex.restype = i
+    lib.sgemm_f32_ex.argtypes = [i, i, i, p, i, p, i, p, i, vp, i, i]
+    lib.sgemm_f32_granule.restype = None
+    lib.sgemm_f32_granule.argtypes = [ctypes.POINTER(i)] * 3
+    lib.sgemm_f32_status_string.restype = ctypes.c_char_p
+    lib.sgemm_f32_status_string.argtypes = [i]
+    lib.sgemm_f32_last_hip_error.restype = i
+    lib.sgemm_f32_last_hip_error.argtypes = []
+    lib.sgemm_f32_plan.restype = i
+    lib.sgemm_f32_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(_Plan)]
+    lib.sgemm_f32_release.restype = i
+    lib.sgemm_f32_release.argtypes = []
+    _lib = lib
+    return lib
+
+
+def granule():
+    """(gm, gn, gk): M, N, K must be multiples of these."""
+    g = [ctypes.c_int() for _ in range(3)]
+    library().sgemm_f32_granule(*[ctypes.byref(x) for x in g])
+    return tuple(x.value for x in g)
+
+
+def status_string(status: int) -> str:
+    return library().sgemm_f32_status_string(int(status)).decode()
+
+
+def last_hip_error() -> int:
+    return library().sgemm_f32_last_hip_error()
+
+
+def release() -> None:
+    st = library().sgemm_f32_release()
+    if st != OK:
+        raise SgemmError(st, "sgemm_f32_release")
+
+
+def plan(M, N, K, config=CFG_AUTO, sched=SCHED_AUTO, num_cus=256, occupancy=None) -> dict:
+    """The launch plan for a shape (host computation only, no GPU needed)."""
+    occ = None
+    if occupancy is not None:
+        if len(occupancy) != NUM_CFGS:
+            raise ValueError(f"occupancy needs {NUM_CFGS} entries")
+        occ = (ctypes.c_int * NUM_CFGS)(*occupancy)
+    out = _Plan()
+    st = library().sgemm_f32_plan(M, N, K, config, sched, num_cus, occ, ctypes.byref(out))
+    if st != OK:
+        raise SgemmError(st, "sgemm_f32_plan")
+    return {name: getattr(out, name) for name, _ in _Plan._fields_}
+
+
+def sgemm_raw(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream=0,
+              config=CFG_AUTO, sched=SCHED_AUTO) -> int:
+    """Direct call with integer device addresses; returns the status code."""
+    lib = library()
+    if config == CFG_AUTO and sched == SCHED_AUTO:
+        return lib.sgemm_f32(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream)
+    return lib.sgemm_f32_ex(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream, config, sched)
+
+
+def _row_major_ld(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major (unit column stride)")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def matmul(A, B, out=None, config=CFG_AUTO, sched=SCHED_AUTO, stream=None):
+    """C = A @ B for float32 CUDA (HIP) tensors, on the current (or given) stream.
+
+    A: (M, K), B: (K, N), row-major (unit column stride; padded rows allowed).
+    Returns `out` (allocated if None).  Raises SgemmError on a library error.
+    """
+    import torch
+
+    for t, n in ((A, "A"), (B, "B")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda:
+            raise TypeError(f"{n} must be a float32 tensor on a HIP device")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or out.device != A.device:
+        raise ValueError("out must be float32 (M, N) on A's device")
+    lda, ldb, ldc = _row_major_ld(A, "A"), _row_major_ld(B, "B"), _row_major_ld(out, "out")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device)
+    with torch.cuda.device(A.device):
+        st = sgemm_raw(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc,
+                       stream.cuda_stream, config, sched)
+    if st != OK:
+        raise SgemmError(st)
+    return out

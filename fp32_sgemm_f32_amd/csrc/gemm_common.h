@@ -1,0 +1,155 @@
+// Device-side pieces shared by every kernel configuration: the kernel
+// argument block, the workgroup -> work mapping (data-parallel tiles first,
+// then the Stream-K share), and the deterministic partial-tile fixup.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgemm {
+
+// Native 4-wide vector (one 128-bit load/store).  Arrays of it are promoted to
+// registers, unlike arrays of HIP's float4 struct.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Passed by value to every GEMM kernel.  Row-major A (M x K), B (K x N),
+// C (M x N) with leading dimensions in elements.
+struct KernelArgs {
+    const float *A;
+    const float *B;
+    float *C;
+    int64_t lda, ldb, ldc;
+    int tiles_m, tiles_n;
+    int ipt;          // K chunks per tile
+    int dp_tiles;     // tiles [0, dp_tiles) are computed whole
+    int sk_tiles;     // tiles [dp_tiles, dp_tiles + sk_tiles) are K-split
+    int grid;         // workgroups launched
+    int sk_grid;      // logical workgroups [0, sk_grid) share the split tiles
+    int xcd_remap;    // remap blockIdx so each XCD owns a contiguous run of work
+    int group_m;      // tile order: groups of group_m tile rows
+    int64_t sk_iters; // sk_tiles * ipt
+    int *counters;    // [sk_tiles] arrival counters, zero between calls
+    float *partials;  // [sk_grid][2][tile floats] partial tiles
+};
+
+// Workgroups are handed to the 8 XCDs round-robin by blockIdx.  With the
+// remap, XCD x runs logical ids [x*grid/8, (x+1)*grid/8): neighbouring tiles
+// (and the K-split pieces of one tile) land on one XCD and share its L2.
+__device__ __forceinline__ int logical_wg(const KernelArgs &a) {
+    int w = (int)blockIdx.x;
+    if (a.xcd_remap) {
+        const int per = a.grid >> 3;
+        w = (w & 7) * per + (w >> 3);
+    }
+    return w;
+}
+
+// Tile id -> (tile row, tile column): groups of group_m tile rows, walked
+// down each column of the group before moving right.
+__device__ __forceinline__ void tile_coords(const KernelArgs &a, int t, int &tm, int &tn) {
+    const int gsz = a.group_m * a.tiles_n;
+    const int g = t / gsz;
+    const int first = g * a.group_m;
+    int rows = a.tiles_m - first;
+    if (rows > a.group_m) rows = a.group_m;
+    const int r = t - g * gsz;
+    tm = first + r % rows;
+    tn = r / rows;
+}
+
+// Stream-K partition of the sk_iters (tile, K chunk) steps over sk_grid
+// workgroups: workgroup w owns [begin(w), begin(w + 1)).  The planner keeps
+// sk_grid <= sk_iters (every owner has at least one step) and
+// (sk_iters + 1) * sk_grid < 2^31, so 32-bit arithmetic is exact here.
+__device__ __forceinline__ int sk_begin(const KernelArgs &a, int w) {
+    return (int)((uint32_t)w * (uint32_t)a.sk_iters / (uint32_t)a.sk_grid);
+}
+
+// The workgroup whose range holds step i.
+__device__ __forceinline__ int sk_owner(const KernelArgs &a, int i) {
+    return (int)(((uint32_t)(i + 1) * (uint32_t)a.sk_grid - 1u) / (uint32_t)a.sk_iters);
+}
+
+// Partial slot of workgroup w for split tile tl: 0 if tl is the tile its
+// range starts in, else 1 (its range can only leave a partial in its first
+// and its last tile).
+__device__ __forceinline__ int sk_slot(const KernelArgs &a, int w, int tl) {
+    return sk_begin(a, w) / a.ipt == tl ? 0 : 1;
+}
+
+template <int TILE_FLOATS>
+__device__ __forceinline__ float *partial_ptr(const KernelArgs &a, int w, int slot) {
+    return a.partials + ((int64_t)w * 2 + slot) * TILE_FLOATS;
+}
+
+// Runs one workgroup's share of the GEMM with the given core.  The core
+// provides:
+//   zero()                          accumulators := 0
+//   mainloop(a, lds, tm, tn, k0, k1) accumulate K chunks [k0, k1) of tile (tm, tn)
+//   store_c(a, tm, tn)              write the accumulators to C
+//   store_partial(p) / add_partial(p)  thread-private copy to/from a partial tile
+//
+// SPLIT = false is the whole-tile-only instance (sk_tiles == 0): it carries
+// none of the split bookkeeping, which keeps its register allocation to the
+// main loop's needs.
+template <class Core, bool SPLIT>
+__device__ __forceinline__ void run_gemm(const KernelArgs &a, float *lds, int *flag) {
+    Core core;
+    const int w = logical_wg(a);
+
+    for (int t = w; t < a.dp_tiles; t += a.grid) {
+        int tm, tn;
+        tile_coords(a, t, tm, tn);
+        core.zero();
+        core.mainloop(a, lds, tm, tn, 0, a.ipt);
+        core.store_c(a, tm, tn);
+    }
+    if (!SPLIT || w >= a.sk_grid) return;
+
+    int s = sk_begin(a, w);
+    const int e = sk_begin(a, w + 1);
+    while (s < e) {
+        // Uniform bookkeeping first, while the accumulators are not yet live.
+        const int tl = __builtin_amdgcn_readfirstlane(s / a.ipt);   // split-tile index
+        const int k0 = s - tl * a.ipt;
+        const int k1 = k0 + (e - s < a.ipt - k0 ? e - s : a.ipt - k0);
+        const int first = __builtin_amdgcn_readfirstlane(sk_owner(a, tl * a.ipt));
+        const int last = __builtin_amdgcn_readfirstlane(sk_owner(a, (tl + 1) * a.ipt - 1));
+        int tm, tn;
+        tile_coords(a, a.dp_tiles + tl, tm, tn);
+        core.zero();
+        core.mainloop(a, lds, tm, tn, k0, k1);
+
+        if (first == last) {
+            core.store_c(a, tm, tn);
+        } else {
+            // Every contributor leaves its partial; the last to arrive sums
+            // all partials in contributor order (a fixed order, so the result
+            // does not depend on arrival order) and writes C.  Nobody waits
+            // for anybody, and the counter is reset for the next call.
+            core.store_partial(partial_ptr<Core::TILE_FLOATS>(a, w, sk_slot(a, w, tl)));
+            __threadfence();
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const int old = __hip_atomic_fetch_add(&a.counters[tl], 1, __ATOMIC_ACQ_REL,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+                *flag = (old == last - first) ? 1 : 0;
+            }
+            __syncthreads();
+            const int is_last = __builtin_amdgcn_readfirstlane(*flag);
+            if (is_last) {
+                __threadfence();
+                core.zero();
+                for (int c = first; c <= last; ++c)
+                    core.add_partial(partial_ptr<Core::TILE_FLOATS>(a, c, sk_slot(a, c, tl)));
+                core.store_c(a, tm, tn);
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(&a.counters[tl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();   // *flag is reused by the next split tile
+        }
+        s += k1 - k0;
+    }
+}
+
+}  // namespace sgemm

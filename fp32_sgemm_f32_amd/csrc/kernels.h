@@ -1,0 +1,19 @@
+// Host-callable launchers of the GEMM kernels (one per source file).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "sgemm_f32.h"
+
+namespace sgemm {
+
+struct KernelArgs;
+
+hipError_t launch_mfma(int cfg, const KernelArgs &a, hipStream_t s);
+hipError_t occupancy_mfma(int cfg, int *wg_per_cu);
+hipError_t launch_valu(int cfg, const KernelArgs &a, hipStream_t s);
+hipError_t occupancy_valu(int cfg, int *wg_per_cu);
+hipError_t launch_fill_zero(float *C, int M, int N, int64_t ldc, hipStream_t s);
+
+}  // namespace sgemm

@@ -1,0 +1,138 @@
+// Launch planning: which kernel configuration runs a shape, and how its
+// output tiles and K chunks are spread over the workgroups.
+//
+// Scheduling follows the persistent Stream-K scheme described on "Beyond
+// Kernel 7: Closing the Gap to cuBLAS on an H100 FP32 GEMM", section
+// "Kernel 14 and Stream-K": the work is the stream of (output tile, K chunk)
+// steps; whole tiles are handed out in full waves first, and only the tiles
+// left over are split, evenly, over a grid of resident workgroups.  Tile
+// counts that fill whole waves run purely data-parallel (one workgroup per
+// tile), which is the plain tiling of the other pages.
+#include "plan.h"
+
+#include "sgemm_f32.h"
+
+namespace sgemm {
+
+const CfgInfo kCfgs[] = {
+    {SGEMM_CFG_AUTO, 0, 0, 0, 0, false, 0, "auto"},
+    {SGEMM_CFG_MFMA_256x256x16, 256, 256, 16, 512, true, 1, "mfma_256x256x16"},
+    {SGEMM_CFG_MFMA_128x128x32, 128, 128, 32, 256, true, 2, "mfma_128x128x32"},
+    {SGEMM_CFG_MFMA_256x256x32, 256, 256, 32, 256, true, 1, "mfma_256x256x32"},
+    {SGEMM_CFG_MFMA_256x128x32, 256, 128, 32, 256, true, 1, "mfma_256x128x32"},
+    {SGEMM_CFG_VALU_128x128x8, 128, 128, 8, 256, false, 2, "valu_128x128x8"},
+};
+const int kNumCfgs = SGEMM_NUM_CFGS;
+
+static_assert(sizeof(kCfgs) / sizeof(kCfgs[0]) == SGEMM_NUM_CFGS, "config table size");
+
+int64_t workspace_bytes(int grid, int sk_tiles, int bm, int bn) {
+    if (sk_tiles <= 0) return 0;
+    int64_t counters = ((int64_t)sk_tiles * 4 + 255) / 256 * 256;
+    return counters + (int64_t)grid * 2 * bm * bn * 4;
+}
+
+static bool fits(const CfgInfo &c, int M, int N, int K) {
+    return M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0;
+}
+
+static int occ_of(const PlanRequest &r, int cfg) {
+    int o = r.occupancy ? r.occupancy[cfg] : kCfgs[cfg].default_occ;
+    return o > 0 ? o : 1;
+}
+
+// Tile-order grouping for a run of R consecutive tiles (one XCD's share):
+// groups of g tile rows, walked column by column, so that a run covers about
+// g rows x R/g columns; g minimises the panels touched, g + R/g.
+static int pick_group_m(int tiles_m, int run) {
+    int best = 1, best_cost = 1 + run;
+    for (int g = 2; g <= tiles_m && g <= run; g *= 2) {
+        if (tiles_m % g) continue;
+        int cost = g + (run + g - 1) / g;
+        if (cost < best_cost) { best = g; best_cost = cost; }
+    }
+    return best;
+}
+
+int make_plan(const PlanRequest &req, Plan *out) {
+    const int M = req.M, N = req.N, K = req.K;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SHAPE;
+    if (M % kGranM || N % kGranN || K % kGranK) return SGEMM_ERR_SHAPE;
+    if (req.config < 0 || req.config >= kNumCfgs) return SGEMM_ERR_CONFIG;
+    if (req.sched < SGEMM_SCHED_AUTO || req.sched > SGEMM_SCHED_STREAMK) return SGEMM_ERR_CONFIG;
+    const int cus = req.num_cus > 0 ? req.num_cus : 1;
+
+    int cfg = req.config;
+    if (cfg == SGEMM_CFG_AUTO) {
+        // Largest matrix-core tile that still gives every CU a tile; else
+        // the 128x128 tile, split along K when there are too few tiles.
+        const CfgInfo &big = kCfgs[SGEMM_CFG_MFMA_256x256x16];
+        if (fits(big, M, N, K) && (int64_t)(M / big.bm) * (N / big.bn) >= cus)
+            cfg = SGEMM_CFG_MFMA_256x256x16;
+        else
+            cfg = SGEMM_CFG_MFMA_128x128x32;
+    }
+    const CfgInfo &c = kCfgs[cfg];
+    if (!fits(c, M, N, K)) return SGEMM_ERR_CONFIG;
+
+    Plan p{};
+    p.config = cfg;
+    p.bm = c.bm; p.bn = c.bn; p.bk = c.bk; p.threads = c.threads;
+    p.tiles_m = M / c.bm;
+    p.tiles_n = N / c.bn;
+    p.ipt = K / c.bk;
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int occ = occ_of(req, cfg);
+    const int sk_per_cu = req.sk_wg_per_cu > 0 ? req.sk_wg_per_cu : occ;
+    const int cap = cus * sk_per_cu;
+
+    int sched = req.sched;
+    if (tiles == 0 || p.ipt == 0) sched = SGEMM_SCHED_DP;  // nothing to split
+    if (sched == SGEMM_SCHED_AUTO) {
+        if (tiles >= cus && tiles % cus == 0) sched = SGEMM_SCHED_DP;
+        else sched = SGEMM_SCHED_STREAMK;
+    }
+
+    if (sched == SGEMM_SCHED_DP) {
+        p.dp_tiles = tiles;
+        p.sk_tiles = 0;
+        p.sk_grid = 0;
+        p.grid = tiles;
+    } else {
+        // Whole tiles in full waves first, the remainder split.  The split
+        // part runs on the first sk_grid logical workgroups, each owning a
+        // contiguous run of at least kMinSkIters (tile, K chunk) steps when
+        // there are that many.
+        int dp = req.sched == SGEMM_SCHED_STREAMK ? 0 : (tiles / cap) * cap;
+        p.dp_tiles = dp;
+        p.sk_tiles = tiles - dp;
+        int64_t sk_iters = (int64_t)p.sk_tiles * p.ipt;
+        int64_t g = sk_iters / kMinSkIters;
+        if (g > cap) g = cap;
+        if (g < 1) g = 1;
+        if (sk_iters == 0) g = 0;
+        p.sk_grid = (int)g;
+        p.grid = dp > 0 ? cap : (int)g;
+        // The kernel's split bookkeeping is 32-bit; beyond that range run
+        // whole tiles only.
+        if ((sk_iters + 1) * g >= ((int64_t)1 << 31)) {
+            p.dp_tiles = tiles;
+            p.sk_tiles = 0;
+            p.sk_grid = 0;
+            p.grid = tiles;
+        }
+    }
+    p.sk_iters = (int64_t)p.sk_tiles * p.ipt;
+    p.sched = p.sk_tiles > 0 ? SGEMM_SCHED_STREAMK : SGEMM_SCHED_DP;
+    p.xcd_remap = (p.grid >= 8 && p.grid % 8 == 0) ? 1 : 0;
+    int run = p.xcd_remap ? p.grid / 8 : p.grid;
+    if (run < 1) run = 1;
+    p.group_m = pick_group_m(p.tiles_m > 0 ? p.tiles_m : 1, run);
+    p.workspace_bytes = workspace_bytes(p.sk_grid, p.sk_tiles, p.bm, p.bn);
+    p.counters_offset = 0;
+    p.partials_offset = p.sk_tiles > 0 ? ((int64_t)p.sk_tiles * 4 + 255) / 256 * 256 : 0;
+    *out = p;
+    return SGEMM_OK;
+}
+
+}  // namespace sgemm

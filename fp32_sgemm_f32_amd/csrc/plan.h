@@ -1,0 +1,60 @@
+// Host-side launch planning for sgemm_f32: configuration choice, tile grid,
+// and the data-parallel / Stream-K split.  Pure C++ with no HIP dependency so
+// that it runs (and is tested) on a machine without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace sgemm {
+
+struct CfgInfo {
+    int id;
+    int bm, bn, bk;     // output tile and K chunk
+    int threads;        // threads per workgroup
+    bool mfma;          // matrix-core FP32 product (else scalar VALU FMAs)
+    int default_occ;    // workgroups per CU expected from its LDS/VGPR use
+    const char *name;
+};
+
+// Indexed by SGEMM_CFG_* (entry 0 is a placeholder for AUTO).
+extern const CfgInfo kCfgs[];
+extern const int kNumCfgs;
+
+// Shape granule accepted by the library: every configuration's tile divides
+// multiples of 256 in M and N; the planner only picks configurations whose
+// tile divides the actual shape.
+constexpr int kGranM = 128, kGranN = 128, kGranK = 32;
+
+// Smallest number of K chunks a Stream-K workgroup should own.
+constexpr int kMinSkIters = 2;
+
+struct PlanRequest {
+    int M, N, K;
+    int config;          // SGEMM_CFG_*
+    int sched;           // SGEMM_SCHED_*
+    int num_cus;
+    const int *occupancy;  // [kNumCfgs] or nullptr
+    int sk_wg_per_cu;    // Stream-K grid = num_cus * this (0: occupancy)
+};
+
+struct Plan {
+    int config, sched;
+    int bm, bn, bk, threads;
+    int tiles_m, tiles_n, ipt;
+    int dp_tiles, sk_tiles, grid, sk_grid;
+    int xcd_remap, group_m;
+    int64_t sk_iters;
+    int64_t workspace_bytes;
+    int64_t counters_offset, partials_offset;   // within the workspace
+};
+
+// Returns an SGEMM_* status; fills *out on success.
+int make_plan(const PlanRequest &req, Plan *out);
+
+// Workspace layout for Stream-K: sk_tiles int counters (256-byte aligned
+// block), then sk_grid * 2 partial tiles of bm*bn floats (a split workgroup
+// leaves a partial for at most two tiles: the first and the last it touches).
+int64_t workspace_bytes(int grid, int sk_tiles, int bm, int bn);
+
+}  // namespace sgemm

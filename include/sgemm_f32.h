@@ -1,0 +1,152 @@
+/*
+ * sgemm_f32: single-precision GEMM C = A * B for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Beyond Kernel 7: Closing the Gap to cuBLAS on an H100
+ * FP32 GEMM", section "The operation: GEMM and the precision of the
+ * comparison"): for row-major FP32 matrices A (M x K) and B (K x N),
+ *
+ *     C[m][n] = sum over k of A[m][k] * B[k][n]        (AB only: no alpha/beta)
+ *
+ * with FP32 inputs and FP32 arithmetic throughout (fused multiply-adds, one
+ * rounding each; no reduced-precision input rounding of any kind).  Shapes
+ * are restricted to multiples of the tile granule, as on that page.
+ *
+ * Memory and ownership
+ *   A, B, C are device pointers, caller-owned, allocated on the HIP device
+ *   that is current when the call is made.  The library never frees or keeps
+ *   them.  Layout is row-major with leading dimensions:
+ *       A[m * lda + k],  B[k * ldb + n],  C[m * ldc + n].
+ *   Only the logical M x N region of C is written; the ldc padding is left
+ *   untouched.  C is overwritten, never read.  C must not overlap A or B.
+ *
+ * Asynchrony
+ *   Every call only enqueues work on `stream` (0 = the null stream) and
+ *   returns without synchronising the host.  Faults during execution surface
+ *   at the caller's next synchronisation, as usual for HIP.
+ *
+ * Errors
+ *   Arguments are fully checked before anything is enqueued, so on any error
+ *   C is untouched.  Return values are the SGEMM_* status codes below.
+ *
+ * Workspace
+ *   Split-K ("Stream-K") schedules keep partial tiles and per-tile arrival
+ *   counters in a workspace owned by the library, one per (device, stream),
+ *   grown on demand with hipMalloc and kept until sgemm_f32_release() or
+ *   process exit.  Calls on different streams therefore never share one.
+ *   Calls that run concurrently on the SAME stream are impossible by stream
+ *   order; calls from several host threads on one stream are serialised by
+ *   the stream as well.
+ */
+#ifndef SGEMM_F32_H
+#define SGEMM_F32_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SGEMM_OK            0  /* success (also for M == 0 or N == 0: nothing to do) */
+#define SGEMM_ERR_SHAPE     1  /* M, N or K negative or not a multiple of the granule */
+#define SGEMM_ERR_LD        2  /* lda < K, ldb < N or ldc < N */
+#define SGEMM_ERR_ALIGN     3  /* a pointer not 16-byte aligned, or an ld not a multiple of 4 */
+#define SGEMM_ERR_NULL      4  /* a required pointer is NULL */
+#define SGEMM_ERR_ALIAS     5  /* the C region overlaps the A or B region */
+#define SGEMM_ERR_HIP       6  /* a HIP runtime call failed: see sgemm_f32_last_hip_error() */
+#define SGEMM_ERR_POINTER   7  /* a pointer is not device memory of the current device, or
+                                  the matrix extent runs past the end of its allocation */
+#define SGEMM_ERR_CONFIG    8  /* unknown kernel configuration/schedule, or one whose tile
+                                  does not divide this shape */
+
+/* Kernel configurations (sgemm_f32_ex / sgemm_f32_plan).  "MFMA" configs
+ * run the product on the FP32 matrix cores (v_mfma_f32_32x32x2_f32: full
+ * FP32 inputs, FP32 accumulation); the "VALU" config runs it as a
+ * register-tiled outer product of scalar FP32 fused multiply-adds. */
+#define SGEMM_CFG_AUTO              0
+#define SGEMM_CFG_MFMA_256x256x16   1  /* 512 threads, 8 waves of 64x128 */
+#define SGEMM_CFG_MFMA_128x128x32   2  /* 256 threads, 4 waves of 64x64  */
+#define SGEMM_CFG_MFMA_256x256x32   3  /* 256 threads, 4 waves of 128x128 */
+#define SGEMM_CFG_MFMA_256x128x32   4  /* 256 threads, 4 waves of 128x64 */
+#define SGEMM_CFG_VALU_128x128x8    5  /* 256 threads, 8x8 outputs per lane */
+#define SGEMM_NUM_CFGS              6  /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
+
+/* Schedules. */
+#define SGEMM_SCHED_AUTO     0  /* whole tiles in full waves, Stream-K for the rest */
+#define SGEMM_SCHED_DP       1  /* one workgroup per output tile, full K each */
+#define SGEMM_SCHED_STREAMK  2  /* every tile's K range split evenly over a resident grid */
+
+/*
+ * C = A * B.  Requirements: M, N multiples of gm, K a multiple of gk, where
+ * sgemm_f32_granule() gives (gm, gn, gk); lda >= K, ldb >= N, ldc >= N, all
+ * multiples of 4; A, B, C 16-byte aligned device pointers.  K == 0 writes
+ * zeros to C (the empty sum).  Returns an SGEMM_* status code.
+ */
+int sgemm_f32(int M, int N, int K,
+              const float *A, int lda,
+              const float *B, int ldb,
+              float *C, int ldc,
+              hipStream_t stream);
+
+/*
+ * As sgemm_f32, with the kernel configuration and schedule forced (for
+ * tests and benchmarks).  config = SGEMM_CFG_*, sched = SGEMM_SCHED_*;
+ * SGEMM_CFG_AUTO / SGEMM_SCHED_AUTO select as sgemm_f32 does.  Returns
+ * SGEMM_ERR_CONFIG if the forced configuration cannot run this shape.
+ */
+int sgemm_f32_ex(int M, int N, int K,
+                 const float *A, int lda,
+                 const float *B, int ldb,
+                 float *C, int ldc,
+                 hipStream_t stream, int config, int sched);
+
+/* Shape multiples accepted by sgemm_f32 (any pointer may be NULL). */
+void sgemm_f32_granule(int *gm, int *gn, int *gk);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *sgemm_f32_status_string(int status);
+
+/* hipError_t of the most recent SGEMM_ERR_HIP in the calling thread (0 if none). */
+int sgemm_f32_last_hip_error(void);
+
+/*
+ * The launch plan the library would use, computed on the host only (no HIP
+ * call): which configuration, the tile, the grid, how many tiles are done
+ * whole and how many are split, and the workspace size.  num_cus is the
+ * compute-unit count; occupancy[c] is the number of workgroups of
+ * configuration c that fit on one compute unit (NULL: the library's
+ * built-in figures).  Returns an SGEMM_* status code; *out is filled on
+ * success.
+ */
+typedef struct sgemm_f32_plan_t {
+    int config;          /* SGEMM_CFG_* chosen */
+    int sched;           /* SGEMM_SCHED_DP or SGEMM_SCHED_STREAMK (DP+split mix reports STREAMK) */
+    int tile_m, tile_n, tile_k;
+    int threads;         /* threads per workgroup */
+    int tiles_m, tiles_n;
+    int iters_per_tile;  /* K / tile_k */
+    int dp_tiles;        /* tiles computed whole, first in tile order */
+    int sk_tiles;        /* remaining tiles, K-split over the grid */
+    int grid;            /* workgroups launched */
+    int sk_grid;         /* logical workgroups 0 .. sk_grid-1 share the split tiles */
+    int xcd_remap;       /* 1: workgroup ids are remapped so each XCD gets a contiguous run */
+    int group_m;         /* tile order: groups of group_m tile rows, column-major inside */
+    long long sk_iters;  /* sk_tiles * iters_per_tile */
+    long long workspace_bytes;
+} sgemm_f32_plan_t;
+
+int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,
+                   const int *occupancy, sgemm_f32_plan_t *out);
+
+/*
+ * Free every workspace the library holds (all devices, all streams).  The
+ * caller must ensure no sgemm call is still executing.  Returns SGEMM_OK or
+ * SGEMM_ERR_HIP.
+ */
+int sgemm_f32_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_F32_H */

@@ -1,0 +1,280 @@
+"""GPU parity: the HIP library (through its C-ABI) against the FP64 CPU oracle.
+
+Acceptance per element: finite and |C_gpu - C_ref| <= 1e-5 * S with
+S = sum_k |A[m,k] B[k,n]| (tolerance of the GEMM's accuracy target); on
+integer-valued inputs, bit-exact.  The pages' own looser check (finite, and
+max |err| / max |ref| < 1e-4; "Beyond Kernel 7", section "What the result
+establishes") is reported alongside.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import fp32_sgemm_f32_amd as sg
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    sg.library()
+    return torch.device("cuda:0")
+
+
+def to_dev(x, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def gpu_matmul(A, B, dev, config=sg.CFG_AUTO, sched=sg.SCHED_AUTO):
+    import torch
+    C = sg.matmul(to_dev(A, dev), to_dev(B, dev), config=config, sched=sched)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def fits(config, M, N, K):
+    if config == sg.CFG_AUTO:
+        return True
+    p = {sg.CFG_MFMA_256x256x16: (256, 256, 16), sg.CFG_MFMA_128x128x32: (128, 128, 32),
+         sg.CFG_MFMA_256x256x32: (256, 256, 32), sg.CFG_MFMA_256x128x32: (256, 128, 32),
+         sg.CFG_VALU_128x128x8: (128, 128, 8)}[config]
+    return M % p[0] == 0 and N % p[1] == 0 and K % p[2] == 0
+
+
+def check(C, C_ref, S, label):
+    ok, worst = oracle.within_bound(C, C_ref, S, TOL)
+    pages = float(np.max(np.abs(C - C_ref)) / max(np.max(np.abs(C_ref)), 1e-300))
+    log(f"  {label}: max|err|/S = {worst:.3e}, pages' max|err|/max|ref| = {pages:.3e}")
+    assert ok, f"{label}: per-element bound violated (worst {worst:.3e})"
+    assert pages < 1e-4
+
+
+CONFIGS = [sg.CFG_AUTO, sg.CFG_MFMA_256x256x16, sg.CFG_MFMA_128x128x32, sg.CFG_MFMA_256x256x32,
+           sg.CFG_MFMA_256x128x32, sg.CFG_VALU_128x128x8]
+SCHEDS = [sg.SCHED_AUTO, sg.SCHED_DP, sg.SCHED_STREAMK]
+# Several tiles each way, uneven Stream-K splits (K chunks not divisible by
+# the grid), non-square shapes, and the smallest accepted shape.
+SHAPES = [(512, 512, 512), (768, 512, 416), (256, 1280, 1152), (1536, 256, 2080), (128, 128, 32)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("sched", SCHEDS, ids=lambda s: sg.SCHED_NAMES[s])
+@pytest.mark.parametrize("config", CONFIGS, ids=lambda c: sg.CFG_NAMES[c])
+def test_parity_random(dev, config, sched, shape):
+    M, N, K = shape
+    log(f"case config={sg.CFG_NAMES[config]} sched={sg.SCHED_NAMES[sched]} shape={shape}")
+    A, B = workloads.generate(M, N, K, "uniform", 1000 + M + N + K)
+    if not fits(config, M, N, K):
+        import torch
+        with pytest.raises(sg.SgemmError) as e:
+            sg.matmul(to_dev(A, dev), to_dev(B, dev), config=config, sched=sched)
+        torch.cuda.synchronize()
+        assert e.value.status == sg.ERR_CONFIG
+        return
+    C = gpu_matmul(A, B, dev, config, sched)
+    C_ref, S = oracle.gemm(A, B)
+    check(C, C_ref, S, f"{sg.CFG_NAMES[config]}/{sg.SCHED_NAMES[sched]}")
+
+
+@pytest.mark.parametrize("sched", SCHEDS, ids=lambda s: sg.SCHED_NAMES[s])
+@pytest.mark.parametrize("config", CONFIGS, ids=lambda c: sg.CFG_NAMES[c])
+def test_integer_inputs_bit_exact(dev, config, sched):
+    """Entries in {-4..4} with K <= 1024: every partial sum is an integer below
+    2^24, exact in FP32 in any order, so every variant must match exactly."""
+    M, N, K = 512, 768, 1024
+    log(f"case int4 config={sg.CFG_NAMES[config]} sched={sg.SCHED_NAMES[sched]}")
+    A, B = workloads.generate(M, N, K, "int4", 77)
+    C = gpu_matmul(A, B, dev, config, sched)
+    C_ref, _ = oracle.gemm(A, B)
+    assert np.array_equal(C.astype(np.float64), C_ref)
+
+
+@pytest.mark.parametrize("config", CONFIGS, ids=lambda c: sg.CFG_NAMES[c])
+def test_identity_b_gives_a(dev, config):
+    M, K = 512, 256
+    log(f"case identity config={sg.CFG_NAMES[config]}")
+    A, _ = workloads.generate(M, K, K, "normal", 5)
+    C = gpu_matmul(A, np.eye(K, dtype=np.float32), dev, config, sg.SCHED_STREAMK)
+    assert np.array_equal(C, A)
+
+
+def test_all_ones_a_gives_column_sums(dev):
+    M, N, K = 256, 384, 1024
+    log("case all-ones A")
+    _, B = workloads.generate(M, N, K, "int4", 6)
+    C = gpu_matmul(np.ones((M, K), np.float32), B, dev)
+    assert np.array_equal(C, np.tile(B.astype(np.int64).sum(axis=0), (M, 1)).astype(np.float32))
+
+
+def test_k_zero_writes_zeros(dev):
+    import torch
+    log("case K=0")
+    A = torch.empty((256, 0), dtype=torch.float32, device=dev)
+    B = torch.empty((0, 384), dtype=torch.float32, device=dev)
+    C = torch.full((256, 384), float("nan"), dtype=torch.float32, device=dev)
+    sg.matmul(A, B, out=C)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(C).item() == 0
+
+
+def test_empty_m_is_a_no_op(dev):
+    import torch
+    log("case M=0")
+    A = torch.zeros((0, 64), dtype=torch.float32, device=dev)
+    B = torch.zeros((64, 128), dtype=torch.float32, device=dev)
+    C = sg.matmul(A, B)
+    torch.cuda.synchronize()
+    assert C.shape == (0, 128)
+
+
+@pytest.mark.parametrize("config", [sg.CFG_AUTO, sg.CFG_MFMA_128x128x32, sg.CFG_VALU_128x128x8],
+                         ids=lambda c: sg.CFG_NAMES[c])
+def test_padded_leading_dimensions_and_untouched_gap(dev, config):
+    """lda > K, ldb > N, ldc > N: results use only the logical region, and C's
+    padding columns (NaN sentinels) are never written."""
+    import torch
+    M, N, K = 384, 256, 320
+    log(f"case padded ld config={sg.CFG_NAMES[config]}")
+    A, B = workloads.generate(M, N, K, "normal", 9)
+    Ap = torch.full((M, K + 12), float("nan"), device=dev)
+    Bp = torch.full((K, N + 36), float("nan"), device=dev)
+    Cp = torch.full((M, N + 20), float("nan"), device=dev)
+    Ap[:, :K] = to_dev(A, dev)
+    Bp[:, :N] = to_dev(B, dev)
+    sg.matmul(Ap[:, :K], Bp[:, :N], out=Cp[:, :N], config=config, sched=sg.SCHED_STREAMK)
+    torch.cuda.synchronize()
+    Cn = Cp.cpu().numpy()
+    assert np.all(np.isnan(Cn[:, N:])), "ldc padding was written"
+    C_ref, S = oracle.gemm(A, B)
+    check(Cn[:, :N], C_ref, S, "padded")
+
+
+@pytest.mark.parametrize("config", [sg.CFG_MFMA_128x128x32, sg.CFG_MFMA_256x256x16, sg.CFG_VALU_128x128x8],
+                         ids=lambda c: sg.CFG_NAMES[c])
+def test_repeatable_and_fully_written(dev, config):
+    """C pre-filled with NaN is fully overwritten; repeated split runs are
+    bit-identical (the partial sums are combined in a fixed order)."""
+    import torch
+    M, N, K = 512, 512, 2048
+    log(f"case repeatability config={sg.CFG_NAMES[config]}")
+    A, B = workloads.generate(M, N, K, "normal", 10)
+    Ad, Bd = to_dev(A, dev), to_dev(B, dev)
+    outs = []
+    for _ in range(3):
+        C = torch.full((M, N), float("nan"), device=dev)
+        sg.matmul(Ad, Bd, out=C, config=config, sched=sg.SCHED_STREAMK)
+        torch.cuda.synchronize()
+        outs.append(C.cpu().numpy())
+    assert np.all(np.isfinite(outs[0]))
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_non_default_stream(dev):
+    import torch
+    M, N, K = 512, 256, 1024
+    log("case non-default stream")
+    A, B = workloads.generate(M, N, K, "uniform", 11)
+    s = torch.cuda.Stream(device=dev)
+    Ad, Bd = to_dev(A, dev), to_dev(B, dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        C = sg.matmul(Ad, Bd)
+    s.synchronize()
+    C_ref, S = oracle.gemm(A, B)
+    check(C.cpu().numpy(), C_ref, S, "side stream")
+
+
+def test_rejects_bad_memory_and_leaves_c_untouched(dev):
+    import ctypes
+
+    import torch
+    log("case pointer checks")
+    M, N, K = 256, 256, 256
+    Ad = torch.zeros((M, K), device=dev)
+    Bd = torch.zeros((K, N), device=dev)
+    C = torch.full((M, N), 7.0, device=dev)
+    host = np.zeros((M, K), np.float32)
+    st = sg.sgemm_raw(M, N, K, host.ctypes.data, K, Bd.data_ptr(), N, C.data_ptr(), N)
+    assert st == sg.ERR_POINTER
+    with pytest.raises(sg.SgemmError) as e:
+        sg.matmul(Ad[:128], Bd[:, :128], config=sg.CFG_MFMA_256x256x16)
+    assert e.value.status == sg.ERR_CONFIG
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0).item()
+    assert sg.last_hip_error() == 0
+
+    # A matrix whose extent runs past its own allocation (hipMalloc of 128 rows,
+    # used as 256): refused unless the runtime reports a larger allocation, in
+    # which case the access stays inside mapped memory.
+    hip = ctypes.CDLL("libamdhip64.so")
+    ptr = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(ptr), ctypes.c_size_t(128 * K * 4)) == 0
+    try:
+        base, size = ctypes.c_void_p(), ctypes.c_size_t()
+        assert hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size), ptr) == 0
+        C2 = torch.empty((M, N), device=dev)
+        st = sg.sgemm_raw(M, N, K, ptr.value, K, Bd.data_ptr(), N, C2.data_ptr(), N)
+        torch.cuda.synchronize()
+        if size.value < M * K * 4:
+            assert st == sg.ERR_POINTER
+        else:
+            assert st == sg.OK
+    finally:
+        hip.hipFree(ptr)
+
+
+def test_release_then_reuse(dev):
+    log("case release")
+    M, N, K = 256, 256, 512
+    A, B = workloads.generate(M, N, K, "int4", 12)
+    C1 = gpu_matmul(A, B, dev, sg.CFG_MFMA_128x128x32, sg.SCHED_STREAMK)
+    sg.release()
+    C2 = gpu_matmul(A, B, dev, sg.CFG_MFMA_128x128x32, sg.SCHED_STREAMK)
+    assert np.array_equal(C1, C2)
+
+
+# ---------------------------------------------------------------------------
+# The measured workloads at full size, in the launch configuration the
+# benchmark times (automatic choice).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_full_size(dev, name):
+    w = workloads.WORKLOADS[name]
+    log(f"case workload {name} {w.shape} {w.dist} seed {w.seed}")
+    A, B = workloads.generate_workload(w)
+    C = gpu_matmul(A, B, dev)
+    assert np.all(np.isfinite(C))
+    if w.dist == "int4":
+        C_ref, _ = oracle.gemm(A, B)
+        assert np.array_equal(C.astype(np.float64), C_ref)
+        return
+    if w.M * w.N * w.K <= 2048 ** 3 or w.K > w.M:
+        C_ref, S = oracle.gemm(A, B)
+        check(C, C_ref, S, name)
+        return
+    # Largest case: whole rows and columns spread over the tiles, plus random points.
+    rng = np.random.default_rng(w.seed)
+    rows_full = rng.choice(w.M, 4, replace=False)
+    cols_full = rng.choice(w.N, 4, replace=False)
+    r = [np.repeat(rows_full, w.N), np.tile(np.arange(w.M), 4), rng.integers(0, w.M, 20000)]
+    c = [np.tile(np.arange(w.N), 4), np.repeat(cols_full, w.M), rng.integers(0, w.N, 20000)]
+    r, c = np.concatenate(r), np.concatenate(c)
+    C_ref, S = oracle.gemm_points(A, B, r, c)
+    Cs = C[r, c].astype(np.float64)
+    ok = np.all(np.abs(Cs - C_ref) <= TOL * S)
+    worst = float(np.max(np.abs(Cs - C_ref) / S))
+    log(f"  {name}: {len(r)} sampled elements, max|err|/S = {worst:.3e}")
+    assert ok

@@ -1,0 +1,202 @@
+"""Host-side launch planning (no GPU): configuration choice, whole-tile waves,
+and the Stream-K partition of (tile, K chunk) steps.
+
+The work mapping below restates, for checking, how each workgroup of a
+launch walks its share (logical id, tile order, Stream-K range, partial
+slot); coverage and slot uniqueness are then checked on the planner's own
+numbers for many shapes and grids.
+"""
+import os
+from collections import Counter, defaultdict
+
+import pytest
+
+import fp32_sgemm_f32_amd as sg
+
+OCC = [0, 1, 2, 1, 1, 2]
+
+
+def logical_ids(p):
+    g = p["grid"]
+    ids = []
+    for b in range(g):
+        if p["xcd_remap"]:
+            per = g >> 3
+            ids.append((b & 7) * per + (b >> 3))
+        else:
+            ids.append(b)
+    return ids
+
+
+def tile_coords(p, t):
+    gsz = p["group_m"] * p["tiles_n"]
+    g = t // gsz
+    first = g * p["group_m"]
+    rows = min(p["tiles_m"] - first, p["group_m"])
+    r = t - g * gsz
+    return first + r % rows, r // rows
+
+
+def sk_begin(p, w):
+    return w * p["sk_iters"] // p["sk_grid"]
+
+
+def sk_owner(p, i):
+    return ((i + 1) * p["sk_grid"] - 1) // p["sk_iters"]
+
+
+def walk(p):
+    """Yield (logical wg, tile_m, tile_n, k0, k1, kind, slot) for every piece of work."""
+    ipt = p["iters_per_tile"]
+    for w in sorted(logical_ids(p)):
+        t = w
+        while t < p["dp_tiles"]:
+            tm, tn = tile_coords(p, t)
+            yield w, tm, tn, 0, ipt, "whole", None
+            t += p["grid"]
+        if w >= p["sk_grid"]:
+            continue
+        s, e = sk_begin(p, w), sk_begin(p, w + 1)
+        while s < e:
+            tl = s // ipt
+            k0 = s - tl * ipt
+            k1 = k0 + min(e - s, ipt - k0)
+            tm, tn = tile_coords(p, p["dp_tiles"] + tl)
+            first, last = sk_owner(p, tl * ipt), sk_owner(p, (tl + 1) * ipt - 1)
+            if first == last:
+                yield w, tm, tn, k0, k1, "whole", None
+            else:
+                slot = 0 if sk_begin(p, w) // ipt == tl else 1
+                yield w, tm, tn, k0, k1, "partial", slot
+            s += k1 - k0
+
+
+def check_plan(p, M, N, K):
+    assert p["tiles_m"] * p["tile_m"] == M and p["tiles_n"] * p["tile_n"] == N
+    assert p["iters_per_tile"] * p["tile_k"] == K
+    assert sorted(logical_ids(p)) == list(range(p["grid"]))        # remap is a bijection
+    assert p["sk_grid"] <= p["grid"]
+    if p["sk_tiles"]:
+        assert 1 <= p["sk_grid"] <= p["sk_iters"]
+        assert (p["sk_iters"] + 1) * p["sk_grid"] < 2 ** 31
+    cover = Counter()
+    slots = set()
+    per_tile = defaultdict(set)
+    for w, tm, tn, k0, k1, kind, slot in walk(p):
+        assert 0 <= tm < p["tiles_m"] and 0 <= tn < p["tiles_n"] and 0 <= k0 < k1 <= p["iters_per_tile"]
+        for k in range(k0, k1):
+            cover[(tm, tn, k)] += 1
+        if kind == "partial":
+            assert (w, slot) not in slots, "two partials in one slot"
+            slots.add((w, slot))
+            per_tile[(tm, tn)].add(w)
+    tiles = p["tiles_m"] * p["tiles_n"]
+    assert len(cover) == tiles * p["iters_per_tile"]
+    assert set(cover.values()) == {1}, "a (tile, K chunk) step is missing or repeated"
+    # Contributors of a split tile are consecutive workgroups.
+    for ws in per_tile.values():
+        assert sorted(ws) == list(range(min(ws), max(ws) + 1))
+    need = p["sk_grid"] * 2 * p["tile_m"] * p["tile_n"] * 4 if p["sk_tiles"] else 0
+    assert p["workspace_bytes"] >= need
+    return per_tile
+
+
+SHAPES = [(128, 128, 32), (256, 256, 256), (512, 384, 96), (1024, 1024, 1024), (1024, 1024, 16384),
+          (2048, 2048, 2048), (4096, 4096, 4096), (1280, 768, 640), (3072, 2048, 352)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("config", range(sg.NUM_CFGS))
+@pytest.mark.parametrize("sched", [sg.SCHED_AUTO, sg.SCHED_DP, sg.SCHED_STREAMK])
+@pytest.mark.parametrize("cus", [256, 132, 7])
+def test_every_step_covered_once(shape, config, sched, cus):
+    M, N, K = shape
+    try:
+        p = sg.plan(M, N, K, config, sched, num_cus=cus, occupancy=OCC)
+    except sg.SgemmError as e:
+        # Only a forced tile that does not divide the shape may be refused.
+        assert e.status == sg.ERR_CONFIG and config != sg.CFG_AUTO
+        return
+    check_plan(p, M, N, K)
+    if sched == sg.SCHED_DP:
+        assert p["sk_tiles"] == 0 and p["grid"] == p["tiles_m"] * p["tiles_n"]
+    if sched == sg.SCHED_STREAMK:
+        assert p["dp_tiles"] == 0
+
+
+def test_stream_k_example_from_the_page():
+    """n = 1024, 128x128 tiles, 264 resident blocks: all 64 tiles split, each
+    shared by roughly four blocks."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "streamk_p4_example.txt")
+    g = dict(ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#"))
+    n, tile = int(g["n"]), int(g["tile"])
+    occ = [0] * sg.NUM_CFGS
+    occ[sg.CFG_MFMA_128x128x32] = int(g["blocks_per_sm"])
+    p = sg.plan(n, n, n, sg.CFG_MFMA_128x128x32, sg.SCHED_AUTO, num_cus=int(g["sms"]), occupancy=occ)
+    assert p["tile_m"] == p["tile_n"] == tile
+    assert p["tiles_m"] * p["tiles_n"] == int(g["tiles"])
+    assert p["grid"] == int(g["resident_blocks"])
+    assert p["dp_tiles"] == 0 and p["sk_tiles"] == int(g["tiles"])
+    per_tile = check_plan(p, n, n, n)
+    counts = [len(v) for v in per_tile.values()]
+    assert len(counts) == int(g["tiles"])
+    # "Roughly four" blocks per tile: each tile holds grid / tiles = 4.125
+    # blocks' worth of K chunks.  A tile's K range therefore meets that many
+    # block ranges, plus one wherever the range boundaries fall inside it.
+    share = p["grid"] / (p["tiles_m"] * p["tiles_n"])
+    assert round(share) == int(g["blocks_per_tile_approx"])
+    assert all(int(share) <= c <= int(share) + 2 for c in counts)
+    mean = sum(counts) / len(counts)
+    assert share <= mean <= share + 1.0
+
+
+def test_full_waves_first_then_split():
+    # 1.25 waves of 128x128 tiles on 64 CUs x 2 = 128 resident workgroups:
+    # one full wave of whole tiles, the other 32 tiles split over the grid.
+    occ = [0] * sg.NUM_CFGS
+    occ[sg.CFG_MFMA_128x128x32] = 2
+    p = sg.plan(128 * 16, 128 * 10, 1024, sg.CFG_MFMA_128x128x32, sg.SCHED_AUTO, num_cus=64, occupancy=occ)
+    assert p["tiles_m"] * p["tiles_n"] == 160
+    assert p["dp_tiles"] == 128 and p["sk_tiles"] == 32 and p["grid"] == 128
+    check_plan(p, 128 * 16, 128 * 10, 1024)
+
+
+def test_auto_choices_on_256_cus():
+    occ = OCC
+    p = sg.plan(4096, 4096, 4096, num_cus=256, occupancy=occ)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_256x256x16, sg.SCHED_DP, 256)
+    p = sg.plan(2048, 2048, 2048, num_cus=256, occupancy=occ)
+    assert p["config"] == sg.CFG_MFMA_128x128x32 and p["sched"] == sg.SCHED_DP
+    for shape in [(1024, 1024, 1024), (1024, 1024, 16384)]:
+        p = sg.plan(*shape, num_cus=256, occupancy=occ)
+        assert p["sched"] == sg.SCHED_STREAMK and p["dp_tiles"] == 0 and p["grid"] >= 256
+
+
+def test_xcd_grouping_for_the_headline_shape():
+    """4096^3 on 256 CUs: each XCD's 32 consecutive tiles form a 4 x 8 block."""
+    p = sg.plan(4096, 4096, 4096, num_cus=256, occupancy=OCC)
+    assert p["xcd_remap"] == 1 and p["group_m"] == 4
+    ids = logical_ids(p)
+    for x in range(8):
+        tiles = {tile_coords(p, ids[b]) for b in range(p["grid"]) if b % 8 == x}
+        rows = {t[0] for t in tiles}
+        cols = {t[1] for t in tiles}
+        assert len(tiles) == 32 and len(rows) == 4 and len(cols) == 8
+
+
+def test_plan_errors():
+    with pytest.raises(sg.SgemmError) as e:
+        sg.plan(100, 128, 32)
+    assert e.value.status == sg.ERR_SHAPE
+    with pytest.raises(sg.SgemmError) as e:
+        sg.plan(128, 128, 32, config=sg.CFG_MFMA_256x256x16)
+    assert e.value.status == sg.ERR_CONFIG
+    with pytest.raises(sg.SgemmError) as e:
+        sg.plan(128, 128, 32, config=42)
+    assert e.value.status == sg.ERR_CONFIG
+
+
+def test_empty_shapes_plan_no_work():
+    for shape in [(0, 128, 32), (128, 0, 32), (128, 128, 0)]:
+        p = sg.plan(*shape, num_cus=256, occupancy=OCC)
+        assert p["sk_tiles"] == 0 and p["workspace_bytes"] == 0

@@ -84,3 +84,8 @@ def generate_workload(w: Workload):
 def sha256(x: np.ndarray) -> str:
     """Digest of a matrix's bytes, recorded with results."""
     return hashlib.sha256(np.ascontiguousarray(x).tobytes()).hexdigest()
+
+
+def tflops(M: int, N: int, K: int, seconds: float) -> float:
+    """Throughput in TFLOP/s, counting 2*M*N*K operations (multiply-add = 2)."""
+    return 2.0 * M * N * K / seconds / 1e12
