@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--detail", default=None, help="write a detail JSON file")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead: time a plain device copy of this many MiB (calibrates "
+                         "the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -185,6 +188,18 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     props = torch.cuda.get_device_properties(dev)
     log(f"device: {props.name}, {props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB")
+
+    if args.copy_mib:
+        n = args.copy_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            per, wall = time_calls(lambda: dst.copy_(src), stream, args.steps, args.warmup)
+        t = statistics.median(per) * 1e-3
+        print(json.dumps({"metric": "device copy GB/s (read + write)", "value": round(2 * n * 4 / t / 1e9, 1),
+                          "unit": "GB/s", "bytes_read": n * 4, "bytes_written": n * 4,
+                          "median_ms": round(t * 1e3, 4), "steps": args.steps}), flush=True)
+        return
 
     w = workloads.WORKLOADS[args.workload]
     head = bench_workload(sg, w, args, dev, stream, cold=args.cold, with_torch=args.torch)

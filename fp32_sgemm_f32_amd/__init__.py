@@ -9,7 +9,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsgemm_f32.so")
+# The in-tree build; SGEMM_F32_LIBRARY may name another build of the same sources.
+LIB_PATH = os.environ.get("SGEMM_F32_LIBRARY") or os.path.join(_HERE, "libsgemm_f32.so")
 
 # Status codes (SGEMM_*).
 OK = 0
@@ -29,7 +30,11 @@ CFG_MFMA_128x128x32 = 2
 CFG_MFMA_256x256x32 = 3
 CFG_MFMA_256x128x32 = 4
 CFG_VALU_128x128x8 = 5
-NUM_CFGS = 6
+CFG_MFMA_256x256x32_W8 = 6
+CFG_MFMA_128x128x32_W8 = 7
+CFG_MFMA_64x64x32 = 8
+CFG_MFMA_128x64x32 = 9
+NUM_CFGS = 10
 CFG_NAMES = {
     CFG_AUTO: "auto",
     CFG_MFMA_256x256x16: "mfma_256x256x16",
@@ -37,6 +42,18 @@ CFG_NAMES = {
     CFG_MFMA_256x256x32: "mfma_256x256x32",
     CFG_MFMA_256x128x32: "mfma_256x128x32",
     CFG_VALU_128x128x8: "valu_128x128x8",
+    CFG_MFMA_256x256x32_W8: "mfma_256x256x32_w8",
+    CFG_MFMA_128x128x32_W8: "mfma_128x128x32_w8",
+    CFG_MFMA_64x64x32: "mfma_64x64x32",
+    CFG_MFMA_128x64x32: "mfma_128x64x32",
+}
+# (tile_m, tile_n, tile_k) of each configuration.
+CFG_TILES = {
+    CFG_MFMA_256x256x16: (256, 256, 16), CFG_MFMA_128x128x32: (128, 128, 32),
+    CFG_MFMA_256x256x32: (256, 256, 32), CFG_MFMA_256x128x32: (256, 128, 32),
+    CFG_VALU_128x128x8: (128, 128, 8), CFG_MFMA_256x256x32_W8: (256, 256, 32),
+    CFG_MFMA_128x128x32_W8: (128, 128, 32), CFG_MFMA_64x64x32: (64, 64, 32),
+    CFG_MFMA_128x64x32: (128, 64, 32),
 }
 
 # Schedules (SGEMM_SCHED_*).
@@ -88,7 +105,7 @@ def library():
     lib.sgemm_f32_last_hip_error.restype = i
     lib.sgemm_f32_last_hip_error.argtypes = []
     lib.sgemm_f32_plan.restype = i
-    lib.sgemm_f32_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(_Plan)]
+    lib.sgemm_f32_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), i, ctypes.POINTER(_Plan)]
     lib.sgemm_f32_release.restype = i
     lib.sgemm_f32_release.argtypes = []
     _lib = lib
@@ -116,7 +133,8 @@ def release() -> None:
         raise SgemmError(st, "sgemm_f32_release")
 
 
-def plan(M, N, K, config=CFG_AUTO, sched=SCHED_AUTO, num_cus=256, occupancy=None) -> dict:
+def plan(M, N, K, config=CFG_AUTO, sched=SCHED_AUTO, num_cus=256, occupancy=None,
+         sk_wg_per_cu=0) -> dict:
     """The launch plan for a shape (host computation only, no GPU needed)."""
     occ = None
     if occupancy is not None:
@@ -124,7 +142,7 @@ def plan(M, N, K, config=CFG_AUTO, sched=SCHED_AUTO, num_cus=256, occupancy=None
             raise ValueError(f"occupancy needs {NUM_CFGS} entries")
         occ = (ctypes.c_int * NUM_CFGS)(*occupancy)
     out = _Plan()
-    st = library().sgemm_f32_plan(M, N, K, config, sched, num_cus, occ, ctypes.byref(out))
+    st = library().sgemm_f32_plan(M, N, K, config, sched, num_cus, occ, sk_wg_per_cu, ctypes.byref(out))
     if st != OK:
         raise SgemmError(st, "sgemm_f32_plan")
     return {name: getattr(out, name) for name, _ in _Plan._fields_}
@@ -142,7 +160,9 @@ def sgemm_raw(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream=0,
 def _row_major_ld(t, name):
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
-    if t.stride(1) != 1:
+    if t.numel() == 0:          # nothing is read or written through it
+        return (t.shape[1] + 3) // 4 * 4
+    if t.stride(1) != 1 and t.shape[1] > 1:
         raise ValueError(f"{name} must be row-major (unit column stride)")
     return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
 

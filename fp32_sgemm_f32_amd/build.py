@@ -34,8 +34,8 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def _compile(src: str, extra, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, verbose: bool, tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [hipcc(), *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
@@ -51,19 +51,21 @@ def _compile(src: str, extra, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=None) -> str:
-    """Compile every source and link the library; returns its path."""
+def build(verbose: bool = False, extra=None, out: str = LIB) -> str:
+    """Compile every source and link the library (extra: more hipcc flags,
+    out: library path); returns its path."""
     extra = list(extra or [])
+    tag = "" if out == LIB else "_" + os.path.splitext(os.path.basename(out))[0]
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra, verbose), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, extra, verbose, tag), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -6,6 +6,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// How split workgroups publish partial tiles to the last arriver (see run_gemm).
+#ifndef SGEMM_FIXUP_MODE
+#define SGEMM_FIXUP_MODE 1
+#endif
+
 namespace sgemm {
 
 // Native 4-wide vector (one 128-bit load/store).  Arrays of it are promoted to
@@ -128,6 +133,7 @@ __device__ __forceinline__ void run_gemm(const KernelArgs &a, float *lds, int *f
             // does not depend on arrival order) and writes C.  Nobody waits
             // for anybody, and the counter is reset for the next call.
             core.store_partial(partial_ptr<Core::TILE_FLOATS>(a, w, sk_slot(a, w, tl)));
+#if SGEMM_FIXUP_MODE == 0
             __threadfence();
             __syncthreads();
             if (threadIdx.x == 0) {
@@ -136,9 +142,34 @@ __device__ __forceinline__ void run_gemm(const KernelArgs &a, float *lds, int *f
                 *flag = (old == last - first) ? 1 : 0;
             }
             __syncthreads();
+#elif SGEMM_FIXUP_MODE == 1
+            // Each thread publishes its own partial (release at device scope),
+            // then one counter increment per workgroup.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const int old = __hip_atomic_fetch_add(&a.counters[tl], 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+                *flag = (old == last - first) ? 1 : 0;
+            }
+            __syncthreads();
+#else
+            // The workgroup barrier orders every thread's partial before thread
+            // 0's increment, which releases (and, for the last arriver,
+            // acquires) at device scope for the whole workgroup.
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const int old = __hip_atomic_fetch_add(&a.counters[tl], 1, __ATOMIC_ACQ_REL,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+                *flag = (old == last - first) ? 1 : 0;
+            }
+            __syncthreads();
+#endif
             const int is_last = __builtin_amdgcn_readfirstlane(*flag);
             if (is_last) {
-                __threadfence();
+#if SGEMM_FIXUP_MODE != 2
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#endif
                 core.zero();
                 for (int c = first; c <= last; ++c)
                     core.add_partial(partial_ptr<Core::TILE_FLOATS>(a, c, sk_slot(a, c, tl)));

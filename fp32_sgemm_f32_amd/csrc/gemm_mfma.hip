@@ -9,19 +9,23 @@
 //
 // Structure of one workgroup (BM x BN output tile, K chunks of BK):
 //   * global -> registers: each lane issues 128-bit loads (global_load_dwordx4)
-//     of A rows and B rows, adjacent lanes on adjacent addresses; chunk c+1 is
-//     in flight while chunk c is multiplied (register prefetch).
+//     of A rows and B rows, adjacent lanes on adjacent addresses; the next
+//     chunk but one is in flight while the current chunk is multiplied
+//     (register prefetch).
 //   * registers -> LDS: two LDS stages (ping-pong), one barrier per chunk.
-//     A is kept row-major (k contiguous) with rows padded to BK+4 floats; B is
-//     kept row-major (n contiguous) with rows padded to BN+4 floats.  Both
-//     paddings make the fragment reads below free of bank conflicts.
+//     Both tiles are kept k-contiguous with rows padded to BK+4 floats: A as
+//     loaded (row-major), B transposed on the way in (each lane loads R
+//     consecutive k-rows of 4 columns and writes, per column, R consecutive
+//     k values).  With a row stride of 4 x odd words, the operand reads
+//     below are free of bank conflicts.
 //   * LDS -> matrix cores: the waves tile the workgroup tile WAVES_M x
 //     WAVES_N; a wave owns FM x FN blocks of 32x32.  Inside a chunk the K
 //     index is permuted so that lane half h (lanes 32h .. 32h+31) works on
 //     k in [h*BK/2, (h+1)*BK/2): each MFMA step p pairs k = p (half 0) with
 //     k = BK/2 + p (half 1).  A sum is a sum, so the product is unchanged,
-//     and a lane's A operands for consecutive steps are consecutive floats in
-//     its LDS row: one ds_read_b128 feeds four steps.
+//     and a lane's operands for four consecutive steps are four consecutive
+//     floats of its LDS row: one ds_read_b128 per 32-row block of A and one
+//     per 32-column block of B feed four MFMA steps.
 //   * epilogue: each lane owns 16 values of each 32x32 block; a lane half
 //     writes 32 consecutive floats of a C row per store.
 #include "gemm_common.h"
@@ -40,22 +44,24 @@ struct MfmaCore {
     static constexpr int FM = WTM / 32;           // 32x32 blocks per wave, down
     static constexpr int FN = WTN / 32;           // 32x32 blocks per wave, across
     static constexpr int KH = BK / 2;             // k values per lane half per chunk
-    static constexpr int LDA_S = BK + 4;          // LDS row stride of the A tile
-    static constexpr int LDB_S = BN + 4;          // LDS row stride of the B tile
-    static constexpr int A_STAGE = BM * LDA_S;
-    static constexpr int B_STAGE = BK * LDB_S;
+    static constexpr int G = KH / 4;              // groups of four MFMA steps per chunk
+    static constexpr int LDK = BK + 4;            // LDS row stride of both tiles (floats)
+    static constexpr int A_STAGE = BM * LDK;
+    static constexpr int B_STAGE = BN * LDK;
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int LDS_FLOATS = 2 * STAGE;
     static constexpr int A_VEC = BM * BK / 4 / NT;   // float4 loads of A per lane per chunk
-    static constexpr int B_VEC = BK * BN / 4 / NT;   // float4 loads of B per lane per chunk
+    static constexpr int R = BK * BN / 4 / NT;       // k-rows of B per lane per chunk (4 columns each)
     static constexpr int A_ROWS_PER_PASS = NT / (BK / 4);
-    static constexpr int B_ROWS_PER_PASS = NT / (BN / 4);
     static constexpr int TILE_FLOATS = BM * BN;
 
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(BK % 8 == 0, "BK/2 must be a multiple of 4 (one b128 per four steps)");
+    static_assert(G % 2 == 0, "operand register sets alternate by group; the parity must carry");
     static_assert(A_VEC >= 1 && A_VEC * NT * 4 == BM * BK, "A tile must split evenly into float4s");
-    static_assert(B_VEC >= 1 && B_VEC * NT * 4 == BK * BN, "B tile must split evenly into float4s");
+    static_assert((R == 1 || R == 2 || R == 4 || R == 8) && R * NT * 4 == BK * BN,
+                  "B tile must split into R x 4 blocks");
+    static_assert((LDK / 4) % 2 == 1, "row stride must be 4 x odd words");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
 
     floatx16 acc[FM][FN];
@@ -69,88 +75,157 @@ struct MfmaCore {
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     }
 
+    // Per-lane addressing, computed once per tile.
+    struct Geo {
+        const float *ga, *gb;   // next global A / B chunk of this lane
+        int64_t ga_pass;        // A rows handled by the other passes
+        int64_t gb_row;         // one k-row of B
+        int64_t gb_chunk;       // one chunk of B rows
+        int sa, sb;             // LDS store offsets within a stage
+        int fa, fb;             // LDS operand offsets within a stage
+    };
+
+    // K loop over chunks [k0, k1) of tile (tm, tn).  A chunk is G groups of
+    // four MFMA steps.  Schedule (one barrier per chunk, two LDS stages, two
+    // register sets of operands):
+    //
+    //   group g < G-1:  read operands of group g+1      | MFMAs of group g
+    //   group G-1:      store chunk c+1 to the other stage, barrier,
+    //                   issue global loads of chunk c+2,
+    //                   read operands of group 0 of c+1 | MFMAs of group G-1
+    //
+    // so the last group's MFMAs cover the barrier and the first LDS reads of
+    // the next chunk, and global loads have a whole chunk to land.  The stage
+    // written at chunk c was last read during chunk c-1, before the barrier
+    // of chunk c-1 (which waits for the LDS reads to complete).  Chunks are
+    // unrolled in pairs so that stage and register set are compile-time.
     __device__ __forceinline__ void mainloop(const KernelArgs &a, float *lds, int tm, int tn,
                                              int k0, int k1) {
         const int tid = threadIdx.x;
-        const int64_t lda = a.lda, ldb = a.ldb;
+        Geo g;
+        {
+            const int a_row = tid / (BK / 4), a_c4 = tid % (BK / 4);
+            const int b_c4 = tid % (BN / 4), b_kb = tid / (BN / 4);   // columns 4*b_c4.., k rows R*b_kb..
+            g.ga = a.A + ((int64_t)tm * BM + a_row) * a.lda + (int64_t)k0 * BK + a_c4 * 4;
+            g.gb = a.B + ((int64_t)k0 * BK + b_kb * R) * a.ldb + (int64_t)tn * BN + b_c4 * 4;
+            g.ga_pass = (int64_t)A_ROWS_PER_PASS * a.lda;
+            g.gb_row = a.ldb;
+            g.gb_chunk = (int64_t)BK * a.ldb;
+            g.sa = a_row * LDK + a_c4 * 4;
+            g.sb = A_STAGE + (b_c4 * 4) * LDK + b_kb * R;
+            const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+            const int lane = tid & 63;
+            const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+            const int lr = lane & 31, lh = lane >> 5;
+            g.fa = (wm * WTM + lr) * LDK + lh * KH;
+            g.fb = A_STAGE + (wn * WTN + lr) * LDK + lh * KH;
+        }
 
-        // Loader geometry (hoisted out of the K loop).
-        const int a_row = tid / (BK / 4), a_c4 = tid % (BK / 4);
-        const int b_row = tid / (BN / 4), b_c4 = tid % (BN / 4);
-        const float *ga = a.A + ((int64_t)tm * BM + a_row) * lda + (int64_t)k0 * BK + a_c4 * 4;
-        const float *gb = a.B + ((int64_t)k0 * BK + b_row) * ldb + (int64_t)tn * BN + b_c4 * 4;
-        const int64_t ga_pass = (int64_t)A_ROWS_PER_PASS * lda;
-        const int64_t gb_pass = (int64_t)B_ROWS_PER_PASS * ldb;
-        const int64_t gb_chunk = (int64_t)BK * ldb;
-        const int sa = a_row * LDA_S + a_c4 * 4;
-        const int sb = A_STAGE + b_row * LDB_S + b_c4 * 4;
-
-        // Fragment geometry.
-        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int lane = tid & 63;
-        const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-        const int lr = lane & 31, lh = lane >> 5;
-        const int fa = (wm * WTM + lr) * LDA_S + lh * KH;
-        const int fb = A_STAGE + lh * KH * LDB_S + wn * WTN + lr;
-
-        f32x4 ra[A_VEC], rb[B_VEC];
-
-        auto load_global = [&]() {
-#pragma unroll
-            for (int i = 0; i < A_VEC; ++i) ra[i] = *(const f32x4 *)(ga + i * ga_pass);
-#pragma unroll
-            for (int i = 0; i < B_VEC; ++i) rb[i] = *(const f32x4 *)(gb + i * gb_pass);
-        };
-        auto store_lds = [&](int stage) {
-            float *s = lds + stage * STAGE;
-#pragma unroll
-            for (int i = 0; i < A_VEC; ++i)
-                *(f32x4 *)(s + sa + i * A_ROWS_PER_PASS * LDA_S) = ra[i];
-#pragma unroll
-            for (int i = 0; i < B_VEC; ++i)
-                *(f32x4 *)(s + sb + i * B_ROWS_PER_PASS * LDB_S) = rb[i];
-        };
-        auto compute = [&](int stage) {
-            const float *s = lds + stage * STAGE;
-#pragma unroll
-            for (int p = 0; p < KH; p += 4) {
-                f32x4 av[FM];
-                float bv[FN][4];
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    av[i] = *(const f32x4 *)(s + fa + i * 32 * LDA_S + p);
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) bv[j][q] = s[fb + (p + q) * LDB_S + j * 32];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                av[i][q], bv[j][q], acc[i][j], 0, 0, 0);
-            }
-        };
+        f32x4 ra[A_VEC], rb[R];
+        f32x4 av[2][FM], bv[2][FN];
 
         const int nch = k1 - k0;
-        load_global();
-        __syncthreads();            // LDS may still be read by a previous tile
-        store_lds(0);
+        // Prologue: chunk 0 into stage 0, chunk 1 in flight, group 0 operands.
+        load_global(g, ra, rb);
+        __syncthreads();                 // LDS may still be read by a previous tile
+        store_lds(lds, g, ra, rb);
         __syncthreads();
-        for (int c = 0; c < nch; ++c) {
-            const int cur = c & 1;
-            const bool more = c + 1 < nch;
-            if (more) {
-                ga += BK;
-                gb += gb_chunk;
-                load_global();
-            }
-            compute(cur);
-            if (more) store_lds(cur ^ 1);
-            __syncthreads();
+        if (nch > 1) {
+            g.ga += BK;
+            g.gb += g.gb_chunk;
+            load_global(g, ra, rb);
         }
+        read_operands(lds, 0, g, av[0], bv[0]);
+
+        // Steady state without branches (chunks c, c+1 both have two more
+        // chunks after them), so that no control-flow merge forces the
+        // compiler to wait for outstanding LDS reads before the MFMAs; then
+        // the last chunks with their conditions.
+        int c = 0;
+        for (; c + 3 < nch; c += 2) {
+            chunk<0, true>(c, nch, lds, g, ra, rb, av, bv);
+            chunk<1, true>(c + 1, nch, lds, g, ra, rb, av, bv);
+        }
+        for (; c < nch; c += 2) {
+            chunk<0, false>(c, nch, lds, g, ra, rb, av, bv);
+            if (c + 1 < nch) chunk<1, false>(c + 1, nch, lds, g, ra, rb, av, bv);
+        }
+    }
+
+    template <int ST, bool STEADY>
+    __device__ __forceinline__ void chunk(int c, int nch, float *lds, Geo &g, f32x4 (&ra)[A_VEC],
+                                          f32x4 (&rb)[R], f32x4 (&av)[2][FM], f32x4 (&bv)[2][FN]) {
+        const float *cur = lds + ST * STAGE;
+        float *nxt = lds + (ST ^ 1) * STAGE;
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const int cb = q & 1;
+            if (q + 1 < G) {
+                read_operands(cur, (q + 1) * 4, g, av[cb ^ 1], bv[cb ^ 1]);
+            } else if (STEADY || c + 1 < nch) {
+                store_lds(nxt, g, ra, rb);
+                __syncthreads();
+                if (STEADY || c + 2 < nch) {
+                    g.ga += BK;
+                    g.gb += g.gb_chunk;
+                    load_global(g, ra, rb);
+                    // Keep the loads here, a whole chunk ahead of their use:
+                    // the scheduler would otherwise sink them next to the
+                    // LDS stores to shorten their live ranges.
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                read_operands(nxt, 0, g, av[cb ^ 1], bv[cb ^ 1]);
+            }
+            mfma_group(av[cb], bv[cb]);
+        }
+    }
+
+    __device__ __forceinline__ static void load_global(const Geo &g, f32x4 (&ra)[A_VEC], f32x4 (&rb)[R]) {
+#pragma unroll
+        for (int i = 0; i < A_VEC; ++i) ra[i] = *(const f32x4 *)(g.ga + i * g.ga_pass);
+#pragma unroll
+        for (int r = 0; r < R; ++r) rb[r] = *(const f32x4 *)(g.gb + r * g.gb_row);
+    }
+
+    // A as loaded; B transposed: column 4*b_c4 + i receives the R k-values
+    // rb[0][i] .. rb[R-1][i] as one contiguous run.
+    __device__ __forceinline__ static void store_lds(float *s, const Geo &g, const f32x4 (&ra)[A_VEC],
+                                                     const f32x4 (&rb)[R]) {
+#pragma unroll
+        for (int i = 0; i < A_VEC; ++i) *(f32x4 *)(s + g.sa + i * A_ROWS_PER_PASS * LDK) = ra[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float *d = s + g.sb + i * LDK;
+            if constexpr (R == 1) {
+                *d = rb[0][i];
+            } else if constexpr (R == 2) {
+                typedef float f32x2 __attribute__((ext_vector_type(2)));
+                *(f32x2 *)d = f32x2{rb[0][i], rb[1][i]};
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; r += 4)
+                    *(f32x4 *)(d + r) = f32x4{rb[r][i], rb[r + 1][i], rb[r + 2][i], rb[r + 3][i]};
+            }
+        }
+    }
+
+    // Operands of the four MFMA steps starting at step p.
+    __device__ __forceinline__ static void read_operands(const float *s, int p, const Geo &g,
+                                                         f32x4 (&av)[FM], f32x4 (&bv)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) av[i] = *(const f32x4 *)(s + g.fa + i * 32 * LDK + p);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bv[j] = *(const f32x4 *)(s + g.fb + j * 32 * LDK + p);
+    }
+
+    __device__ __forceinline__ void mfma_group(const f32x4 (&av)[FM], const f32x4 (&bv)[FN]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][q], bv[j][q], acc[i][j], 0, 0, 0);
     }
 
     // C element (row, col) of block (i, j), register r, for this lane:
@@ -210,6 +285,10 @@ using Mfma256x256x16 = MfmaCore<256, 256, 16, 4, 2>;
 using Mfma128x128x32 = MfmaCore<128, 128, 32, 2, 2>;
 using Mfma256x256x32 = MfmaCore<256, 256, 32, 2, 2>;
 using Mfma256x128x32 = MfmaCore<256, 128, 32, 2, 2>;
+using Mfma256x256x32W8 = MfmaCore<256, 256, 32, 4, 2>;
+using Mfma128x128x32W8 = MfmaCore<128, 128, 32, 4, 2>;
+using Mfma64x64x32 = MfmaCore<64, 64, 32, 2, 2>;
+using Mfma128x64x32 = MfmaCore<128, 64, 32, 2, 2>;
 
 template <class Core>
 static hipError_t launch(const KernelArgs &a, hipStream_t s) {
@@ -234,6 +313,10 @@ hipError_t launch_mfma(int cfg, const KernelArgs &a, hipStream_t s) {
     case SGEMM_CFG_MFMA_128x128x32: return launch<Mfma128x128x32>(a, s);
     case SGEMM_CFG_MFMA_256x256x32: return launch<Mfma256x256x32>(a, s);
     case SGEMM_CFG_MFMA_256x128x32: return launch<Mfma256x128x32>(a, s);
+    case SGEMM_CFG_MFMA_256x256x32_W8: return launch<Mfma256x256x32W8>(a, s);
+    case SGEMM_CFG_MFMA_128x128x32_W8: return launch<Mfma128x128x32W8>(a, s);
+    case SGEMM_CFG_MFMA_64x64x32: return launch<Mfma64x64x32>(a, s);
+    case SGEMM_CFG_MFMA_128x64x32: return launch<Mfma128x64x32>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -244,6 +327,10 @@ hipError_t occupancy_mfma(int cfg, int *wg_per_cu) {
     case SGEMM_CFG_MFMA_128x128x32: return occ<Mfma128x128x32>(wg_per_cu);
     case SGEMM_CFG_MFMA_256x256x32: return occ<Mfma256x256x32>(wg_per_cu);
     case SGEMM_CFG_MFMA_256x128x32: return occ<Mfma256x128x32>(wg_per_cu);
+    case SGEMM_CFG_MFMA_256x256x32_W8: return occ<Mfma256x256x32W8>(wg_per_cu);
+    case SGEMM_CFG_MFMA_128x128x32_W8: return occ<Mfma128x128x32W8>(wg_per_cu);
+    case SGEMM_CFG_MFMA_64x64x32: return occ<Mfma64x64x32>(wg_per_cu);
+    case SGEMM_CFG_MFMA_128x64x32: return occ<Mfma128x64x32>(wg_per_cu);
     default: return hipErrorInvalidValue;
     }
 }

@@ -21,6 +21,10 @@ const CfgInfo kCfgs[] = {
     {SGEMM_CFG_MFMA_256x256x32, 256, 256, 32, 256, true, 1, "mfma_256x256x32"},
     {SGEMM_CFG_MFMA_256x128x32, 256, 128, 32, 256, true, 1, "mfma_256x128x32"},
     {SGEMM_CFG_VALU_128x128x8, 128, 128, 8, 256, false, 2, "valu_128x128x8"},
+    {SGEMM_CFG_MFMA_256x256x32_W8, 256, 256, 32, 512, true, 1, "mfma_256x256x32_w8"},
+    {SGEMM_CFG_MFMA_128x128x32_W8, 128, 128, 32, 512, true, 2, "mfma_128x128x32_w8"},
+    {SGEMM_CFG_MFMA_64x64x32, 64, 64, 32, 256, true, 4, "mfma_64x64x32"},
+    {SGEMM_CFG_MFMA_128x64x32, 128, 64, 32, 256, true, 3, "mfma_128x64x32"},
 };
 const int kNumCfgs = SGEMM_NUM_CFGS;
 
@@ -54,6 +58,28 @@ static int pick_group_m(int tiles_m, int run) {
     return best;
 }
 
+static int64_t tiles_of(int cfg, int M, int N) {
+    return (int64_t)(M / kCfgs[cfg].bm) * (N / kCfgs[cfg].bn);
+}
+
+// Automatic choice, from timings of the configurations on MI355X (256 CUs):
+//   * 256x256 tiles (8 waves) when every CU gets at least one: the highest
+//     per-CU MFMA utilisation;
+//   * else 128x64 tiles when that gives two or more per CU (two workgroups
+//     per CU hide each other's barrier and memory stalls);
+//   * else, for long K (K >= 4 max(M, N)), 128x128 tiles with the K range
+//     split over the CUs (Stream-K);
+//   * else 64x64 tiles, whole.
+static int auto_config(int M, int N, int K, int cus) {
+    const int big = SGEMM_CFG_MFMA_256x256x32_W8, mid = SGEMM_CFG_MFMA_128x64x32,
+              skc = SGEMM_CFG_MFMA_128x128x32, small = SGEMM_CFG_MFMA_64x64x32;
+    if (fits(kCfgs[big], M, N, K) && tiles_of(big, M, N) >= cus) return big;
+    if (fits(kCfgs[mid], M, N, K) && tiles_of(mid, M, N) >= 2LL * cus) return mid;
+    const int mn = M > N ? M : N;
+    if (fits(kCfgs[skc], M, N, K) && (int64_t)K >= 4LL * mn) return skc;
+    return small;
+}
+
 int make_plan(const PlanRequest &req, Plan *out) {
     const int M = req.M, N = req.N, K = req.K;
     if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SHAPE;
@@ -63,15 +89,7 @@ int make_plan(const PlanRequest &req, Plan *out) {
     const int cus = req.num_cus > 0 ? req.num_cus : 1;
 
     int cfg = req.config;
-    if (cfg == SGEMM_CFG_AUTO) {
-        // Largest matrix-core tile that still gives every CU a tile; else
-        // the 128x128 tile, split along K when there are too few tiles.
-        const CfgInfo &big = kCfgs[SGEMM_CFG_MFMA_256x256x16];
-        if (fits(big, M, N, K) && (int64_t)(M / big.bm) * (N / big.bn) >= cus)
-            cfg = SGEMM_CFG_MFMA_256x256x16;
-        else
-            cfg = SGEMM_CFG_MFMA_128x128x32;
-    }
+    if (cfg == SGEMM_CFG_AUTO) cfg = auto_config(M, N, K, cus);
     const CfgInfo &c = kCfgs[cfg];
     if (!fits(c, M, N, K)) return SGEMM_ERR_CONFIG;
 
@@ -83,13 +101,16 @@ int make_plan(const PlanRequest &req, Plan *out) {
     p.ipt = K / c.bk;
     const int tiles = p.tiles_m * p.tiles_n;
     const int occ = occ_of(req, cfg);
-    const int sk_per_cu = req.sk_wg_per_cu > 0 ? req.sk_wg_per_cu : occ;
-    const int cap = cus * sk_per_cu;
+    // Split workgroups per CU: one by default (measured faster than filling
+    // every resident slot, which multiplies partial tiles), else as asked.
+    const int sk_per_cu = req.sk_wg_per_cu > 0 ? req.sk_wg_per_cu : 1;
+    const int cap = cus * (sk_per_cu < occ ? sk_per_cu : occ);
 
     int sched = req.sched;
     if (tiles == 0 || p.ipt == 0) sched = SGEMM_SCHED_DP;  // nothing to split
     if (sched == SGEMM_SCHED_AUTO) {
         if (tiles >= cus && tiles % cus == 0) sched = SGEMM_SCHED_DP;
+        else if (tiles < cus && p.ipt < 2 * kMinSkIters) sched = SGEMM_SCHED_DP;  // too short to split
         else sched = SGEMM_SCHED_STREAMK;
     }
 

@@ -27,7 +27,7 @@ extern const int kNumCfgs;
 constexpr int kGranM = 128, kGranN = 128, kGranK = 32;
 
 // Smallest number of K chunks a Stream-K workgroup should own.
-constexpr int kMinSkIters = 2;
+constexpr int kMinSkIters = 8;
 
 struct PlanRequest {
     int M, N, K;

@@ -112,9 +112,10 @@ int check_args(int M, int N, int K, const float *A, int lda, const float *B, int
     if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SHAPE;
     if (M % kGranM || N % kGranN || K % kGranK) return SGEMM_ERR_SHAPE;
     if (M == 0 || N == 0) return SGEMM_OK;
-    if (lda < K || ldb < N || ldc < N || lda < 0 || ldb < 0) return SGEMM_ERR_LD;
+    // A and B (and their leading dimensions) are not read when K == 0.
+    if (ldc < N || (K > 0 && (lda < K || ldb < N))) return SGEMM_ERR_LD;
     if (!C || (K > 0 && (!A || !B))) return SGEMM_ERR_NULL;
-    if ((lda & 3) || (ldb & 3) || (ldc & 3)) return SGEMM_ERR_ALIGN;
+    if ((ldc & 3) || (K > 0 && ((lda & 3) || (ldb & 3)))) return SGEMM_ERR_ALIGN;
     if (((uintptr_t)C & 15) || (K > 0 && (((uintptr_t)A & 15) || ((uintptr_t)B & 15))))
         return SGEMM_ERR_ALIGN;
     const int64_t nc = extent_bytes(M, N, ldc);
@@ -248,9 +249,9 @@ SGEMM_API const char *sgemm_f32_status_string(int status) {
 SGEMM_API int sgemm_f32_last_hip_error(void) { return sgemm::g_last_hip_error; }
 
 SGEMM_API int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,
-                             const int *occupancy, sgemm_f32_plan_t *out) {
+                             const int *occupancy, int sk_wg_per_cu, sgemm_f32_plan_t *out) {
     if (!out) return SGEMM_ERR_NULL;
-    sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, 0};
+    sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu};
     sgemm::Plan p;
     int st = sgemm::make_plan(req, &p);
     if (st != SGEMM_OK) return st;

@@ -69,7 +69,11 @@ extern "C" {
 #define SGEMM_CFG_MFMA_256x256x32   3  /* 256 threads, 4 waves of 128x128 */
 #define SGEMM_CFG_MFMA_256x128x32   4  /* 256 threads, 4 waves of 128x64 */
 #define SGEMM_CFG_VALU_128x128x8    5  /* 256 threads, 8x8 outputs per lane */
-#define SGEMM_NUM_CFGS              6  /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
+#define SGEMM_CFG_MFMA_256x256x32_W8 6 /* 512 threads, 8 waves of 64x128 */
+#define SGEMM_CFG_MFMA_128x128x32_W8 7 /* 512 threads, 8 waves of 32x64 */
+#define SGEMM_CFG_MFMA_64x64x32     8  /* 256 threads, 4 waves of 32x32 */
+#define SGEMM_CFG_MFMA_128x64x32    9  /* 256 threads, 4 waves of 64x32 */
+#define SGEMM_NUM_CFGS              10 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
 
 /* Schedules. */
 #define SGEMM_SCHED_AUTO     0  /* whole tiles in full waves, Stream-K for the rest */
@@ -80,7 +84,8 @@ extern "C" {
  * C = A * B.  Requirements: M, N multiples of gm, K a multiple of gk, where
  * sgemm_f32_granule() gives (gm, gn, gk); lda >= K, ldb >= N, ldc >= N, all
  * multiples of 4; A, B, C 16-byte aligned device pointers.  K == 0 writes
- * zeros to C (the empty sum).  Returns an SGEMM_* status code.
+ * zeros to C (the empty sum); A, B, lda and ldb are then not used or checked.
+ * Returns an SGEMM_* status code.
  */
 int sgemm_f32(int M, int N, int K,
               const float *A, int lda,
@@ -115,8 +120,9 @@ int sgemm_f32_last_hip_error(void);
  * whole and how many are split, and the workspace size.  num_cus is the
  * compute-unit count; occupancy[c] is the number of workgroups of
  * configuration c that fit on one compute unit (NULL: the library's
- * built-in figures).  Returns an SGEMM_* status code; *out is filled on
- * success.
+ * built-in figures); sk_wg_per_cu is the number of split workgroups per CU
+ * (0: the library's default, one), capped by the occupancy.  Returns an
+ * SGEMM_* status code; *out is filled on success.
  */
 typedef struct sgemm_f32_plan_t {
     int config;          /* SGEMM_CFG_* chosen */
@@ -136,7 +142,7 @@ typedef struct sgemm_f32_plan_t {
 } sgemm_f32_plan_t;
 
 int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,
-                   const int *occupancy, sgemm_f32_plan_t *out);
+                   const int *occupancy, int sk_wg_per_cu, sgemm_f32_plan_t *out);
 
 /*
  * Free every workspace the library holds (all devices, all streams).  The

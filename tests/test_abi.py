@@ -101,6 +101,14 @@ def test_rejects_unknown_config_or_schedule():
     assert call(128, 128, 64, sched=7) == sg.ERR_CONFIG
 
 
+def test_k_zero_ignores_a_and_b_layout():
+    # With K == 0 only C is checked: A/B strides and alignment do not matter,
+    # but C's still do (and valid arguments would then need a device).
+    assert call(128, 128, 0, lda=1, ldb=3, ldc=130) == sg.ERR_ALIGN
+    assert call(128, 128, 0, lda=1, ldb=3, ldc=100) == sg.ERR_LD
+    assert call(128, 128, 0, A=0, B=0, C=0) == sg.ERR_NULL
+
+
 def test_empty_output_is_a_no_op():
     # M == 0 or N == 0: nothing to compute, nothing touched, no device needed.
     assert call(0, 128, 64, A=0, B=0, C=0) == sg.OK

@@ -47,10 +47,8 @@ def gpu_matmul(A, B, dev, config=sg.CFG_AUTO, sched=sg.SCHED_AUTO):
 def fits(config, M, N, K):
     if config == sg.CFG_AUTO:
         return True
-    p = {sg.CFG_MFMA_256x256x16: (256, 256, 16), sg.CFG_MFMA_128x128x32: (128, 128, 32),
-         sg.CFG_MFMA_256x256x32: (256, 256, 32), sg.CFG_MFMA_256x128x32: (256, 128, 32),
-         sg.CFG_VALU_128x128x8: (128, 128, 8)}[config]
-    return M % p[0] == 0 and N % p[1] == 0 and K % p[2] == 0
+    bm, bn, bk = sg.CFG_TILES[config]
+    return M % bm == 0 and N % bn == 0 and K % bk == 0
 
 
 def check(C, C_ref, S, label):
@@ -61,8 +59,7 @@ def check(C, C_ref, S, label):
     assert pages < 1e-4
 
 
-CONFIGS = [sg.CFG_AUTO, sg.CFG_MFMA_256x256x16, sg.CFG_MFMA_128x128x32, sg.CFG_MFMA_256x256x32,
-           sg.CFG_MFMA_256x128x32, sg.CFG_VALU_128x128x8]
+CONFIGS = list(range(sg.NUM_CFGS))
 SCHEDS = [sg.SCHED_AUTO, sg.SCHED_DP, sg.SCHED_STREAMK]
 # Several tiles each way, uneven Stream-K splits (K chunks not divisible by
 # the grid), non-square shapes, and the smallest accepted shape.

@@ -13,7 +13,7 @@ import pytest
 
 import fp32_sgemm_f32_amd as sg
 
-OCC = [0, 1, 2, 1, 1, 2]
+OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2]
 
 
 def logical_ids(p):
@@ -130,9 +130,12 @@ def test_stream_k_example_from_the_page():
     path = os.path.join(os.path.dirname(__file__), "golden", "streamk_p4_example.txt")
     g = dict(ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#"))
     n, tile = int(g["n"]), int(g["tile"])
+    # The 128x128 tile with K chunks of 8, as on the page's FFMA kernels.
+    cfg = sg.CFG_VALU_128x128x8
     occ = [0] * sg.NUM_CFGS
-    occ[sg.CFG_MFMA_128x128x32] = int(g["blocks_per_sm"])
-    p = sg.plan(n, n, n, sg.CFG_MFMA_128x128x32, sg.SCHED_AUTO, num_cus=int(g["sms"]), occupancy=occ)
+    occ[cfg] = int(g["blocks_per_sm"])
+    p = sg.plan(n, n, n, cfg, sg.SCHED_AUTO, num_cus=int(g["sms"]), occupancy=occ,
+                sk_wg_per_cu=int(g["blocks_per_sm"]))
     assert p["tile_m"] == p["tile_n"] == tile
     assert p["tiles_m"] * p["tiles_n"] == int(g["tiles"])
     assert p["grid"] == int(g["resident_blocks"])
@@ -155,7 +158,8 @@ def test_full_waves_first_then_split():
     # one full wave of whole tiles, the other 32 tiles split over the grid.
     occ = [0] * sg.NUM_CFGS
     occ[sg.CFG_MFMA_128x128x32] = 2
-    p = sg.plan(128 * 16, 128 * 10, 1024, sg.CFG_MFMA_128x128x32, sg.SCHED_AUTO, num_cus=64, occupancy=occ)
+    p = sg.plan(128 * 16, 128 * 10, 1024, sg.CFG_MFMA_128x128x32, sg.SCHED_AUTO, num_cus=64,
+                occupancy=occ, sk_wg_per_cu=2)
     assert p["tiles_m"] * p["tiles_n"] == 160
     assert p["dp_tiles"] == 128 and p["sk_tiles"] == 32 and p["grid"] == 128
     check_plan(p, 128 * 16, 128 * 10, 1024)
@@ -164,12 +168,15 @@ def test_full_waves_first_then_split():
 def test_auto_choices_on_256_cus():
     occ = OCC
     p = sg.plan(4096, 4096, 4096, num_cus=256, occupancy=occ)
-    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_256x256x16, sg.SCHED_DP, 256)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_256x256x32_W8, sg.SCHED_DP, 256)
     p = sg.plan(2048, 2048, 2048, num_cus=256, occupancy=occ)
-    assert p["config"] == sg.CFG_MFMA_128x128x32 and p["sched"] == sg.SCHED_DP
-    for shape in [(1024, 1024, 1024), (1024, 1024, 16384)]:
-        p = sg.plan(*shape, num_cus=256, occupancy=occ)
-        assert p["sched"] == sg.SCHED_STREAMK and p["dp_tiles"] == 0 and p["grid"] >= 256
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_128x64x32, sg.SCHED_DP, 512)
+    p = sg.plan(1024, 1024, 1024, num_cus=256, occupancy=occ)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_64x64x32, sg.SCHED_DP, 256)
+    p = sg.plan(1024, 1024, 16384, num_cus=256, occupancy=occ)
+    assert (p["config"], p["sched"], p["dp_tiles"], p["grid"]) == (sg.CFG_MFMA_128x128x32, sg.SCHED_STREAMK, 0, 256)
+    p = sg.plan(256, 256, 256, num_cus=256, occupancy=occ)
+    assert (p["config"], p["sched"]) == (sg.CFG_MFMA_64x64x32, sg.SCHED_DP)
 
 
 def test_xcd_grouping_for_the_headline_shape():
