@@ -33,6 +33,27 @@ PEAK_HBM_GBS = 8000.0
 # Kernel 7", section "The confirmed result", k13f 2761.2 us = 49.8 TFLOP/s.
 PAGES_4096_TFLOPS = 49.8
 
+# HBM-side bytes per launch of the headline kernel, from two rocprofv3 --pmc
+# runs (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by what the
+# same counter reads for a plain 256 MiB device copy (FETCH_SIZE 2.0, WRITE_SIZE
+# 1.0); see profiles/sgemm_4096_mfma_256x256x32_w8_counters.md.  Valid only for
+# the kernel sources they were taken on (digest below); otherwise reported null.
+TRAFFIC = {
+    "kernel": "mfma_256x256x32_w8", "workload": "sgemm_4096",
+    "source_digest": "e4b3520ab7202d64",
+    "bytes": 469919218,
+}
+KERNEL_SOURCES = ("fp32_sgemm_f32_amd/csrc/gemm_mfma.hip", "fp32_sgemm_f32_amd/csrc/gemm_common.h")
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -216,8 +237,13 @@ def main():
         detail["others"] = rest
 
     achieved = w.flops / (head["event_ms_mean"] * 1e-3) / 1e12
+    traffic = None
+    if (TRAFFIC["kernel"] == sg.CFG_NAMES[head["plan"]["config"]] and TRAFFIC["workload"] == w.name
+            and TRAFFIC["source_digest"] == kernel_source_digest()):
+        traffic = TRAFFIC["bytes"]
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch"}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
