@@ -52,6 +52,7 @@ struct MfmaCore {
     static constexpr int LDS_FLOATS = 2 * STAGE;
     static constexpr int A_VEC = BM * BK / 4 / NT;   // float4 loads of A per lane per chunk
     static constexpr int R = BK * BN / 4 / NT;       // k-rows of B per lane per chunk (4 columns each)
+    static constexpr int RL = R >= 4 ? 4 : (R == 2 ? 8 : 16);   // lanes along k in the B loader
     static constexpr int A_ROWS_PER_PASS = NT / (BK / 4);
     static constexpr int TILE_FLOATS = BM * BN;
 
@@ -62,6 +63,7 @@ struct MfmaCore {
     static_assert((R == 1 || R == 2 || R == 4 || R == 8) && R * NT * 4 == BK * BN,
                   "B tile must split into R x 4 blocks");
     static_assert((LDK / 4) % 2 == 1, "row stride must be 4 x odd words");
+    static_assert((BK / R) % RL == 0 && NT % (RL * (BN / 4)) == 0, "B loader lane map must tile the chunk");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
 
     floatx16 acc[FM][FN];
@@ -86,26 +88,38 @@ struct MfmaCore {
     };
 
     // K loop over chunks [k0, k1) of tile (tm, tn).  A chunk is G groups of
-    // four MFMA steps.  Schedule (one barrier per chunk, two LDS stages, two
-    // register sets of operands):
+    // four MFMA steps.  Schedule of chunk c (two LDS stages, two register
+    // sets of operands, one barrier):
     //
-    //   group g < G-1:  read operands of group g+1      | MFMAs of group g
-    //   group G-1:      store chunk c+1 to the other stage, barrier,
-    //                   issue global loads of chunk c+2,
-    //                   read operands of group 0 of c+1 | MFMAs of group G-1
+    //   group 0:        read operands of group 1          | MFMAs of group 0
+    //                   store chunk c+1 (loaded during chunk c-1) to the
+    //                   other stage, issue global loads of chunk c+2
+    //   group g < G-1:  read operands of group g+1        | MFMAs of group g
+    //   group G-1:      barrier,
+    //                   read operands of group 0 of c+1   | MFMAs of group G-1
     //
-    // so the last group's MFMAs cover the barrier and the first LDS reads of
-    // the next chunk, and global loads have a whole chunk to land.  The stage
-    // written at chunk c was last read during chunk c-1, before the barrier
-    // of chunk c-1 (which waits for the LDS reads to complete).  Chunks are
-    // unrolled in pairs so that stage and register set are compile-time.
+    // The LDS stores land early in the chunk, so the barrier has nothing to
+    // wait for but the other waves; the last group's MFMAs cover the barrier
+    // and the next chunk's first LDS reads; the global loads have a whole
+    // chunk to land.  Stage safety: the stage written in chunk c held chunk
+    // c-1, whose reads all finished before the barrier ending chunk c-1; the
+    // barrier ending chunk c orders those writes before their reads and every
+    // read of chunk c's stage before its next write (in chunk c+1).  Chunks
+    // are unrolled in pairs so that stage and register set are compile-time.
     __device__ __forceinline__ void mainloop(const KernelArgs &a, float *lds, int tm, int tn,
                                              int k0, int k1) {
         const int tid = threadIdx.x;
         Geo g;
         {
             const int a_row = tid / (BK / 4), a_c4 = tid % (BK / 4);
-            const int b_c4 = tid % (BN / 4), b_kb = tid / (BN / 4);   // columns 4*b_c4.., k rows R*b_kb..
+            // B: columns 4*b_c4 .. +3, k rows R*b_kb .. +R-1.  Lanes vary the
+            // k block fastest (RL of them), then the column block, so that the
+            // lanes the LDS serves together (16 for b128 writes, 32 for b64)
+            // land on 4 column blocks x RL k blocks: distinct banks, as the
+            // column stride is 4 x LDK = 16 x odd words.  Each global load
+            // instruction still covers whole 128-256 B row segments.
+            const int b_c4 = (tid / RL) % (BN / 4);
+            const int b_kb = tid % RL + RL * (tid / (RL * (BN / 4)));
             g.ga = a.A + ((int64_t)tm * BM + a_row) * a.lda + (int64_t)k0 * BK + a_c4 * 4;
             g.gb = a.B + ((int64_t)k0 * BK + b_kb * R) * a.ldb + (int64_t)tn * BN + b_c4 * 4;
             g.ga_pass = (int64_t)A_ROWS_PER_PASS * a.lda;
@@ -134,6 +148,7 @@ struct MfmaCore {
             g.ga += BK;
             g.gb += g.gb_chunk;
             load_global(g, ra, rb);
+            __builtin_amdgcn_sched_barrier(0);
         }
         read_operands(lds, 0, g, av[0], bv[0]);
 
@@ -157,27 +172,47 @@ struct MfmaCore {
                                           f32x4 (&rb)[R], f32x4 (&av)[2][FM], f32x4 (&bv)[2][FN]) {
         const float *cur = lds + ST * STAGE;
         float *nxt = lds + (ST ^ 1) * STAGE;
+        const bool more = STEADY || c + 1 < nch;
 #pragma unroll
         for (int q = 0; q < G; ++q) {
             const int cb = q & 1;
             if (q + 1 < G) {
                 read_operands(cur, (q + 1) * 4, g, av[cb ^ 1], bv[cb ^ 1]);
-            } else if (STEADY || c + 1 < nch) {
-                store_lds(nxt, g, ra, rb);
+            } else if (more) {
                 __syncthreads();
+                read_operands(nxt, 0, g, av[cb ^ 1], bv[cb ^ 1]);
+            }
+            mfma_group(av[cb], bv[cb]);
+            if (STEADY) interleave_reads_with_mfmas();
+            if (q == 0 && more) {
+                store_lds(nxt, g, ra, rb);
+                __builtin_amdgcn_sched_barrier(0);   // stores free ra/rb before the loads refill them
                 if (STEADY || c + 2 < nch) {
                     g.ga += BK;
                     g.gb += g.gb_chunk;
                     load_global(g, ra, rb);
-                    // Keep the loads here, a whole chunk ahead of their use:
-                    // the scheduler would otherwise sink them next to the
-                    // LDS stores to shorten their live ranges.
-                    __builtin_amdgcn_sched_barrier(0);
                 }
-                read_operands(nxt, 0, g, av[cb ^ 1], bv[cb ^ 1]);
+                // Keep the stores and loads here: the scheduler would otherwise
+                // sink the loads next to their use to shorten live ranges.
+                __builtin_amdgcn_sched_barrier(0);
             }
-            mfma_group(av[cb], bv[cb]);
         }
+    }
+
+    // Scheduling directive for one group: its operand reads for the next
+    // group go out one after each of the first MFMAs, so their latency is
+    // covered by the rest of the group.  (Left alone, the scheduler delays
+    // the reads to the end of the group to shorten register live ranges, and
+    // the next group's first MFMAs then wait on them.)
+    __device__ __forceinline__ static void interleave_reads_with_mfmas() {
+        constexpr int reads = FM + FN, mfmas = 4 * FM * FN;
+        static_assert(mfmas >= reads, "one MFMA per read");
+#pragma unroll
+        for (int i = 0; i < reads; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, mfmas - reads, 0);
     }
 
     __device__ __forceinline__ static void load_global(const Geo &g, f32x4 (&ra)[A_VEC], f32x4 (&rb)[R]) {
