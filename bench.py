@@ -36,12 +36,12 @@ PAGES_4096_TFLOPS = 49.8
 # HBM-side bytes per launch of the headline kernel, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by what the
 # same counter reads for a plain 256 MiB device copy (FETCH_SIZE 2.0, WRITE_SIZE
-# 1.0); see profiles/sgemm_4096_mfma_256x256x32_w8_counters.md.  Valid only for
+# 1.0); see profiles/sgemm_4096_mfma_256x256x16_counters.md.  Valid only for
 # the kernel sources they were taken on (digest below); otherwise reported null.
 TRAFFIC = {
-    "kernel": "mfma_256x256x32_w8", "workload": "sgemm_4096",
-    "source_digest": "e4b3520ab7202d64",
-    "bytes": 469919218,
+    "kernel": "mfma_256x256x16", "workload": "sgemm_4096",
+    "source_digest": "366698cf35f68534",
+    "bytes": 469861879,
 }
 KERNEL_SOURCES = ("fp32_sgemm_f32_amd/csrc/gemm_mfma.hip", "fp32_sgemm_f32_amd/csrc/gemm_common.h")
 

@@ -34,7 +34,10 @@ CFG_MFMA_256x256x32_W8 = 6
 CFG_MFMA_128x128x32_W8 = 7
 CFG_MFMA_64x64x32 = 8
 CFG_MFMA_128x64x32 = 9
-NUM_CFGS = 10
+CFG_MFMA_64x64x64 = 10
+CFG_MFMA_128x128x64 = 11
+CFG_MFMA_64x64x128 = 12
+NUM_CFGS = 13
 CFG_NAMES = {
     CFG_AUTO: "auto",
     CFG_MFMA_256x256x16: "mfma_256x256x16",
@@ -46,6 +49,9 @@ CFG_NAMES = {
     CFG_MFMA_128x128x32_W8: "mfma_128x128x32_w8",
     CFG_MFMA_64x64x32: "mfma_64x64x32",
     CFG_MFMA_128x64x32: "mfma_128x64x32",
+    CFG_MFMA_64x64x64: "mfma_64x64x64",
+    CFG_MFMA_128x128x64: "mfma_128x128x64",
+    CFG_MFMA_64x64x128: "mfma_64x64x128",
 }
 # (tile_m, tile_n, tile_k) of each configuration.
 CFG_TILES = {
@@ -53,7 +59,8 @@ CFG_TILES = {
     CFG_MFMA_256x256x32: (256, 256, 32), CFG_MFMA_256x128x32: (256, 128, 32),
     CFG_VALU_128x128x8: (128, 128, 8), CFG_MFMA_256x256x32_W8: (256, 256, 32),
     CFG_MFMA_128x128x32_W8: (128, 128, 32), CFG_MFMA_64x64x32: (64, 64, 32),
-    CFG_MFMA_128x64x32: (128, 64, 32),
+    CFG_MFMA_128x64x32: (128, 64, 32), CFG_MFMA_64x64x64: (64, 64, 64),
+    CFG_MFMA_128x128x64: (128, 128, 64), CFG_MFMA_64x64x128: (64, 64, 128),
 }
 
 # Schedules (SGEMM_SCHED_*).

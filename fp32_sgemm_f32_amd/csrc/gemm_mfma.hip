@@ -35,9 +35,10 @@ namespace sgemm {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N>
+template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int PF_ = 1>
 struct MfmaCore {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int PF = PF_;                // chunks of global loads in flight (register sets)
     static constexpr int NT = 64 * WAVES_M * WAVES_N;
     static constexpr int WTM = BM / WAVES_M;      // wave tile rows
     static constexpr int WTN = BN / WAVES_N;      // wave tile columns
@@ -63,6 +64,7 @@ struct MfmaCore {
     static_assert((R == 1 || R == 2 || R == 4 || R == 8) && R * NT * 4 == BK * BN,
                   "B tile must split into R x 4 blocks");
     static_assert((LDK / 4) % 2 == 1, "row stride must be 4 x odd words");
+    static_assert(PF == 1 || PF == 2, "prefetch depth");
     static_assert((BK / R) % RL == 0 && NT % (RL * (BN / 4)) == 0, "B loader lane map must tile the chunk");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
 
@@ -89,23 +91,26 @@ struct MfmaCore {
 
     // K loop over chunks [k0, k1) of tile (tm, tn).  A chunk is G groups of
     // four MFMA steps.  Schedule of chunk c (two LDS stages, two register
-    // sets of operands, one barrier):
+    // sets of operands, PF register sets of global loads, one barrier):
     //
     //   group 0:        read operands of group 1          | MFMAs of group 0
-    //                   store chunk c+1 (loaded during chunk c-1) to the
-    //                   other stage, issue global loads of chunk c+2
+    //                   store chunk c+1 (loaded PF chunks ago) to the other
+    //                   stage, issue global loads of chunk c+1+PF into the
+    //                   register set just freed
     //   group g < G-1:  read operands of group g+1        | MFMAs of group g
     //   group G-1:      barrier,
     //                   read operands of group 0 of c+1   | MFMAs of group G-1
     //
     // The LDS stores land early in the chunk, so the barrier has nothing to
     // wait for but the other waves; the last group's MFMAs cover the barrier
-    // and the next chunk's first LDS reads; the global loads have a whole
-    // chunk to land.  Stage safety: the stage written in chunk c held chunk
-    // c-1, whose reads all finished before the barrier ending chunk c-1; the
-    // barrier ending chunk c orders those writes before their reads and every
-    // read of chunk c's stage before its next write (in chunk c+1).  Chunks
-    // are unrolled in pairs so that stage and register set are compile-time.
+    // and the next chunk's first LDS reads; the global loads have PF whole
+    // chunks to land (two where registers allow: under full load the memory
+    // latency exceeds one chunk of 256x256x16).  Stage safety: the stage
+    // written in chunk c held chunk c-1, whose reads all finished before the
+    // barrier ending chunk c-1; the barrier ending chunk c orders those writes
+    // before their reads and every read of chunk c's stage before its next
+    // write (in chunk c+1).  Chunks are unrolled in pairs so that stage and
+    // register sets are compile-time.
     __device__ __forceinline__ void mainloop(const KernelArgs &a, float *lds, int tm, int tn,
                                              int k0, int k1) {
         const int tid = threadIdx.x;
@@ -135,29 +140,36 @@ struct MfmaCore {
             g.fb = A_STAGE + (wn * WTN + lr) * LDK + lh * KH;
         }
 
-        f32x4 ra[A_VEC], rb[R];
+        f32x4 ra[PF][A_VEC], rb[PF][R];
         f32x4 av[2][FM], bv[2][FN];
 
         const int nch = k1 - k0;
-        // Prologue: chunk 0 into stage 0, chunk 1 in flight, group 0 operands.
-        load_global(g, ra, rb);
-        __syncthreads();                 // LDS may still be read by a previous tile
-        store_lds(lds, g, ra, rb);
-        __syncthreads();
-        if (nch > 1) {
+        // Prologue: chunk 0 into stage 0, chunks 1 .. PF in flight (chunk j in
+        // register set j % PF), group 0 operands.
+        load_global(g, ra[0], rb[0]);
+        if (PF == 2 && nch > 1) {
             g.ga += BK;
             g.gb += g.gb_chunk;
-            load_global(g, ra, rb);
+            load_global(g, ra[PF - 1], rb[PF - 1]);
+        }
+        __syncthreads();                 // LDS may still be read by a previous tile
+        store_lds(lds, g, ra[0], rb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        if (nch > PF) {
+            g.ga += BK;
+            g.gb += g.gb_chunk;
+            load_global(g, ra[0], rb[0]);
             __builtin_amdgcn_sched_barrier(0);
         }
         read_operands(lds, 0, g, av[0], bv[0]);
 
-        // Steady state without branches (chunks c, c+1 both have two more
-        // chunks after them), so that no control-flow merge forces the
-        // compiler to wait for outstanding LDS reads before the MFMAs; then
-        // the last chunks with their conditions.
+        // Steady state without branches (every condition of chunks c, c+1
+        // holds), so that no control-flow merge forces the compiler to wait
+        // for outstanding LDS reads before the MFMAs; then the last chunks
+        // with their conditions.
         int c = 0;
-        for (; c + 3 < nch; c += 2) {
+        for (; c + PF + 2 < nch; c += 2) {
             chunk<0, true>(c, nch, lds, g, ra, rb, av, bv);
             chunk<1, true>(c + 1, nch, lds, g, ra, rb, av, bv);
         }
@@ -168,10 +180,11 @@ struct MfmaCore {
     }
 
     template <int ST, bool STEADY>
-    __device__ __forceinline__ void chunk(int c, int nch, float *lds, Geo &g, f32x4 (&ra)[A_VEC],
-                                          f32x4 (&rb)[R], f32x4 (&av)[2][FM], f32x4 (&bv)[2][FN]) {
+    __device__ __forceinline__ void chunk(int c, int nch, float *lds, Geo &g, f32x4 (&ra)[PF][A_VEC],
+                                          f32x4 (&rb)[PF][R], f32x4 (&av)[2][FM], f32x4 (&bv)[2][FN]) {
         const float *cur = lds + ST * STAGE;
         float *nxt = lds + (ST ^ 1) * STAGE;
+        constexpr int SET = PF == 2 ? (ST ^ 1) : 0;   // register set holding chunk c+1
         const bool more = STEADY || c + 1 < nch;
 #pragma unroll
         for (int q = 0; q < G; ++q) {
@@ -183,20 +196,57 @@ struct MfmaCore {
                 read_operands(nxt, 0, g, av[cb ^ 1], bv[cb ^ 1]);
             }
             mfma_group(av[cb], bv[cb]);
-            if (STEADY) interleave_reads_with_mfmas();
             if (q == 0 && more) {
-                store_lds(nxt, g, ra, rb);
-                __builtin_amdgcn_sched_barrier(0);   // stores free ra/rb before the loads refill them
-                if (STEADY || c + 2 < nch) {
+                store_lds(nxt, g, ra[SET], rb[SET]);
+                if (STEADY || c + 1 + PF < nch) {
                     g.ga += BK;
                     g.gb += g.gb_chunk;
-                    load_global(g, ra, rb);
+                    load_global(g, ra[SET], rb[SET]);
                 }
-                // Keep the stores and loads here: the scheduler would otherwise
-                // sink the loads next to their use to shorten live ranges.
-                __builtin_amdgcn_sched_barrier(0);
+                if (STEADY && INTERLEAVE_REFILL) {
+                    interleave_refill_group();
+                } else {
+                    // Keep the loads here: the scheduler would otherwise sink
+                    // them next to their use to shorten live ranges.
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else if (STEADY) {
+                interleave_reads_with_mfmas();
             }
         }
+    }
+
+    // Groups of at least 8 MFMAs interleave the refill with them; with fewer
+    // (64-wide wave tiles) the refill stays a block of its own, which measured
+    // faster there.
+    static constexpr bool INTERLEAVE_REFILL = 4 * FM * FN >= 8;
+
+    // Scheduling directive for group 0 of a chunk, which also refills: its
+    // operand reads, then the LDS stores of the next chunk, then the global
+    // loads of the chunk after, each placed after one MFMA, so that the wave
+    // keeps issuing MFMAs throughout (a cluster of stores and loads would
+    // stall the MFMA stream while the stores wait for their data), and the
+    // loads stay a chunk ahead of their use.
+    __device__ __forceinline__ static void interleave_refill_group() {
+        constexpr int reads = FM + FN, mfmas = 4 * FM * FN;
+        constexpr int writes = A_VEC + (R >= 4 ? R : 4), loads = A_VEC + R;
+        constexpr int paired = reads + writes + loads < mfmas ? reads + writes + loads : mfmas;
+#pragma unroll
+        for (int i = 0; i < reads; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        }
+#pragma unroll
+        for (int i = 0; i < writes; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
+        }
+#pragma unroll
+        for (int i = 0; i < loads; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+        }
+        if (mfmas > paired) __builtin_amdgcn_sched_group_barrier(0x008, mfmas - paired, 0);
     }
 
     // Scheduling directive for one group: its operand reads for the next
@@ -324,6 +374,9 @@ using Mfma256x256x32W8 = MfmaCore<256, 256, 32, 4, 2>;
 using Mfma128x128x32W8 = MfmaCore<128, 128, 32, 4, 2>;
 using Mfma64x64x32 = MfmaCore<64, 64, 32, 2, 2>;
 using Mfma128x64x32 = MfmaCore<128, 64, 32, 2, 2>;
+using Mfma64x64x64 = MfmaCore<64, 64, 64, 2, 2>;
+using Mfma128x128x64 = MfmaCore<128, 128, 64, 2, 2>;
+using Mfma64x64x128 = MfmaCore<64, 64, 128, 2, 2>;
 
 template <class Core>
 static hipError_t launch(const KernelArgs &a, hipStream_t s) {
@@ -352,6 +405,9 @@ hipError_t launch_mfma(int cfg, const KernelArgs &a, hipStream_t s) {
     case SGEMM_CFG_MFMA_128x128x32_W8: return launch<Mfma128x128x32W8>(a, s);
     case SGEMM_CFG_MFMA_64x64x32: return launch<Mfma64x64x32>(a, s);
     case SGEMM_CFG_MFMA_128x64x32: return launch<Mfma128x64x32>(a, s);
+    case SGEMM_CFG_MFMA_64x64x64: return launch<Mfma64x64x64>(a, s);
+    case SGEMM_CFG_MFMA_128x128x64: return launch<Mfma128x128x64>(a, s);
+    case SGEMM_CFG_MFMA_64x64x128: return launch<Mfma64x64x128>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -366,6 +422,9 @@ hipError_t occupancy_mfma(int cfg, int *wg_per_cu) {
     case SGEMM_CFG_MFMA_128x128x32_W8: return occ<Mfma128x128x32W8>(wg_per_cu);
     case SGEMM_CFG_MFMA_64x64x32: return occ<Mfma64x64x32>(wg_per_cu);
     case SGEMM_CFG_MFMA_128x64x32: return occ<Mfma128x64x32>(wg_per_cu);
+    case SGEMM_CFG_MFMA_64x64x64: return occ<Mfma64x64x64>(wg_per_cu);
+    case SGEMM_CFG_MFMA_128x128x64: return occ<Mfma128x128x64>(wg_per_cu);
+    case SGEMM_CFG_MFMA_64x64x128: return occ<Mfma64x64x128>(wg_per_cu);
     default: return hipErrorInvalidValue;
     }
 }

@@ -24,7 +24,10 @@ const CfgInfo kCfgs[] = {
     {SGEMM_CFG_MFMA_256x256x32_W8, 256, 256, 32, 512, true, 1, "mfma_256x256x32_w8"},
     {SGEMM_CFG_MFMA_128x128x32_W8, 128, 128, 32, 512, true, 2, "mfma_128x128x32_w8"},
     {SGEMM_CFG_MFMA_64x64x32, 64, 64, 32, 256, true, 4, "mfma_64x64x32"},
-    {SGEMM_CFG_MFMA_128x64x32, 128, 64, 32, 256, true, 3, "mfma_128x64x32"},
+    {SGEMM_CFG_MFMA_128x64x32, 128, 64, 32, 256, true, 2, "mfma_128x64x32"},
+    {SGEMM_CFG_MFMA_64x64x64, 64, 64, 64, 256, true, 2, "mfma_64x64x64"},
+    {SGEMM_CFG_MFMA_128x128x64, 128, 128, 64, 256, true, 1, "mfma_128x128x64"},
+    {SGEMM_CFG_MFMA_64x64x128, 64, 64, 128, 256, true, 1, "mfma_64x64x128"},
 };
 const int kNumCfgs = SGEMM_NUM_CFGS;
 
@@ -63,18 +66,17 @@ static int64_t tiles_of(int cfg, int M, int N) {
 }
 
 // Automatic choice, from timings of the configurations on MI355X (256 CUs):
-//   * 256x256 tiles (8 waves) when every CU gets at least one: the highest
-//     per-CU MFMA utilisation;
-//   * else 128x64 tiles when that gives two or more per CU (two workgroups
-//     per CU hide each other's barrier and memory stalls);
-//   * else, for long K (K >= 4 max(M, N)), 128x128 tiles with the K range
-//     split over the CUs (Stream-K);
-//   * else 64x64 tiles, whole.
+//   * 256x256x16 tiles (8 waves) when every CU gets at least one: the
+//     highest per-CU MFMA utilisation (148 TFLOP/s at 4096^3);
+//   * else 128x128x32 tiles with 8 waves when every CU gets one (132 at 2048^3);
+//   * else, for long K (K >= 4 max(M, N)), 128x128x32 tiles with the K range
+//     split over the CUs (Stream-K; 128 at 1024x1024x16384);
+//   * else 64x64 tiles, whole (84 at 1024^3).
 static int auto_config(int M, int N, int K, int cus) {
-    const int big = SGEMM_CFG_MFMA_256x256x32_W8, mid = SGEMM_CFG_MFMA_128x64x32,
+    const int big = SGEMM_CFG_MFMA_256x256x16, mid = SGEMM_CFG_MFMA_128x128x32_W8,
               skc = SGEMM_CFG_MFMA_128x128x32, small = SGEMM_CFG_MFMA_64x64x32;
     if (fits(kCfgs[big], M, N, K) && tiles_of(big, M, N) >= cus) return big;
-    if (fits(kCfgs[mid], M, N, K) && tiles_of(mid, M, N) >= 2LL * cus) return mid;
+    if (fits(kCfgs[mid], M, N, K) && tiles_of(mid, M, N) >= cus) return mid;
     const int mn = M > N ? M : N;
     if (fits(kCfgs[skc], M, N, K) && (int64_t)K >= 4LL * mn) return skc;
     return small;

@@ -73,7 +73,10 @@ extern "C" {
 #define SGEMM_CFG_MFMA_128x128x32_W8 7 /* 512 threads, 8 waves of 32x64 */
 #define SGEMM_CFG_MFMA_64x64x32     8  /* 256 threads, 4 waves of 32x32 */
 #define SGEMM_CFG_MFMA_128x64x32    9  /* 256 threads, 4 waves of 64x32 */
-#define SGEMM_NUM_CFGS              10 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
+#define SGEMM_CFG_MFMA_64x64x64     10 /* 256 threads, 4 waves of 32x32 */
+#define SGEMM_CFG_MFMA_128x128x64   11 /* 256 threads, 4 waves of 64x64 */
+#define SGEMM_CFG_MFMA_64x64x128    12 /* 256 threads, 4 waves of 32x32 */
+#define SGEMM_NUM_CFGS              13 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
 
 /* Schedules. */
 #define SGEMM_SCHED_AUTO     0  /* whole tiles in full waves, Stream-K for the rest */

@@ -13,7 +13,7 @@ import pytest
 
 import fp32_sgemm_f32_amd as sg
 
-OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2]
+OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1]
 
 
 def logical_ids(p):
@@ -168,9 +168,9 @@ def test_full_waves_first_then_split():
 def test_auto_choices_on_256_cus():
     occ = OCC
     p = sg.plan(4096, 4096, 4096, num_cus=256, occupancy=occ)
-    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_256x256x32_W8, sg.SCHED_DP, 256)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_256x256x16, sg.SCHED_DP, 256)
     p = sg.plan(2048, 2048, 2048, num_cus=256, occupancy=occ)
-    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_128x64x32, sg.SCHED_DP, 512)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_128x128x32_W8, sg.SCHED_DP, 256)
     p = sg.plan(1024, 1024, 1024, num_cus=256, occupancy=occ)
     assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_64x64x32, sg.SCHED_DP, 256)
     p = sg.plan(1024, 1024, 16384, num_cus=256, occupancy=occ)
