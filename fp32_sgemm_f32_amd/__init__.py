@@ -37,7 +37,14 @@ CFG_MFMA_128x64x32 = 9
 CFG_MFMA_64x64x64 = 10
 CFG_MFMA_128x128x64 = 11
 CFG_MFMA_64x64x128 = 12
-NUM_CFGS = 13
+CFG_DL_64x64x32 = 13
+CFG_DL_64x64x64_K2 = 14
+CFG_DL_128x128x32 = 15
+CFG_DL_256x256x16 = 16
+CFG_DL_64x64x32_K2 = 17
+CFG_DL_128x128x32_K2 = 18
+CFG_DL_64x64x64 = 19
+NUM_CFGS = 20
 CFG_NAMES = {
     CFG_AUTO: "auto",
     CFG_MFMA_256x256x16: "mfma_256x256x16",
@@ -52,6 +59,13 @@ CFG_NAMES = {
     CFG_MFMA_64x64x64: "mfma_64x64x64",
     CFG_MFMA_128x128x64: "mfma_128x128x64",
     CFG_MFMA_64x64x128: "mfma_64x64x128",
+    CFG_DL_64x64x32: "dl_64x64x32",
+    CFG_DL_64x64x64_K2: "dl_64x64x64_k2",
+    CFG_DL_128x128x32: "dl_128x128x32",
+    CFG_DL_256x256x16: "dl_256x256x16",
+    CFG_DL_64x64x32_K2: "dl_64x64x32_k2",
+    CFG_DL_128x128x32_K2: "dl_128x128x32_k2",
+    CFG_DL_64x64x64: "dl_64x64x64",
 }
 # (tile_m, tile_n, tile_k) of each configuration.
 CFG_TILES = {
@@ -61,6 +75,10 @@ CFG_TILES = {
     CFG_MFMA_128x128x32_W8: (128, 128, 32), CFG_MFMA_64x64x32: (64, 64, 32),
     CFG_MFMA_128x64x32: (128, 64, 32), CFG_MFMA_64x64x64: (64, 64, 64),
     CFG_MFMA_128x128x64: (128, 128, 64), CFG_MFMA_64x64x128: (64, 64, 128),
+    CFG_DL_64x64x32: (64, 64, 32), CFG_DL_64x64x64_K2: (64, 64, 64),
+    CFG_DL_128x128x32: (128, 128, 32), CFG_DL_256x256x16: (256, 256, 16),
+    CFG_DL_64x64x32_K2: (64, 64, 32), CFG_DL_128x128x32_K2: (128, 128, 32),
+    CFG_DL_64x64x64: (64, 64, 64),
 }
 
 # Schedules (SGEMM_SCHED_*).

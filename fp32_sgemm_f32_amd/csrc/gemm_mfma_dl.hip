@@ -1,0 +1,528 @@
+// FP32 GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x2_f32) with the
+// tiles moved from global memory straight into LDS (global_load_lds_dwordx4).
+//
+// The register-staged core (gemm_mfma.hip) loads a chunk into VGPRs and
+// writes it to LDS a chunk later; a wave whose data has not arrived stalls
+// on that write, and with one wave per SIMD (the 64x64 tiles that fill 256
+// CUs at 1024 x 1024) the matrix core idles with it.  Here each lane names
+// the global address of 16 bytes and the load itself deposits them in LDS,
+// in lane order: no staging registers, no LDS write instructions, and the
+// loads of a chunk may stay in flight for S-1 chunks of MFMAs (a ring of S
+// LDS stages).  This is the role asynchronous global->shared copies play in
+// "Beyond Kernel 7: Closing the Gap to cuBLAS on an H100 FP32 GEMM" (kernel
+// 8, the multi-stage pipeline).
+//
+// LDS layout of one stage (a DMA instruction fills 1 KiB in lane order, so
+// the layout is chosen through the global address each lane loads):
+//   * A (BM x BK, k-contiguous rows of BK floats, no padding): the 16-byte
+//     quad Q of row r is stored at quad position Q ^ swz(r).  With the XOR
+//     the operand reads below (one quad of 8 or 16 consecutive rows per
+//     phase) hit distinct banks in both a 32-bank and a 64-bank LDS.
+//   * B (BK x BN, n-contiguous rows as in memory).
+// Operands: as in the register-staged core, lane half h (lanes 32h..32h+31)
+// handles k in [h*BK/2, (h+1)*BK/2), so one ds_read_b128 of A feeds four
+// MFMA steps.  B is read along n: the wave's FN column blocks are
+// interleaved, column FN*l + j of the wave tile belonging to block j, so a
+// lane's FN columns for one k are adjacent (one b32/b64/b128 read per step),
+// and the epilogue writes FN adjacent floats per store.
+//
+// Synchronisation of the ring (chunk c in stage c % S, S >= 3): chunks
+// 0 .. S-2 are loaded up front; during chunk c the loads of chunk c+S-1 go
+// out, spread over its groups, into the stage of chunk c-1.  Each chunk has
+// one barrier, LA groups before its end: before it a wave waits until its
+// loads of chunk c+1 have landed (S-3 later chunks and the part of chunk
+// c+S-1 issued so far may stay in flight) and its LDS reads of chunk c are
+// done; after it the waves read chunk c+1.  The compiler does not order
+// these loads against LDS reads, so the waits and the barrier are explicit
+// (s_waitcnt vmcnt(N)).
+#include <utility>
+
+#include "gemm_common.h"
+#include "kernels.h"
+
+namespace sgemm {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8; a field at its maximum does not wait.
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_counts() {
+    static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+    constexpr int imm = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8);
+    __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// Workgroup barrier that is also a compiler barrier for memory operations.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// LDS byte address of a pointer into the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const float *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float *)p;
+}
+
+// Operand reads from LDS.  They are issued as instructions of their own and
+// waited for explicitly (lgkmcnt), so that reads for two groups ahead may be
+// in flight: the compiler's own waits for these loads drain every
+// outstanding LDS read.
+template <int OFF>
+__device__ __forceinline__ f32x4 lds_read4(uint32_t addr) {
+    f32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ f32x2 lds_read2(uint32_t addr) {
+    f32x2 v;
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ float lds_read1(uint32_t addr) {
+    float v;
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+// One LDS-DMA load: 16 bytes per lane from base + voff (a uniform 64-bit
+// base and a per-lane 32-bit offset, so the address costs no vector ALU
+// instruction) into LDS at m0 + 16 * lane.  m0 is set here; nothing else in
+// these kernels keeps a value in it (gfx9 LDS instructions do not read it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t m0v) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0v)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int FN>
+struct BVec;
+template <>
+struct BVec<1> { typedef float T; };
+template <>
+struct BVec<2> { typedef f32x2 T; };
+template <>
+struct BVec<4> { typedef f32x4 T; };
+
+// KSPLIT = 2 splits every chunk's K range between two groups of waves
+// (sliced K): with one tile per CU the SIMDs then hold two waves each, one
+// issuing MFMAs while the other waits; the groups' sums are added through
+// LDS at the end of the tile.
+template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int S_, int KSPLIT = 1, int LA_ = 1>
+struct MfmaDlCore {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
+    static constexpr int LA = LA_;                  // groups of operand reads ahead of the MFMAs
+    static constexpr int NS = LA == 1 ? 2 : 4;      // operand register sets
+    static constexpr int NW_MN = WAVES_M * WAVES_N;   // waves per K group
+    static constexpr int NW = NW_MN * KSPLIT;
+    static constexpr int NT = 64 * NW;
+    static constexpr int NT_MN = 64 * NW_MN;          // threads holding the result
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    static constexpr int KW = BK / KSPLIT;         // k values per wave per chunk
+    static constexpr int KH = KW / 2;              // k values per lane half per chunk
+    static constexpr int G = KH / 4;               // groups of four MFMA steps per chunk
+    static constexpr int QPR = BK / 4;             // quads per A row
+    static constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    static constexpr int LDS_FLOATS = S * STAGE;
+    static constexpr int A_INSTR = A_STAGE / 256, B_INSTR = B_STAGE / 256;   // 1 KiB DMA blocks
+    static constexpr int A_PW = A_INSTR / NW, B_PW = B_INSTR / NW;           // per wave
+    static constexpr int L = A_PW + B_PW;          // loads per wave per chunk
+    static constexpr int A_RPI = 256 / BK;         // A rows per DMA block
+    static constexpr int B_RPI = 256 / BN;         // B k-rows per DMA block
+    static constexpr int TILE_FLOATS = BM * BN;
+    typedef typename BVec<FN>::T bvec;
+
+    static_assert(WTM % 32 == 0 && (FN == 1 || FN == 2 || FN == 4), "wave tile");
+    static_assert(BK == 16 || BK == 32 || BK == 64, "A swizzle defined for BK 16/32/64");
+    static_assert(KSPLIT == 1 || KSPLIT == 2, "K groups");
+    static_assert(LA == 1 || LA == 2, "read-ahead depth");
+    static_assert(G > LA && G % NS == 0, "operand register sets rotate by group; the rotation must carry");
+    static_assert(BN <= 256 && 256 % BN == 0, "B DMA block = whole k-rows");
+    static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0 && A_PW >= 1 && B_PW >= 1,
+                  "DMA blocks must split evenly over the waves");
+    static_assert(S >= 3 && L * (S - 2) < 64, "ring depth (loads run S-2 chunks ahead) / vmcnt range");
+    static_assert(LDS_FLOATS * 4 + 16 <= 160 * 1024, "LDS budget");
+    static_assert(KSPLIT == 1 || TILE_FLOATS <= LDS_FLOATS, "room to add the K groups' sums");
+
+    floatx16 acc[FM][FN];
+
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    }
+
+    // Quad position of quad Q of A row r is Q ^ swz(r).
+    __device__ __forceinline__ static int swz(int r) {
+        if constexpr (BK == 16) return ((r >> 1) ^ (r >> 3)) & 3;
+        else if constexpr (BK == 32) return (r ^ (r >> 3)) & 7;
+        else return r & 15;
+    }
+
+    // Per-lane addressing, computed once per tile.  The main loop holds no
+    // vector ALU instruction: on gfx950 one between two dependent MFMAs
+    // stalls the second for most of an MFMA's duration, so every address
+    // the loop needs is either a register set up here or a scalar.
+    struct Geo {
+        const char *ga, *gb;     // uniform: A / B source of the next chunk to load
+        int64_t a_step, b_step;  // uniform: bytes per chunk
+        uint32_t va[A_PW];       // this lane's byte offset in each of its A DMA blocks
+        uint32_t vb[B_PW];
+        uint32_t ra[S][FM][G];   // LDS byte address of the A operands of group q, per stage
+        uint32_t rb[S];          // LDS byte address of the B operand of step 0, per stage
+        uint32_t lds;            // uniform: LDS byte address of the ring
+        int wave;
+    };
+
+    __device__ __forceinline__ void setup(Geo &g, const KernelArgs &a, float *lds, int tm, int tn, int k0) const {
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+        for (int u = 0; u < A_PW; ++u) {
+            const int blk = g.wave + NW * u;
+            const int r = blk * A_RPI + lane / QPR;
+            const int q = (lane % QPR) ^ swz(r);
+            g.va[u] = (uint32_t)(((int64_t)r * a.lda + 4 * q) * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < B_PW; ++u) {
+            const int blk = g.wave + NW * u;
+            const int kr = blk * B_RPI + lane / (BN / 4);
+            g.vb[u] = (uint32_t)(((int64_t)kr * a.ldb + 4 * (lane % (BN / 4))) * 4);
+        }
+        g.ga = (const char *)(a.A + (int64_t)tm * BM * a.lda + (int64_t)k0 * BK);
+        g.gb = (const char *)(a.B + (int64_t)k0 * BK * a.ldb + (int64_t)tn * BN);
+        g.a_step = (int64_t)BK * 4;
+        g.b_step = (int64_t)BK * a.ldb * 4;
+        const int kg = g.wave / NW_MN, wmn = g.wave % NW_MN;
+        const int wm = wmn / WAVES_N, wn = wmn % WAVES_N;
+        const int lr = lane & 31, lh = lane >> 5;
+        const uint32_t base = lds_addr(lds);
+        g.lds = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * WTM + i * 32 + lr;
+#pragma unroll
+                for (int q = 0; q < G; ++q)
+                    g.ra[st][i][q] = base + 4 * (st * STAGE + r * BK + 4 * ((kg * (KW / 4) + lh * G + q) ^ swz(r)));
+            }
+            g.rb[st] = base + 4 * (st * STAGE + A_STAGE + (kg * KW + lh * KH) * BN + wn * WTN + FN * lr);
+        }
+    }
+
+    // DMA instruction d (A blocks first, then B blocks) of this wave for the
+    // chunk at g.ga / g.gb into stage ST.
+    template <int ST>
+    __device__ __forceinline__ static void issue_one(const Geo &g, int d) {
+        if (d < A_PW)
+            dma16(g.ga, g.va[d], g.lds + 4 * (ST * STAGE + (g.wave + NW * d) * 256));
+        else
+            dma16(g.gb, g.vb[d - A_PW], g.lds + 4 * (ST * STAGE + A_STAGE + (g.wave + NW * (d - A_PW)) * 256));
+    }
+
+    __device__ __forceinline__ static void advance(Geo &g) {
+        g.ga += g.a_step;
+        g.gb += g.b_step;
+    }
+
+    // Operands of group TQ (four MFMA steps) from stage ST: R = FM + 4
+    // read instructions.
+    static constexpr int R = FM + 4;
+    template <int OFF>
+    __device__ __forceinline__ static bvec read_bvec(uint32_t addr) {
+        if constexpr (FN == 1) return lds_read1<OFF>(addr);
+        else if constexpr (FN == 2) return lds_read2<OFF>(addr);
+        else return lds_read4<OFF>(addr);
+    }
+    template <int ST, int TQ>
+    __device__ __forceinline__ static void read_group(const Geo &g, f32x4 (&av)[FM], bvec (&bv)[4]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) av[i] = lds_read4<0>(g.ra[ST][i][TQ]);
+        bv[0] = read_bvec<(4 * TQ + 0) * BN * 4>(g.rb[ST]);
+        bv[1] = read_bvec<(4 * TQ + 1) * BN * 4>(g.rb[ST]);
+        bv[2] = read_bvec<(4 * TQ + 2) * BN * 4>(g.rb[ST]);
+        bv[3] = read_bvec<(4 * TQ + 3) * BN * 4>(g.rb[ST]);
+    }
+
+    __device__ __forceinline__ static float bcomp(const bvec &v, int j) {
+        if constexpr (FN == 1) return v;
+        else return v[j];
+    }
+
+    __device__ __forceinline__ void mfma_step(const f32x4 (&av)[FM], const bvec &b, int u) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][u], bcomp(b, j), acc[i][j], 0, 0, 0);
+    }
+
+    // DMA instructions [dma_lo(q), dma_lo(q+1)) go out in group q: the
+    // loads of a chunk are spread over the groups of the chunk before (a
+    // wave issues one such load every few dozen cycles; a burst would
+    // stall its MFMAs).
+    __device__ __forceinline__ static constexpr int dma_lo(int q) { return q * L / G; }
+
+    // Group Q of chunk c, in stage ST.  Stage ST+1 holds chunk c+1; stage
+    // ST-1 (free since the barrier of chunk c-1) receives chunk c+S-1 over
+    // the course of the chunk (STEADY only: the last S-1 chunks load
+    // nothing).
+    //   * The group's operands were read LA groups earlier: wait for them,
+    //     then its first MFMA step.
+    //   * Group G-LA holds the chunk's barrier: once chunk c+1 has landed
+    //     (loads of later chunks may stay in flight: S-3 whole chunks and
+    //     what the groups before issued of chunk c+S-1) and this wave's
+    //     reads of chunk c are done, the waves may move on to chunk c+1.
+    //   * The reads for group Q+LA (of this chunk or the next), then the
+    //     group's DMA instructions, then the other three MFMA steps.
+    template <int ST, int Q>
+    __device__ __forceinline__ void group(Geo &g, int c, int nch, f32x4 (&av)[NS][FM], bvec (&bv)[NS][4]) {
+        // Whether this chunk still loads (c <= nch - S), as a scalar register:
+        // a boolean carried across blocks would be kept in a vector register,
+        // and set and tested with vector ALU instructions.
+        int steady_s;
+        asm("s_cmp_le_i32 %1, %2\n\ts_cselect_b32 %0, 1, 0" : "=s"(steady_s) : "s"(c), "s"(nch - S) : "scc");
+#define SGEMM_DL_STEADY (steady_s != 0)
+        constexpr int cs = Q % NS, TQ = Q + LA, ts = TQ % NS;
+        constexpr int NXT = (ST + 1) % S, PRV = (ST + S - 1) % S;
+        wait_counts<63, (LA - 1) * R>();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(av[cs], bv[cs][0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (TQ < G) {
+            read_group<ST, TQ>(g, av[ts], bv[ts]);
+        } else {
+            if constexpr (TQ == G) {
+                if (SGEMM_DL_STEADY) wait_counts<L * (S - 3) + dma_lo(G - LA), 0>();
+                else wait_counts<0, 0>();
+                lds_barrier();
+            }
+            read_group<NXT, TQ - G>(g, av[ts], bv[ts]);
+        }
+        if (SGEMM_DL_STEADY) {
+#pragma unroll
+            for (int d = dma_lo(Q); d < dma_lo(Q + 1); ++d) issue_one<PRV>(g, d);
+            if constexpr (Q == G - 1) advance(g);
+        }
+#undef SGEMM_DL_STEADY
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 1; u < 4; ++u) mfma_step(av[cs], bv[cs][u], u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    template <int ST, int... Qs>
+    __device__ __forceinline__ void chunk_groups(std::integer_sequence<int, Qs...>, Geo &g, int c, int nch,
+                                                 f32x4 (&av)[NS][FM], bvec (&bv)[NS][4]) {
+        (group<ST, Qs>(g, c, nch, av, bv), ...);
+    }
+
+    // Chunks ST, ST+1, ... of the ring from chunk c on; true once chunk
+    // nch-1 is done.  Chunk c loads chunk c+S-1 while c <= nch-S.
+    template <int ST>
+    __device__ __forceinline__ bool chunks_from(int &c, int nch, Geo &g, f32x4 (&av)[NS][FM],
+                                                bvec (&bv)[NS][4]) {
+        chunk_groups<ST>(std::make_integer_sequence<int, G>{}, g, c, nch, av, bv);
+        if (++c >= nch) return true;
+        if constexpr (ST + 1 < S) return chunks_from<ST + 1>(c, nch, g, av, bv);
+        else return false;
+    }
+
+    template <int ST>
+    __device__ __forceinline__ static void issue_prologue(Geo &g, int nch) {
+        if constexpr (ST < S - 1) {
+            if (ST < nch) {
+#pragma unroll
+                for (int d = 0; d < L; ++d) issue_one<ST>(g, d);
+                advance(g);
+                issue_prologue<ST + 1>(g, nch);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void mainloop(const KernelArgs &a, float *lds, int tm, int tn, int k0, int k1) {
+        Geo g;
+        setup(g, a, lds, tm, tn, k0);
+        const int nch = k1 - k0;
+
+        // A previous tile of this workgroup may still read the ring.
+        wait_counts<0, 0>();
+        lds_barrier();
+        // Chunks 0 .. S-2 up front (stage = chunk); chunk c+S-1 is loaded
+        // during chunk c.
+        issue_prologue<0>(g, nch);
+        if (nch >= S - 1) wait_counts<L * (S - 2), 0>();
+        else wait_counts<0, 0>();
+        lds_barrier();
+
+        f32x4 av[NS][FM];
+        bvec bv[NS][4];
+        read_group<0, 0>(g, av[0], bv[0]);
+        if constexpr (LA == 2) read_group<0, 1>(g, av[1], bv[1]);
+
+        int c = 0;
+        while (!chunks_from<0>(c, nch, g, av, bv)) {
+        }
+        // The last groups read operands of a chunk that does not exist; the
+        // registers must not be reused before those reads have returned.
+        wait_counts<0, 0>();
+#pragma unroll
+        for (int v = 0; v < NS; ++v) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) asm volatile("" ::"v"(av[v][i]));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(bv[v][u]));
+        }
+
+        if constexpr (KSPLIT == 2) {
+            // Group 1 hands its sums to group 0 through the (now idle) ring.
+            const int tid = threadIdx.x;
+            const int t = tid % NT_MN;
+            wait_counts<0, 0>();
+            lds_barrier();
+            if (tid >= NT_MN) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) lds[((i * FN + j) * 16 + r) * NT_MN + t] = acc[i][j][r];
+            }
+            wait_counts<0, 0>();
+            lds_barrier();
+            if (tid < NT_MN) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[i][j][r] += lds[((i * FN + j) * 16 + r) * NT_MN + t];
+            }
+        }
+    }
+
+    // C element of block (i, j), register r, for this lane:
+    //   row = 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,  col = FN (lane % 32) + j.
+    // Only the first K group holds the result.
+    __device__ __forceinline__ void store_c(const KernelArgs &a, int tm, int tn) {
+        const int tid = threadIdx.x;
+        if (KSPLIT > 1 && tid >= NT_MN) return;
+        const int wave = tid >> 6, lane = tid & 63;
+        const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+        const int lr = lane & 31, lh = lane >> 5;
+        float *c = a.C + ((int64_t)tm * BM + wm * WTM + 4 * lh) * a.ldc + (int64_t)tn * BN + wn * WTN + FN * lr;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float *p = c + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * a.ldc;
+                if constexpr (FN == 1) {
+                    *p = acc[i][0][r];
+                } else if constexpr (FN == 2) {
+                    *(f32x2 *)p = f32x2{acc[i][0][r], acc[i][1][r]};
+                } else {
+                    *(f32x4 *)p = f32x4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
+                }
+            }
+    }
+
+    // Thread-private layout: value v of thread t (of the first K group) at
+    // p[v * NT_MN + t].
+    __device__ __forceinline__ void store_partial(float *p) {
+        const int tid = threadIdx.x;
+        if (KSPLIT > 1 && tid >= NT_MN) return;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) p[((i * FN + j) * 16 + r) * NT_MN + tid] = acc[i][j][r];
+    }
+
+    __device__ __forceinline__ void add_partial(const float *p) {
+        const int tid = threadIdx.x;
+        if (KSPLIT > 1 && tid >= NT_MN) return;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] += p[((i * FN + j) * 16 + r) * NT_MN + tid];
+                asm volatile("" ::: "memory");
+            }
+    }
+};
+
+template <class Core, bool SPLIT>
+__global__ __launch_bounds__(Core::NT) void sgemm_mfma_dl_kernel(KernelArgs a) {
+    __shared__ __attribute__((aligned(1024))) float lds[Core::LDS_FLOATS];
+    __shared__ int flag;
+    run_gemm<Core, SPLIT>(a, lds, &flag);
+    // No load may still write this workgroup's LDS once its waves are gone.
+    wait_counts<0, 0>();
+}
+
+using Dl64x64x32 = MfmaDlCore<64, 64, 32, 2, 2, 4, 1, 2>;
+using Dl64x64x64K2 = MfmaDlCore<64, 64, 64, 2, 2, 3, 2, 2>;
+using Dl128x128x32 = MfmaDlCore<128, 128, 32, 2, 2, 3, 1, 2>;
+using Dl256x256x16 = MfmaDlCore<256, 256, 16, 4, 2, 3>;
+using Dl64x64x32K2 = MfmaDlCore<64, 64, 32, 2, 2, 4, 2>;
+using Dl128x128x32K2 = MfmaDlCore<128, 128, 32, 2, 2, 3, 2>;
+using Dl64x64x64 = MfmaDlCore<64, 64, 64, 2, 2, 3, 1, 2>;
+
+template <class Core>
+static hipError_t launch(const KernelArgs &a, hipStream_t s) {
+    KernelArgs args = a;
+    void *params[] = {&args};
+    const void *f = a.sk_tiles > 0 ? (const void *)sgemm_mfma_dl_kernel<Core, true>
+                                   : (const void *)sgemm_mfma_dl_kernel<Core, false>;
+    return hipLaunchKernel(f, dim3(a.grid), dim3(Core::NT), params, 0, s);
+}
+
+template <class Core>
+static hipError_t occ(int *n) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, (const void *)sgemm_mfma_dl_kernel<Core, true>,
+                                                        Core::NT, 0);
+}
+
+#define SGEMM_DL_CONFIGS(X)                         \
+    X(SGEMM_CFG_DL_64x64x32, Dl64x64x32)            \
+    X(SGEMM_CFG_DL_64x64x64_K2, Dl64x64x64K2)       \
+    X(SGEMM_CFG_DL_128x128x32, Dl128x128x32)        \
+    X(SGEMM_CFG_DL_256x256x16, Dl256x256x16)        \
+    X(SGEMM_CFG_DL_64x64x32_K2, Dl64x64x32K2)       \
+    X(SGEMM_CFG_DL_128x128x32_K2, Dl128x128x32K2)   \
+    X(SGEMM_CFG_DL_64x64x64, Dl64x64x64)
+
+hipError_t launch_mfma_dl(int cfg, const KernelArgs &a, hipStream_t s) {
+    switch (cfg) {
+#define X(id, core) \
+    case id: return launch<core>(a, s);
+        SGEMM_DL_CONFIGS(X)
+#undef X
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t occupancy_mfma_dl(int cfg, int *wg_per_cu) {
+    switch (cfg) {
+#define X(id, core) \
+    case id: return occ<core>(wg_per_cu);
+        SGEMM_DL_CONFIGS(X)
+#undef X
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace sgemm

@@ -15,19 +15,26 @@
 namespace sgemm {
 
 const CfgInfo kCfgs[] = {
-    {SGEMM_CFG_AUTO, 0, 0, 0, 0, false, 0, "auto"},
-    {SGEMM_CFG_MFMA_256x256x16, 256, 256, 16, 512, true, 1, "mfma_256x256x16"},
-    {SGEMM_CFG_MFMA_128x128x32, 128, 128, 32, 256, true, 2, "mfma_128x128x32"},
-    {SGEMM_CFG_MFMA_256x256x32, 256, 256, 32, 256, true, 1, "mfma_256x256x32"},
-    {SGEMM_CFG_MFMA_256x128x32, 256, 128, 32, 256, true, 1, "mfma_256x128x32"},
-    {SGEMM_CFG_VALU_128x128x8, 128, 128, 8, 256, false, 2, "valu_128x128x8"},
-    {SGEMM_CFG_MFMA_256x256x32_W8, 256, 256, 32, 512, true, 1, "mfma_256x256x32_w8"},
-    {SGEMM_CFG_MFMA_128x128x32_W8, 128, 128, 32, 512, true, 2, "mfma_128x128x32_w8"},
-    {SGEMM_CFG_MFMA_64x64x32, 64, 64, 32, 256, true, 4, "mfma_64x64x32"},
-    {SGEMM_CFG_MFMA_128x64x32, 128, 64, 32, 256, true, 2, "mfma_128x64x32"},
-    {SGEMM_CFG_MFMA_64x64x64, 64, 64, 64, 256, true, 2, "mfma_64x64x64"},
-    {SGEMM_CFG_MFMA_128x128x64, 128, 128, 64, 256, true, 1, "mfma_128x128x64"},
-    {SGEMM_CFG_MFMA_64x64x128, 64, 64, 128, 256, true, 1, "mfma_64x64x128"},
+    {SGEMM_CFG_AUTO, 0, 0, 0, 0, kKindValu, 0, "auto"},
+    {SGEMM_CFG_MFMA_256x256x16, 256, 256, 16, 512, kKindMfma, 1, "mfma_256x256x16"},
+    {SGEMM_CFG_MFMA_128x128x32, 128, 128, 32, 256, kKindMfma, 2, "mfma_128x128x32"},
+    {SGEMM_CFG_MFMA_256x256x32, 256, 256, 32, 256, kKindMfma, 1, "mfma_256x256x32"},
+    {SGEMM_CFG_MFMA_256x128x32, 256, 128, 32, 256, kKindMfma, 1, "mfma_256x128x32"},
+    {SGEMM_CFG_VALU_128x128x8, 128, 128, 8, 256, kKindValu, 2, "valu_128x128x8"},
+    {SGEMM_CFG_MFMA_256x256x32_W8, 256, 256, 32, 512, kKindMfma, 1, "mfma_256x256x32_w8"},
+    {SGEMM_CFG_MFMA_128x128x32_W8, 128, 128, 32, 512, kKindMfma, 2, "mfma_128x128x32_w8"},
+    {SGEMM_CFG_MFMA_64x64x32, 64, 64, 32, 256, kKindMfma, 4, "mfma_64x64x32"},
+    {SGEMM_CFG_MFMA_128x64x32, 128, 64, 32, 256, kKindMfma, 2, "mfma_128x64x32"},
+    {SGEMM_CFG_MFMA_64x64x64, 64, 64, 64, 256, kKindMfma, 2, "mfma_64x64x64"},
+    {SGEMM_CFG_MFMA_128x128x64, 128, 128, 64, 256, kKindMfma, 1, "mfma_128x128x64"},
+    {SGEMM_CFG_MFMA_64x64x128, 64, 64, 128, 256, kKindMfma, 1, "mfma_64x64x128"},
+    {SGEMM_CFG_DL_64x64x32, 64, 64, 32, 256, kKindMfmaDl, 2, "dl_64x64x32"},
+    {SGEMM_CFG_DL_64x64x64_K2, 64, 64, 64, 512, kKindMfmaDl, 1, "dl_64x64x64_k2"},
+    {SGEMM_CFG_DL_128x128x32, 128, 128, 32, 256, kKindMfmaDl, 1, "dl_128x128x32"},
+    {SGEMM_CFG_DL_256x256x16, 256, 256, 16, 512, kKindMfmaDl, 1, "dl_256x256x16"},
+    {SGEMM_CFG_DL_64x64x32_K2, 64, 64, 32, 512, kKindMfmaDl, 2, "dl_64x64x32_k2"},
+    {SGEMM_CFG_DL_128x128x32_K2, 128, 128, 32, 512, kKindMfmaDl, 1, "dl_128x128x32_k2"},
+    {SGEMM_CFG_DL_64x64x64, 64, 64, 64, 256, kKindMfmaDl, 1, "dl_64x64x64"},
 };
 const int kNumCfgs = SGEMM_NUM_CFGS;
 
@@ -66,20 +73,38 @@ static int64_t tiles_of(int cfg, int M, int N) {
 }
 
 // Automatic choice, from timings of the configurations on MI355X (256 CUs):
-//   * 256x256x16 tiles (8 waves) when every CU gets at least one: the
-//     highest per-CU MFMA utilisation (148 TFLOP/s at 4096^3);
-//   * else 128x128x32 tiles with 8 waves when every CU gets one (132 at 2048^3);
-//   * else, for long K (K >= 4 max(M, N)), 128x128x32 tiles with the K range
-//     split over the CUs (Stream-K; 128 at 1024x1024x16384);
-//   * else 64x64 tiles, whole (84 at 1024^3).
+//   * 256x256x16 tiles (8 waves) when every CU gets at least one (149
+//     TFLOP/s at 4096^3);
+//   * else 128x128 tiles loaded straight into LDS, two K groups of waves,
+//     when every CU gets one (138 at 2048^3);
+//   * else 64x64 tiles loaded straight into LDS (142 at 1024x1024x16384,
+//     99 at 1024^3), with a 64-deep K chunk where K allows.
 static int auto_config(int M, int N, int K, int cus) {
-    const int big = SGEMM_CFG_MFMA_256x256x16, mid = SGEMM_CFG_MFMA_128x128x32_W8,
-              skc = SGEMM_CFG_MFMA_128x128x32, small = SGEMM_CFG_MFMA_64x64x32;
+    const int big = SGEMM_CFG_MFMA_256x256x16, mid = SGEMM_CFG_DL_128x128x32_K2,
+              small = SGEMM_CFG_DL_64x64x64, small32 = SGEMM_CFG_DL_64x64x32;
     if (fits(kCfgs[big], M, N, K) && tiles_of(big, M, N) >= cus) return big;
     if (fits(kCfgs[mid], M, N, K) && tiles_of(mid, M, N) >= cus) return mid;
-    const int mn = M > N ? M : N;
-    if (fits(kCfgs[skc], M, N, K) && (int64_t)K >= 4LL * mn) return skc;
-    return small;
+    if (fits(kCfgs[small], M, N, K)) return small;
+    return small32;
+}
+
+int staged_equivalent(int cfg) {
+    switch (cfg) {
+    case SGEMM_CFG_DL_64x64x32:
+    case SGEMM_CFG_DL_64x64x32_K2: return SGEMM_CFG_MFMA_64x64x32;
+    case SGEMM_CFG_DL_64x64x64:
+    case SGEMM_CFG_DL_64x64x64_K2: return SGEMM_CFG_MFMA_64x64x64;
+    case SGEMM_CFG_DL_128x128x32:
+    case SGEMM_CFG_DL_128x128x32_K2: return SGEMM_CFG_MFMA_128x128x32;
+    case SGEMM_CFG_DL_256x256x16: return SGEMM_CFG_MFMA_256x256x16;
+    default: return cfg;
+    }
+}
+
+bool dl_offsets_fit(int cfg, int64_t lda, int64_t ldb) {
+    if (kCfgs[cfg].kind != kKindMfmaDl) return true;
+    const int64_t lim = (int64_t)1 << 32;
+    return (int64_t)kCfgs[cfg].bm * lda * 4 < lim && (int64_t)kCfgs[cfg].bk * ldb * 4 < lim;
 }
 
 int make_plan(const PlanRequest &req, Plan *out) {

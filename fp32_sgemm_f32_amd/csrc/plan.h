@@ -8,11 +8,17 @@
 
 namespace sgemm {
 
+enum CfgKind {
+    kKindValu = 0,      // scalar VALU FMAs
+    kKindMfma = 1,      // matrix cores, tiles staged through registers
+    kKindMfmaDl = 2,    // matrix cores, tiles loaded straight into LDS
+};
+
 struct CfgInfo {
     int id;
     int bm, bn, bk;     // output tile and K chunk
     int threads;        // threads per workgroup
-    bool mfma;          // matrix-core FP32 product (else scalar VALU FMAs)
+    int kind;           // CfgKind: which kernel family runs it
     int default_occ;    // workgroups per CU expected from its LDS/VGPR use
     const char *name;
 };
@@ -51,6 +57,15 @@ struct Plan {
 
 // Returns an SGEMM_* status; fills *out on success.
 int make_plan(const PlanRequest &req, Plan *out);
+
+// The configurations that load tiles straight into LDS address a lane's
+// source as a 32-bit byte offset from the tile's first row (A) or the
+// chunk's first row (B): they need BM * lda and BK * ldb under 2^30 floats.
+bool dl_offsets_fit(int cfg, int64_t lda, int64_t ldb);
+
+// The register-staged configuration with the same tile as `cfg` (itself
+// for those).
+int staged_equivalent(int cfg);
 
 // Workspace layout for Stream-K: sk_tiles int counters (256-byte aligned
 // block), then sk_grid * 2 partial tiles of bm*bn floats (a split workgroup

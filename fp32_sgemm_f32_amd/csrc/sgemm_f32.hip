@@ -43,6 +43,22 @@ std::mutex g_mu;
 std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
 
+hipError_t launch_cfg(int cfg, const KernelArgs &a, hipStream_t s) {
+    switch (kCfgs[cfg].kind) {
+    case kKindMfma: return launch_mfma(cfg, a, s);
+    case kKindMfmaDl: return launch_mfma_dl(cfg, a, s);
+    default: return launch_valu(cfg, a, s);
+    }
+}
+
+hipError_t occupancy_of(int cfg, int *n) {
+    switch (kCfgs[cfg].kind) {
+    case kKindMfma: return occupancy_mfma(cfg, n);
+    case kKindMfmaDl: return occupancy_mfma_dl(cfg, n);
+    default: return occupancy_valu(cfg, n);
+    }
+}
+
 int env_int(const char *name, int dflt) {
     const char *v = std::getenv(name);
     if (!v || !*v) return dflt;
@@ -61,7 +77,7 @@ int device_info(int dev, DeviceInfo *out) {
         d.num_cus = cus;
         for (int c = 1; c < SGEMM_NUM_CFGS; ++c) {
             int n = 0;
-            e = kCfgs[c].mfma ? occupancy_mfma(c, &n) : occupancy_valu(c, &n);
+            e = occupancy_of(c, &n);
             if (e != hipSuccess) return hip_fail(e);
             d.occupancy[c] = n > 0 ? n : 1;
         }
@@ -180,6 +196,14 @@ int run(int M, int N, int K, const float *A, int lda, const float *B, int ldb, f
                     env_int("SGEMM_F32_SK_WG_PER_CU", 0)};
     Plan p;
     if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
+    if (K > 0 && !dl_offsets_fit(p.config, lda, ldb)) {
+        // Leading dimensions too large for the 32-bit source offsets of the
+        // direct-to-LDS kernels: an automatic choice falls back to the
+        // register-staged kernel of the same tile; a forced one is refused.
+        if (config != SGEMM_CFG_AUTO) return SGEMM_ERR_CONFIG;
+        req.config = staged_equivalent(p.config);
+        if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
+    }
 
     if (K == 0) {
         e = launch_fill_zero(C, M, N, ldc, stream);
@@ -205,9 +229,9 @@ int run(int M, int N, int K, const float *A, int lda, const float *B, int ldb, f
         if ((st = workspace_for(dev, stream, p, &w)) != SGEMM_OK) return st;
         a.counters = w.counters;
         a.partials = w.partials;
-        e = kCfgs[p.config].mfma ? launch_mfma(p.config, a, stream) : launch_valu(p.config, a, stream);
+        e = launch_cfg(p.config, a, stream);
     } else {
-        e = kCfgs[p.config].mfma ? launch_mfma(p.config, a, stream) : launch_valu(p.config, a, stream);
+        e = launch_cfg(p.config, a, stream);
     }
     return e == hipSuccess ? SGEMM_OK : hip_fail(e);
 }

@@ -76,7 +76,17 @@ extern "C" {
 #define SGEMM_CFG_MFMA_64x64x64     10 /* 256 threads, 4 waves of 32x32 */
 #define SGEMM_CFG_MFMA_128x128x64   11 /* 256 threads, 4 waves of 64x64 */
 #define SGEMM_CFG_MFMA_64x64x128    12 /* 256 threads, 4 waves of 32x32 */
-#define SGEMM_NUM_CFGS              13 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
+/* Tiles loaded straight from global memory into LDS (no register staging),
+ * with a ring of LDS stages; _k2: two groups of waves split each chunk's K
+ * range (two waves per SIMD with one tile per CU). */
+#define SGEMM_CFG_DL_64x64x32       13 /* 256 threads, 4 waves of 32x32, 4 stages */
+#define SGEMM_CFG_DL_64x64x64_K2    14 /* 512 threads, 2 x 4 waves of 32x32, 3 stages */
+#define SGEMM_CFG_DL_128x128x32     15 /* 256 threads, 4 waves of 64x64, 3 stages */
+#define SGEMM_CFG_DL_256x256x16     16 /* 512 threads, 8 waves of 64x128, 3 stages */
+#define SGEMM_CFG_DL_64x64x32_K2    17 /* 512 threads, 2 x 4 waves of 32x32, 4 stages */
+#define SGEMM_CFG_DL_128x128x32_K2  18 /* 512 threads, 2 x 4 waves of 64x64, 3 stages */
+#define SGEMM_CFG_DL_64x64x64       19 /* 256 threads, 4 waves of 32x32, 3 stages */
+#define SGEMM_NUM_CFGS              20 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
 
 /* Schedules. */
 #define SGEMM_SCHED_AUTO     0  /* whole tiles in full waves, Stream-K for the rest */

@@ -13,7 +13,7 @@ import pytest
 
 import fp32_sgemm_f32_amd as sg
 
-OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1]
+OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1, 2, 1, 1, 1, 2, 1, 1]
 
 
 def logical_ids(p):
@@ -170,13 +170,15 @@ def test_auto_choices_on_256_cus():
     p = sg.plan(4096, 4096, 4096, num_cus=256, occupancy=occ)
     assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_256x256x16, sg.SCHED_DP, 256)
     p = sg.plan(2048, 2048, 2048, num_cus=256, occupancy=occ)
-    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_128x128x32_W8, sg.SCHED_DP, 256)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_DL_128x128x32_K2, sg.SCHED_DP, 256)
     p = sg.plan(1024, 1024, 1024, num_cus=256, occupancy=occ)
-    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_64x64x32, sg.SCHED_DP, 256)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_DL_64x64x64, sg.SCHED_DP, 256)
     p = sg.plan(1024, 1024, 16384, num_cus=256, occupancy=occ)
-    assert (p["config"], p["sched"], p["dp_tiles"], p["grid"]) == (sg.CFG_MFMA_128x128x32, sg.SCHED_STREAMK, 0, 256)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_DL_64x64x64, sg.SCHED_DP, 256)
+    p = sg.plan(1024, 1024, 1056, num_cus=256, occupancy=occ)     # K not a multiple of 64
+    assert p["config"] == sg.CFG_DL_64x64x32
     p = sg.plan(256, 256, 256, num_cus=256, occupancy=occ)
-    assert (p["config"], p["sched"]) == (sg.CFG_MFMA_64x64x32, sg.SCHED_DP)
+    assert p["config"] == sg.CFG_DL_64x64x64
 
 
 def test_xcd_grouping_for_the_headline_shape():
