@@ -44,7 +44,9 @@ CFG_DL_256x256x16 = 16
 CFG_DL_64x64x32_K2 = 17
 CFG_DL_128x128x32_K2 = 18
 CFG_DL_64x64x64 = 19
-NUM_CFGS = 20
+CFG_DL_128x256x16 = 20
+CFG_DL_256x128x16 = 21
+NUM_CFGS = 22
 CFG_NAMES = {
     CFG_AUTO: "auto",
     CFG_MFMA_256x256x16: "mfma_256x256x16",
@@ -66,6 +68,8 @@ CFG_NAMES = {
     CFG_DL_64x64x32_K2: "dl_64x64x32_k2",
     CFG_DL_128x128x32_K2: "dl_128x128x32_k2",
     CFG_DL_64x64x64: "dl_64x64x64",
+    CFG_DL_128x256x16: "dl_128x256x16",
+    CFG_DL_256x128x16: "dl_256x128x16",
 }
 # (tile_m, tile_n, tile_k) of each configuration.
 CFG_TILES = {
@@ -78,7 +82,8 @@ CFG_TILES = {
     CFG_DL_64x64x32: (64, 64, 32), CFG_DL_64x64x64_K2: (64, 64, 64),
     CFG_DL_128x128x32: (128, 128, 32), CFG_DL_256x256x16: (256, 256, 16),
     CFG_DL_64x64x32_K2: (64, 64, 32), CFG_DL_128x128x32_K2: (128, 128, 32),
-    CFG_DL_64x64x64: (64, 64, 64),
+    CFG_DL_64x64x64: (64, 64, 64), CFG_DL_128x256x16: (128, 256, 16),
+    CFG_DL_256x128x16: (256, 128, 16),
 }
 
 # Schedules (SGEMM_SCHED_*).

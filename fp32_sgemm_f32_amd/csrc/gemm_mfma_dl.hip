@@ -480,6 +480,8 @@ using Dl256x256x16 = MfmaDlCore<256, 256, 16, 4, 2, 3>;
 using Dl64x64x32K2 = MfmaDlCore<64, 64, 32, 2, 2, 4, 2>;
 using Dl128x128x32K2 = MfmaDlCore<128, 128, 32, 2, 2, 3, 2>;
 using Dl64x64x64 = MfmaDlCore<64, 64, 64, 2, 2, 3, 1, 2>;
+using Dl128x256x16 = MfmaDlCore<128, 256, 16, 2, 2, 3>;
+using Dl256x128x16 = MfmaDlCore<256, 128, 16, 2, 2, 3>;
 
 template <class Core>
 static hipError_t launch(const KernelArgs &a, hipStream_t s) {
@@ -503,7 +505,9 @@ static hipError_t occ(int *n) {
     X(SGEMM_CFG_DL_256x256x16, Dl256x256x16)        \
     X(SGEMM_CFG_DL_64x64x32_K2, Dl64x64x32K2)       \
     X(SGEMM_CFG_DL_128x128x32_K2, Dl128x128x32K2)   \
-    X(SGEMM_CFG_DL_64x64x64, Dl64x64x64)
+    X(SGEMM_CFG_DL_64x64x64, Dl64x64x64)            \
+    X(SGEMM_CFG_DL_128x256x16, Dl128x256x16)        \
+    X(SGEMM_CFG_DL_256x128x16, Dl256x128x16)
 
 hipError_t launch_mfma_dl(int cfg, const KernelArgs &a, hipStream_t s) {
     switch (cfg) {

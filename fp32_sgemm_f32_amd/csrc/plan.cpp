@@ -35,6 +35,8 @@ const CfgInfo kCfgs[] = {
     {SGEMM_CFG_DL_64x64x32_K2, 64, 64, 32, 512, kKindMfmaDl, 2, "dl_64x64x32_k2"},
     {SGEMM_CFG_DL_128x128x32_K2, 128, 128, 32, 512, kKindMfmaDl, 1, "dl_128x128x32_k2"},
     {SGEMM_CFG_DL_64x64x64, 64, 64, 64, 256, kKindMfmaDl, 1, "dl_64x64x64"},
+    {SGEMM_CFG_DL_128x256x16, 128, 256, 16, 256, kKindMfmaDl, 2, "dl_128x256x16"},
+    {SGEMM_CFG_DL_256x128x16, 256, 128, 16, 256, kKindMfmaDl, 2, "dl_256x128x16"},
 };
 const int kNumCfgs = SGEMM_NUM_CFGS;
 

@@ -86,7 +86,9 @@ extern "C" {
 #define SGEMM_CFG_DL_64x64x32_K2    17 /* 512 threads, 2 x 4 waves of 32x32, 4 stages */
 #define SGEMM_CFG_DL_128x128x32_K2  18 /* 512 threads, 2 x 4 waves of 64x64, 3 stages */
 #define SGEMM_CFG_DL_64x64x64       19 /* 256 threads, 4 waves of 32x32, 3 stages */
-#define SGEMM_NUM_CFGS              20 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
+#define SGEMM_CFG_DL_128x256x16     20 /* 256 threads, 4 waves of 64x128, 3 stages */
+#define SGEMM_CFG_DL_256x128x16     21 /* 256 threads, 4 waves of 128x64, 3 stages */
+#define SGEMM_NUM_CFGS              22 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
 
 /* Schedules. */
 #define SGEMM_SCHED_AUTO     0  /* whole tiles in full waves, Stream-K for the rest */

@@ -13,7 +13,7 @@ import pytest
 
 import fp32_sgemm_f32_amd as sg
 
-OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1, 2, 1, 1, 1, 2, 1, 1]
+OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1, 2, 1, 1, 1, 2, 1, 1, 2, 2]
 
 
 def logical_ids(p):
