@@ -46,7 +46,8 @@ CFG_DL_128x128x32_K2 = 18
 CFG_DL_64x64x64 = 19
 CFG_DL_128x256x16 = 20
 CFG_DL_256x128x16 = 21
-NUM_CFGS = 22
+CFG_GENERIC_64x64x16 = 22
+NUM_CFGS = 23
 CFG_NAMES = {
     CFG_AUTO: "auto",
     CFG_MFMA_256x256x16: "mfma_256x256x16",
@@ -70,6 +71,7 @@ CFG_NAMES = {
     CFG_DL_64x64x64: "dl_64x64x64",
     CFG_DL_128x256x16: "dl_128x256x16",
     CFG_DL_256x128x16: "dl_256x128x16",
+    CFG_GENERIC_64x64x16: "generic_64x64x16",
 }
 # (tile_m, tile_n, tile_k) of each configuration.
 CFG_TILES = {
@@ -83,7 +85,7 @@ CFG_TILES = {
     CFG_DL_128x128x32: (128, 128, 32), CFG_DL_256x256x16: (256, 256, 16),
     CFG_DL_64x64x32_K2: (64, 64, 32), CFG_DL_128x128x32_K2: (128, 128, 32),
     CFG_DL_64x64x64: (64, 64, 64), CFG_DL_128x256x16: (128, 256, 16),
-    CFG_DL_256x128x16: (256, 128, 16),
+    CFG_DL_256x128x16: (256, 128, 16), CFG_GENERIC_64x64x16: (64, 64, 16),
 }
 
 # Schedules (SGEMM_SCHED_*).

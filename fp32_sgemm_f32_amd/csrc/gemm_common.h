@@ -24,6 +24,8 @@ struct KernelArgs {
     const float *B;
     float *C;
     int64_t lda, ldb, ldc;
+    int M, N, K;      // the shape (the edge-masking kernels need it)
+    int edge;         // the shape is not a multiple of the tile
     int tiles_m, tiles_n;
     int ipt;          // K chunks per tile
     int dp_tiles;     // tiles [0, dp_tiles) are computed whole

@@ -96,7 +96,38 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t voff, uint32_t 
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0v)
                  : "memory", "m0");
 }
+
+// The same from a buffer resource: lanes whose offset is out of the
+// resource's range (>= 2^31 here) load nothing and leave zeros in LDS.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void bdma16(i32x4 rsrc, uint32_t voff, uint32_t m0v) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+                 "s"(m0v)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// Raw buffer resource over [p, p + 2^31): base address, stride 0, 2^31
+// records, default data format.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *p) {
+    const uint64_t a = (uint64_t)p;
+    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)kOutOfRange, 0x00020000};
+}
+
+__device__ __forceinline__ void advance_rsrc(i32x4 &r, int64_t bytes) {
+    const uint64_t a = (((uint64_t)(uint32_t)r[1] << 32) | (uint32_t)r[0]) + (uint64_t)bytes;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)(uint32_t)(a >> 32);
+}
+
+// 1 if a == b, else 0, in a scalar register (a boolean would be kept in a
+// vector register and tested with vector ALU instructions).
+__device__ __forceinline__ int scalar_eq(int a, int b) {
+    int r;
+    asm("s_cmp_eq_u32 %1, %2\n\ts_cselect_b32 %0, 1, 0" : "=s"(r) : "s"(a), "s"(b) : "scc");
+    return r;
+}
 
 template <int FN>
 struct BVec;
@@ -111,7 +142,11 @@ struct BVec<4> { typedef f32x4 T; };
 // (sliced K): with one tile per CU the SIMDs then hold two waves each, one
 // issuing MFMAs while the other waits; the groups' sums are added through
 // LDS at the end of the tile.
-template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int S_, int KSPLIT = 1, int LA_ = 1>
+// EDGE: the shape need not be a multiple of the tile (N and K multiples of
+// 4): loads through buffer resources with rows / columns / k beyond the
+// matrix masked to zeros, stores masked.
+template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int S_, int KSPLIT = 1, int LA_ = 1,
+          bool EDGE = false>
 struct MfmaDlCore {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
     static constexpr int LA = LA_;                  // groups of operand reads ahead of the MFMAs
@@ -173,9 +208,12 @@ struct MfmaDlCore {
     // the loop needs is either a register set up here or a scalar.
     struct Geo {
         const char *ga, *gb;     // uniform: A / B source of the next chunk to load
+        i32x4 rsa, rsb;          // EDGE: the same as buffer resources
         int64_t a_step, b_step;  // uniform: bytes per chunk
         uint32_t va[A_PW];       // this lane's byte offset in each of its A DMA blocks
         uint32_t vb[B_PW];
+        uint32_t va_t[A_PW];     // EDGE: the same for the tile's last chunk (K tail masked)
+        uint32_t vb_t[B_PW];
         uint32_t ra[S][FM][G];   // LDS byte address of the A operands of group q, per stage
         uint32_t rb[S];          // LDS byte address of the B operand of step 0, per stage
         uint32_t lds;            // uniform: LDS byte address of the ring
@@ -186,21 +224,34 @@ struct MfmaDlCore {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        // EDGE: valid k values in the tile's last chunk (K and every chunk
+        // boundary are multiples of 4, so a quad is all in or all out).
+        const int kt = EDGE ? a.K - (a.ipt - 1) * BK : BK;
 #pragma unroll
         for (int u = 0; u < A_PW; ++u) {
             const int blk = g.wave + NW * u;
             const int r = blk * A_RPI + lane / QPR;
             const int q = (lane % QPR) ^ swz(r);
-            g.va[u] = (uint32_t)(((int64_t)r * a.lda + 4 * q) * 4);
+            const uint32_t off = (uint32_t)(((int64_t)r * a.lda + 4 * q) * 4);
+            const bool row_ok = !EDGE || tm * BM + r < a.M;
+            g.va[u] = row_ok ? off : kOutOfRange;
+            g.va_t[u] = row_ok && 4 * q < kt ? off : kOutOfRange;
         }
 #pragma unroll
         for (int u = 0; u < B_PW; ++u) {
             const int blk = g.wave + NW * u;
             const int kr = blk * B_RPI + lane / (BN / 4);
-            g.vb[u] = (uint32_t)(((int64_t)kr * a.ldb + 4 * (lane % (BN / 4))) * 4);
+            const uint32_t off = (uint32_t)(((int64_t)kr * a.ldb + 4 * (lane % (BN / 4))) * 4);
+            const bool col_ok = !EDGE || tn * BN + 4 * (lane % (BN / 4)) < a.N;
+            g.vb[u] = col_ok ? off : kOutOfRange;
+            g.vb_t[u] = col_ok && kr < kt ? off : kOutOfRange;
         }
         g.ga = (const char *)(a.A + (int64_t)tm * BM * a.lda + (int64_t)k0 * BK);
         g.gb = (const char *)(a.B + (int64_t)k0 * BK * a.ldb + (int64_t)tn * BN);
+        if constexpr (EDGE) {
+            g.rsa = buffer_rsrc(g.ga);
+            g.rsb = buffer_rsrc(g.gb);
+        }
         g.a_step = (int64_t)BK * 4;
         g.b_step = (int64_t)BK * a.ldb * 4;
         const int kg = g.wave / NW_MN, wmn = g.wave % NW_MN;
@@ -222,18 +273,40 @@ struct MfmaDlCore {
     }
 
     // DMA instruction d (A blocks first, then B blocks) of this wave for the
-    // chunk at g.ga / g.gb into stage ST.
+    // chunk at g.ga / g.gb (EDGE: g.rsa / g.rsb) into stage ST.
     template <int ST>
     __device__ __forceinline__ static void issue_one(const Geo &g, int d) {
-        if (d < A_PW)
-            dma16(g.ga, g.va[d], g.lds + 4 * (ST * STAGE + (g.wave + NW * d) * 256));
-        else
-            dma16(g.gb, g.vb[d - A_PW], g.lds + 4 * (ST * STAGE + A_STAGE + (g.wave + NW * (d - A_PW)) * 256));
+        const uint32_t m0 = g.lds + 4 * (ST * STAGE + (d < A_PW ? 0 : A_STAGE) +
+                                         (g.wave + NW * (d < A_PW ? d : d - A_PW)) * 256);
+        if constexpr (EDGE) {
+            if (d < A_PW) bdma16(g.rsa, g.va[d], m0);
+            else bdma16(g.rsb, g.vb[d - A_PW], m0);
+        } else {
+            if (d < A_PW) dma16(g.ga, g.va[d], m0);
+            else dma16(g.gb, g.vb[d - A_PW], m0);
+        }
+    }
+
+    // EDGE: before the loads of the tile's last chunk (its k beyond K
+    // masked), which are the last loads of the tile: switch to the tail
+    // offsets.  Vector moves, but once per tile.
+    // (Volatile asm moves: plain assignments would be turned into selects
+    // executed on every chunk.)
+    __device__ __forceinline__ static void mask_k_tail(Geo &g) {
+#pragma unroll
+        for (int u = 0; u < A_PW; ++u) asm volatile("v_mov_b32 %0, %1" : "=v"(g.va[u]) : "v"(g.va_t[u]));
+#pragma unroll
+        for (int u = 0; u < B_PW; ++u) asm volatile("v_mov_b32 %0, %1" : "=v"(g.vb[u]) : "v"(g.vb_t[u]));
     }
 
     __device__ __forceinline__ static void advance(Geo &g) {
-        g.ga += g.a_step;
-        g.gb += g.b_step;
+        if constexpr (EDGE) {
+            advance_rsrc(g.rsa, g.a_step);
+            advance_rsrc(g.rsb, g.b_step);
+        } else {
+            g.ga += g.a_step;
+            g.gb += g.b_step;
+        }
     }
 
     // Operands of group TQ (four MFMA steps) from stage ST: R = FM + 4
@@ -287,7 +360,8 @@ struct MfmaDlCore {
     //   * The reads for group Q+LA (of this chunk or the next), then the
     //     group's DMA instructions, then the other three MFMA steps.
     template <int ST, int Q>
-    __device__ __forceinline__ void group(Geo &g, int c, int nch, f32x4 (&av)[NS][FM], bvec (&bv)[NS][4]) {
+    __device__ __forceinline__ void group(Geo &g, int c, int nch, int tail_ch, f32x4 (&av)[NS][FM],
+                                          bvec (&bv)[NS][4]) {
         // Whether this chunk still loads (c <= nch - S), as a scalar register:
         // a boolean carried across blocks would be kept in a vector register,
         // and set and tested with vector ALU instructions.
@@ -311,6 +385,9 @@ struct MfmaDlCore {
             read_group<NXT, TQ - G>(g, av[ts], bv[ts]);
         }
         if (SGEMM_DL_STEADY) {
+            if constexpr (EDGE && Q == 0) {
+                if (scalar_eq(c + S - 1, tail_ch)) mask_k_tail(g);
+            }
 #pragma unroll
             for (int d = dma_lo(Q); d < dma_lo(Q + 1); ++d) issue_one<PRV>(g, d);
             if constexpr (Q == G - 1) advance(g);
@@ -324,29 +401,32 @@ struct MfmaDlCore {
 
     template <int ST, int... Qs>
     __device__ __forceinline__ void chunk_groups(std::integer_sequence<int, Qs...>, Geo &g, int c, int nch,
-                                                 f32x4 (&av)[NS][FM], bvec (&bv)[NS][4]) {
-        (group<ST, Qs>(g, c, nch, av, bv), ...);
+                                                 int tail_ch, f32x4 (&av)[NS][FM], bvec (&bv)[NS][4]) {
+        (group<ST, Qs>(g, c, nch, tail_ch, av, bv), ...);
     }
 
     // Chunks ST, ST+1, ... of the ring from chunk c on; true once chunk
     // nch-1 is done.  Chunk c loads chunk c+S-1 while c <= nch-S.
     template <int ST>
-    __device__ __forceinline__ bool chunks_from(int &c, int nch, Geo &g, f32x4 (&av)[NS][FM],
+    __device__ __forceinline__ bool chunks_from(int &c, int nch, int tail_ch, Geo &g, f32x4 (&av)[NS][FM],
                                                 bvec (&bv)[NS][4]) {
-        chunk_groups<ST>(std::make_integer_sequence<int, G>{}, g, c, nch, av, bv);
+        chunk_groups<ST>(std::make_integer_sequence<int, G>{}, g, c, nch, tail_ch, av, bv);
         if (++c >= nch) return true;
-        if constexpr (ST + 1 < S) return chunks_from<ST + 1>(c, nch, g, av, bv);
+        if constexpr (ST + 1 < S) return chunks_from<ST + 1>(c, nch, tail_ch, g, av, bv);
         else return false;
     }
 
     template <int ST>
-    __device__ __forceinline__ static void issue_prologue(Geo &g, int nch) {
+    __device__ __forceinline__ static void issue_prologue(Geo &g, int nch, int tail_ch) {
         if constexpr (ST < S - 1) {
             if (ST < nch) {
+                if constexpr (EDGE) {
+                    if (ST == tail_ch) mask_k_tail(g);
+                }
 #pragma unroll
                 for (int d = 0; d < L; ++d) issue_one<ST>(g, d);
                 advance(g);
-                issue_prologue<ST + 1>(g, nch);
+                issue_prologue<ST + 1>(g, nch, tail_ch);
             }
         }
     }
@@ -355,13 +435,16 @@ struct MfmaDlCore {
         Geo g;
         setup(g, a, lds, tm, tn, k0);
         const int nch = k1 - k0;
+        // EDGE: the range's last chunk is the tile's last, with k beyond K,
+        // when it reaches the end of a K not a multiple of BK.
+        const int tail_ch = __builtin_amdgcn_readfirstlane(EDGE && k1 == a.ipt && a.K % BK != 0 ? nch - 1 : -1);
 
         // A previous tile of this workgroup may still read the ring.
         wait_counts<0, 0>();
         lds_barrier();
         // Chunks 0 .. S-2 up front (stage = chunk); chunk c+S-1 is loaded
         // during chunk c.
-        issue_prologue<0>(g, nch);
+        issue_prologue<0>(g, nch, tail_ch);
         if (nch >= S - 1) wait_counts<L * (S - 2), 0>();
         else wait_counts<0, 0>();
         lds_barrier();
@@ -372,7 +455,7 @@ struct MfmaDlCore {
         if constexpr (LA == 2) read_group<0, 1>(g, av[1], bv[1]);
 
         int c = 0;
-        while (!chunks_from<0>(c, nch, g, av, bv)) {
+        while (!chunks_from<0>(c, nch, tail_ch, g, av, bv)) {
         }
         // The last groups read operands of a chunk that does not exist; the
         // registers must not be reused before those reads have returned.
@@ -414,19 +497,25 @@ struct MfmaDlCore {
 
     // C element of block (i, j), register r, for this lane:
     //   row = 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,  col = FN (lane % 32) + j.
-    // Only the first K group holds the result.
+    // Only the first K group holds the result.  EDGE: rows beyond M and
+    // columns beyond N are not written (N is a multiple of 4, so a lane's FN
+    // adjacent columns are all in or all out).
     __device__ __forceinline__ void store_c(const KernelArgs &a, int tm, int tn) {
         const int tid = threadIdx.x;
         if (KSPLIT > 1 && tid >= NT_MN) return;
         const int wave = tid >> 6, lane = tid & 63;
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
         const int lr = lane & 31, lh = lane >> 5;
-        float *c = a.C + ((int64_t)tm * BM + wm * WTM + 4 * lh) * a.ldc + (int64_t)tn * BN + wn * WTN + FN * lr;
+        const int row0 = tm * BM + wm * WTM + 4 * lh, col0 = tn * BN + wn * WTN + FN * lr;
+        if (EDGE && col0 >= a.N) return;
+        float *c = a.C + (int64_t)row0 * a.ldc + col0;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float *p = c + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * a.ldc;
+                const int dr = i * 32 + 8 * (r >> 2) + (r & 3);
+                if (EDGE && row0 + dr >= a.M) continue;
+                float *p = c + (int64_t)dr * a.ldc;
                 if constexpr (FN == 1) {
                     *p = acc[i][0][r];
                 } else if constexpr (FN == 2) {
@@ -482,6 +571,11 @@ using Dl128x128x32K2 = MfmaDlCore<128, 128, 32, 2, 2, 3, 2>;
 using Dl64x64x64 = MfmaDlCore<64, 64, 64, 2, 2, 3, 1, 2>;
 using Dl128x256x16 = MfmaDlCore<128, 256, 16, 2, 2, 3>;
 using Dl256x128x16 = MfmaDlCore<256, 128, 16, 2, 2, 3>;
+// Edge-masking variants of the configurations the automatic choice uses.
+using Dl64x64x32E = MfmaDlCore<64, 64, 32, 2, 2, 4, 1, 2, true>;
+using Dl64x64x64E = MfmaDlCore<64, 64, 64, 2, 2, 3, 1, 2, true>;
+using Dl128x128x32K2E = MfmaDlCore<128, 128, 32, 2, 2, 3, 2, 1, true>;
+using Dl256x256x16E = MfmaDlCore<256, 256, 16, 4, 2, 3, 1, 1, true>;
 
 template <class Core>
 static hipError_t launch(const KernelArgs &a, hipStream_t s) {
@@ -509,7 +603,22 @@ static hipError_t occ(int *n) {
     X(SGEMM_CFG_DL_128x256x16, Dl128x256x16)        \
     X(SGEMM_CFG_DL_256x128x16, Dl256x128x16)
 
+#define SGEMM_DL_EDGE_CONFIGS(X)                    \
+    X(SGEMM_CFG_DL_64x64x32, Dl64x64x32E)           \
+    X(SGEMM_CFG_DL_64x64x64, Dl64x64x64E)           \
+    X(SGEMM_CFG_DL_128x128x32_K2, Dl128x128x32K2E)  \
+    X(SGEMM_CFG_DL_256x256x16, Dl256x256x16E)
+
 hipError_t launch_mfma_dl(int cfg, const KernelArgs &a, hipStream_t s) {
+    if (a.edge) {
+        switch (cfg) {
+#define X(id, core) \
+    case id: return launch<core>(a, s);
+            SGEMM_DL_EDGE_CONFIGS(X)
+#undef X
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (cfg) {
 #define X(id, core) \
     case id: return launch<core>(a, s);

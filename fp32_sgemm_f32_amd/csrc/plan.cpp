@@ -15,28 +15,29 @@
 namespace sgemm {
 
 const CfgInfo kCfgs[] = {
-    {SGEMM_CFG_AUTO, 0, 0, 0, 0, kKindValu, 0, "auto"},
-    {SGEMM_CFG_MFMA_256x256x16, 256, 256, 16, 512, kKindMfma, 1, "mfma_256x256x16"},
-    {SGEMM_CFG_MFMA_128x128x32, 128, 128, 32, 256, kKindMfma, 2, "mfma_128x128x32"},
-    {SGEMM_CFG_MFMA_256x256x32, 256, 256, 32, 256, kKindMfma, 1, "mfma_256x256x32"},
-    {SGEMM_CFG_MFMA_256x128x32, 256, 128, 32, 256, kKindMfma, 1, "mfma_256x128x32"},
-    {SGEMM_CFG_VALU_128x128x8, 128, 128, 8, 256, kKindValu, 2, "valu_128x128x8"},
-    {SGEMM_CFG_MFMA_256x256x32_W8, 256, 256, 32, 512, kKindMfma, 1, "mfma_256x256x32_w8"},
-    {SGEMM_CFG_MFMA_128x128x32_W8, 128, 128, 32, 512, kKindMfma, 2, "mfma_128x128x32_w8"},
-    {SGEMM_CFG_MFMA_64x64x32, 64, 64, 32, 256, kKindMfma, 4, "mfma_64x64x32"},
-    {SGEMM_CFG_MFMA_128x64x32, 128, 64, 32, 256, kKindMfma, 2, "mfma_128x64x32"},
-    {SGEMM_CFG_MFMA_64x64x64, 64, 64, 64, 256, kKindMfma, 2, "mfma_64x64x64"},
-    {SGEMM_CFG_MFMA_128x128x64, 128, 128, 64, 256, kKindMfma, 1, "mfma_128x128x64"},
-    {SGEMM_CFG_MFMA_64x64x128, 64, 64, 128, 256, kKindMfma, 1, "mfma_64x64x128"},
-    {SGEMM_CFG_DL_64x64x32, 64, 64, 32, 256, kKindMfmaDl, 2, "dl_64x64x32"},
-    {SGEMM_CFG_DL_64x64x64_K2, 64, 64, 64, 512, kKindMfmaDl, 1, "dl_64x64x64_k2"},
-    {SGEMM_CFG_DL_128x128x32, 128, 128, 32, 256, kKindMfmaDl, 1, "dl_128x128x32"},
-    {SGEMM_CFG_DL_256x256x16, 256, 256, 16, 512, kKindMfmaDl, 1, "dl_256x256x16"},
-    {SGEMM_CFG_DL_64x64x32_K2, 64, 64, 32, 512, kKindMfmaDl, 2, "dl_64x64x32_k2"},
-    {SGEMM_CFG_DL_128x128x32_K2, 128, 128, 32, 512, kKindMfmaDl, 1, "dl_128x128x32_k2"},
-    {SGEMM_CFG_DL_64x64x64, 64, 64, 64, 256, kKindMfmaDl, 1, "dl_64x64x64"},
-    {SGEMM_CFG_DL_128x256x16, 128, 256, 16, 256, kKindMfmaDl, 2, "dl_128x256x16"},
-    {SGEMM_CFG_DL_256x128x16, 256, 128, 16, 256, kKindMfmaDl, 2, "dl_256x128x16"},
+    {SGEMM_CFG_AUTO, 0, 0, 0, 0, kKindValu, 0, false, "auto"},
+    {SGEMM_CFG_MFMA_256x256x16, 256, 256, 16, 512, kKindMfma, 1, false, "mfma_256x256x16"},
+    {SGEMM_CFG_MFMA_128x128x32, 128, 128, 32, 256, kKindMfma, 2, false, "mfma_128x128x32"},
+    {SGEMM_CFG_MFMA_256x256x32, 256, 256, 32, 256, kKindMfma, 1, false, "mfma_256x256x32"},
+    {SGEMM_CFG_MFMA_256x128x32, 256, 128, 32, 256, kKindMfma, 1, false, "mfma_256x128x32"},
+    {SGEMM_CFG_VALU_128x128x8, 128, 128, 8, 256, kKindValu, 2, false, "valu_128x128x8"},
+    {SGEMM_CFG_MFMA_256x256x32_W8, 256, 256, 32, 512, kKindMfma, 1, false, "mfma_256x256x32_w8"},
+    {SGEMM_CFG_MFMA_128x128x32_W8, 128, 128, 32, 512, kKindMfma, 2, false, "mfma_128x128x32_w8"},
+    {SGEMM_CFG_MFMA_64x64x32, 64, 64, 32, 256, kKindMfma, 4, false, "mfma_64x64x32"},
+    {SGEMM_CFG_MFMA_128x64x32, 128, 64, 32, 256, kKindMfma, 2, false, "mfma_128x64x32"},
+    {SGEMM_CFG_MFMA_64x64x64, 64, 64, 64, 256, kKindMfma, 2, false, "mfma_64x64x64"},
+    {SGEMM_CFG_MFMA_128x128x64, 128, 128, 64, 256, kKindMfma, 1, false, "mfma_128x128x64"},
+    {SGEMM_CFG_MFMA_64x64x128, 64, 64, 128, 256, kKindMfma, 1, false, "mfma_64x64x128"},
+    {SGEMM_CFG_DL_64x64x32, 64, 64, 32, 256, kKindMfmaDl, 2, true, "dl_64x64x32"},
+    {SGEMM_CFG_DL_64x64x64_K2, 64, 64, 64, 512, kKindMfmaDl, 1, false, "dl_64x64x64_k2"},
+    {SGEMM_CFG_DL_128x128x32, 128, 128, 32, 256, kKindMfmaDl, 1, false, "dl_128x128x32"},
+    {SGEMM_CFG_DL_256x256x16, 256, 256, 16, 512, kKindMfmaDl, 1, true, "dl_256x256x16"},
+    {SGEMM_CFG_DL_64x64x32_K2, 64, 64, 32, 512, kKindMfmaDl, 2, false, "dl_64x64x32_k2"},
+    {SGEMM_CFG_DL_128x128x32_K2, 128, 128, 32, 512, kKindMfmaDl, 1, true, "dl_128x128x32_k2"},
+    {SGEMM_CFG_DL_64x64x64, 64, 64, 64, 256, kKindMfmaDl, 1, true, "dl_64x64x64"},
+    {SGEMM_CFG_DL_128x256x16, 128, 256, 16, 256, kKindMfmaDl, 2, false, "dl_128x256x16"},
+    {SGEMM_CFG_DL_256x128x16, 256, 128, 16, 256, kKindMfmaDl, 2, false, "dl_256x128x16"},
+    {SGEMM_CFG_GENERIC_64x64x16, 64, 64, 16, 256, kKindGeneric, 2, true, "generic_64x64x16"},
 };
 const int kNumCfgs = SGEMM_NUM_CFGS;
 
@@ -48,8 +49,17 @@ int64_t workspace_bytes(int grid, int sk_tiles, int bm, int bn) {
     return counters + (int64_t)grid * 2 * bm * bn * 4;
 }
 
-static bool fits(const CfgInfo &c, int M, int N, int K) {
+static bool divides(const CfgInfo &c, int M, int N, int K) {
     return M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0;
+}
+
+// Whether configuration c can run the shape: the generic kernel runs
+// anything; the others need the aligned fast-path layout, and a tile that
+// divides the shape unless they mask ragged edges.
+static bool fits(const CfgInfo &c, int M, int N, int K, bool aligned) {
+    if (c.kind == kKindGeneric) return true;
+    if (!aligned) return false;
+    return c.edge || divides(c, M, N, K);
 }
 
 static int occ_of(const PlanRequest &r, int cfg) {
@@ -71,7 +81,8 @@ static int pick_group_m(int tiles_m, int run) {
 }
 
 static int64_t tiles_of(int cfg, int M, int N) {
-    return (int64_t)(M / kCfgs[cfg].bm) * (N / kCfgs[cfg].bn);
+    const int bm = kCfgs[cfg].bm, bn = kCfgs[cfg].bn;
+    return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
 // Automatic choice, from timings of the configurations on MI355X (256 CUs):
@@ -81,12 +92,13 @@ static int64_t tiles_of(int cfg, int M, int N) {
 //     when every CU gets one (138 at 2048^3);
 //   * else 64x64 tiles loaded straight into LDS (142 at 1024x1024x16384,
 //     99 at 1024^3), with a 64-deep K chunk where K allows.
-static int auto_config(int M, int N, int K, int cus) {
-    const int big = SGEMM_CFG_MFMA_256x256x16, mid = SGEMM_CFG_DL_128x128x32_K2,
-              small = SGEMM_CFG_DL_64x64x64, small32 = SGEMM_CFG_DL_64x64x32;
-    if (fits(kCfgs[big], M, N, K) && tiles_of(big, M, N) >= cus) return big;
-    if (fits(kCfgs[mid], M, N, K) && tiles_of(mid, M, N) >= cus) return mid;
-    if (fits(kCfgs[small], M, N, K)) return small;
+static int auto_config(int M, int N, int K, int cus, bool aligned) {
+    if (!aligned) return SGEMM_CFG_GENERIC_64x64x16;
+    const int big = SGEMM_CFG_MFMA_256x256x16, big_edge = SGEMM_CFG_DL_256x256x16,
+              mid = SGEMM_CFG_DL_128x128x32_K2, small = SGEMM_CFG_DL_64x64x64, small32 = SGEMM_CFG_DL_64x64x32;
+    if (tiles_of(big, M, N) >= cus) return divides(kCfgs[big], M, N, K) ? big : big_edge;
+    if (tiles_of(mid, M, N) >= cus) return mid;
+    if (K % 64 == 0 || K % 32 != 0) return small;
     return small32;
 }
 
@@ -103,31 +115,32 @@ int staged_equivalent(int cfg) {
     }
 }
 
-bool dl_offsets_fit(int cfg, int64_t lda, int64_t ldb) {
+bool dl_offsets_fit(int cfg, bool edge, int64_t lda, int64_t ldb) {
     if (kCfgs[cfg].kind != kKindMfmaDl) return true;
-    const int64_t lim = (int64_t)1 << 32;
+    const int64_t lim = (int64_t)1 << (edge ? 31 : 32);
     return (int64_t)kCfgs[cfg].bm * lda * 4 < lim && (int64_t)kCfgs[cfg].bk * ldb * 4 < lim;
 }
 
 int make_plan(const PlanRequest &req, Plan *out) {
     const int M = req.M, N = req.N, K = req.K;
     if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SHAPE;
-    if (M % kGranM || N % kGranN || K % kGranK) return SGEMM_ERR_SHAPE;
     if (req.config < 0 || req.config >= kNumCfgs) return SGEMM_ERR_CONFIG;
     if (req.sched < SGEMM_SCHED_AUTO || req.sched > SGEMM_SCHED_STREAMK) return SGEMM_ERR_CONFIG;
     const int cus = req.num_cus > 0 ? req.num_cus : 1;
 
     int cfg = req.config;
-    if (cfg == SGEMM_CFG_AUTO) cfg = auto_config(M, N, K, cus);
+    const bool aligned = req.aligned != 0;
+    if (cfg == SGEMM_CFG_AUTO) cfg = auto_config(M, N, K, cus, aligned);
     const CfgInfo &c = kCfgs[cfg];
-    if (!fits(c, M, N, K)) return SGEMM_ERR_CONFIG;
+    if (!fits(c, M, N, K, aligned)) return SGEMM_ERR_CONFIG;
 
     Plan p{};
     p.config = cfg;
     p.bm = c.bm; p.bn = c.bn; p.bk = c.bk; p.threads = c.threads;
-    p.tiles_m = M / c.bm;
-    p.tiles_n = N / c.bn;
-    p.ipt = K / c.bk;
+    p.tiles_m = (M + c.bm - 1) / c.bm;
+    p.tiles_n = (N + c.bn - 1) / c.bn;
+    p.ipt = (K + c.bk - 1) / c.bk;
+    p.edge = (c.kind == kKindGeneric || !divides(c, M, N, K)) ? 1 : 0;
     const int tiles = p.tiles_m * p.tiles_n;
     const int occ = occ_of(req, cfg);
     // Split workgroups per CU: one by default (measured faster than filling

@@ -12,6 +12,7 @@ enum CfgKind {
     kKindValu = 0,      // scalar VALU FMAs
     kKindMfma = 1,      // matrix cores, tiles staged through registers
     kKindMfmaDl = 2,    // matrix cores, tiles loaded straight into LDS
+    kKindGeneric = 3,   // matrix cores, element-wise bounds-checked loads (any shape/alignment)
 };
 
 struct CfgInfo {
@@ -20,6 +21,7 @@ struct CfgInfo {
     int threads;        // threads per workgroup
     int kind;           // CfgKind: which kernel family runs it
     int default_occ;    // workgroups per CU expected from its LDS/VGPR use
+    bool edge;          // runs shapes that are not multiples of its tile
     const char *name;
 };
 
@@ -27,10 +29,9 @@ struct CfgInfo {
 extern const CfgInfo kCfgs[];
 extern const int kNumCfgs;
 
-// Shape granule accepted by the library: every configuration's tile divides
-// multiples of 256 in M and N; the planner only picks configurations whose
-// tile divides the actual shape.
-constexpr int kGranM = 128, kGranN = 128, kGranK = 32;
+// Shape granule accepted by the library: every M, N, K >= 0 (ragged edges are
+// masked; see make_plan).
+constexpr int kGranM = 1, kGranN = 1, kGranK = 1;
 
 // Smallest number of K chunks a Stream-K workgroup should own.
 constexpr int kMinSkIters = 8;
@@ -42,6 +43,7 @@ struct PlanRequest {
     int num_cus;
     const int *occupancy;  // [kNumCfgs] or nullptr
     int sk_wg_per_cu;    // Stream-K grid = num_cus * this (0: occupancy)
+    int aligned;         // 16-byte aligned A, B, C; lda, ldb, ldc, N and K multiples of 4
 };
 
 struct Plan {
@@ -50,6 +52,7 @@ struct Plan {
     int tiles_m, tiles_n, ipt;
     int dp_tiles, sk_tiles, grid, sk_grid;
     int xcd_remap, group_m;
+    int edge;            // the shape is not a multiple of the tile: masked loads and stores
     int64_t sk_iters;
     int64_t workspace_bytes;
     int64_t counters_offset, partials_offset;   // within the workspace
@@ -60,8 +63,10 @@ int make_plan(const PlanRequest &req, Plan *out);
 
 // The configurations that load tiles straight into LDS address a lane's
 // source as a 32-bit byte offset from the tile's first row (A) or the
-// chunk's first row (B): they need BM * lda and BK * ldb under 2^30 floats.
-bool dl_offsets_fit(int cfg, int64_t lda, int64_t ldb);
+// chunk's first row (B): they need BM * lda and BK * ldb under 2^30 floats
+// (2^29 for the edge-masking variants, whose offsets mark a masked lane
+// with the top bit).
+bool dl_offsets_fit(int cfg, bool edge, int64_t lda, int64_t ldb);
 
 // The register-staged configuration with the same tile as `cfg` (itself
 // for those).

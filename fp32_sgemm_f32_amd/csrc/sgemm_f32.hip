@@ -47,6 +47,7 @@ hipError_t launch_cfg(int cfg, const KernelArgs &a, hipStream_t s) {
     switch (kCfgs[cfg].kind) {
     case kKindMfma: return launch_mfma(cfg, a, s);
     case kKindMfmaDl: return launch_mfma_dl(cfg, a, s);
+    case kKindGeneric: return launch_generic(cfg, a, s);
     default: return launch_valu(cfg, a, s);
     }
 }
@@ -55,6 +56,7 @@ hipError_t occupancy_of(int cfg, int *n) {
     switch (kCfgs[cfg].kind) {
     case kKindMfma: return occupancy_mfma(cfg, n);
     case kKindMfmaDl: return occupancy_mfma_dl(cfg, n);
+    case kKindGeneric: return occupancy_generic(cfg, n);
     default: return occupancy_valu(cfg, n);
     }
 }
@@ -126,19 +128,23 @@ bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
 int check_args(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
                const float *C, int ldc) {
     if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SHAPE;
-    if (M % kGranM || N % kGranN || K % kGranK) return SGEMM_ERR_SHAPE;
     if (M == 0 || N == 0) return SGEMM_OK;
     // A and B (and their leading dimensions) are not read when K == 0.
     if (ldc < N || (K > 0 && (lda < K || ldb < N))) return SGEMM_ERR_LD;
     if (!C || (K > 0 && (!A || !B))) return SGEMM_ERR_NULL;
-    if ((ldc & 3) || (K > 0 && ((lda & 3) || (ldb & 3)))) return SGEMM_ERR_ALIGN;
-    if (((uintptr_t)C & 15) || (K > 0 && (((uintptr_t)A & 15) || ((uintptr_t)B & 15))))
-        return SGEMM_ERR_ALIGN;
+    if (((uintptr_t)C & 3) || (K > 0 && (((uintptr_t)A & 3) || ((uintptr_t)B & 3)))) return SGEMM_ERR_ALIGN;
     const int64_t nc = extent_bytes(M, N, ldc);
     if (K > 0 && (overlap(C, nc, A, extent_bytes(M, K, lda)) ||
                   overlap(C, nc, B, extent_bytes(K, N, ldb))))
         return SGEMM_ERR_ALIAS;
     return SGEMM_OK;
+}
+
+// The layout the vector (16-byte) kernels need; anything else runs on the
+// general kernel.
+bool vector_layout(int N, int K, const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
+    return (N & 3) == 0 && (K & 3) == 0 && (lda & 3) == 0 && (ldb & 3) == 0 && (ldc & 3) == 0 &&
+           ((uintptr_t)A & 15) == 0 && ((uintptr_t)B & 15) == 0 && ((uintptr_t)C & 15) == 0;
 }
 
 // Stream-K workspace of (dev, stream), grown to hold `plan`.  Counters are
@@ -193,15 +199,17 @@ int run(int M, int N, int K, const float *A, int lda, const float *B, int ldb, f
     DeviceInfo info;
     if ((st = device_info(dev, &info)) != SGEMM_OK) return st;
     PlanRequest req{M, N, K, config, sched, info.num_cus, info.occupancy,
-                    env_int("SGEMM_F32_SK_WG_PER_CU", 0)};
+                    env_int("SGEMM_F32_SK_WG_PER_CU", 0),
+                    vector_layout(N, K, A, lda, B, ldb, C, ldc) ? 1 : 0};
     Plan p;
     if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
-    if (K > 0 && !dl_offsets_fit(p.config, lda, ldb)) {
+    if (K > 0 && !dl_offsets_fit(p.config, p.edge != 0, lda, ldb)) {
         // Leading dimensions too large for the 32-bit source offsets of the
         // direct-to-LDS kernels: an automatic choice falls back to the
-        // register-staged kernel of the same tile; a forced one is refused.
+        // register-staged kernel of the same tile (the general one when the
+        // tile does not divide the shape); a forced one is refused.
         if (config != SGEMM_CFG_AUTO) return SGEMM_ERR_CONFIG;
-        req.config = staged_equivalent(p.config);
+        req.config = p.edge ? SGEMM_CFG_GENERIC_64x64x16 : staged_equivalent(p.config);
         if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
     }
 
@@ -213,6 +221,8 @@ int run(int M, int N, int K, const float *A, int lda, const float *B, int ldb, f
     KernelArgs a{};
     a.A = A; a.B = B; a.C = C;
     a.lda = lda; a.ldb = ldb; a.ldc = ldc;
+    a.M = M; a.N = N; a.K = K;
+    a.edge = p.edge;
     a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n; a.ipt = p.ipt;
     a.dp_tiles = p.dp_tiles; a.sk_tiles = p.sk_tiles;
     a.grid = p.grid; a.sk_grid = p.sk_grid;
@@ -260,7 +270,7 @@ SGEMM_API const char *sgemm_f32_status_string(int status) {
     case SGEMM_OK: return "ok";
     case SGEMM_ERR_SHAPE: return "shape: negative or not a multiple of the granule";
     case SGEMM_ERR_LD: return "leading dimension smaller than the row length";
-    case SGEMM_ERR_ALIGN: return "pointer not 16-byte aligned or leading dimension not a multiple of 4";
+    case SGEMM_ERR_ALIGN: return "pointer not aligned to a float (4 bytes)";
     case SGEMM_ERR_NULL: return "null pointer";
     case SGEMM_ERR_ALIAS: return "C overlaps A or B";
     case SGEMM_ERR_HIP: return "HIP runtime error";
@@ -275,7 +285,9 @@ SGEMM_API int sgemm_f32_last_hip_error(void) { return sgemm::g_last_hip_error; }
 SGEMM_API int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,
                              const int *occupancy, int sk_wg_per_cu, sgemm_f32_plan_t *out) {
     if (!out) return SGEMM_ERR_NULL;
-    sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu};
+    // Planned for dense operands (lda = K, ldb = ldc = N) on 16-byte boundaries.
+    sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu,
+                           (N % 4 == 0 && K % 4 == 0) ? 1 : 0};
     sgemm::Plan p;
     int st = sgemm::make_plan(req, &p);
     if (st != SGEMM_OK) return st;

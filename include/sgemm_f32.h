@@ -8,8 +8,18 @@
  *     C[m][n] = sum over k of A[m][k] * B[k][n]        (AB only: no alpha/beta)
  *
  * with FP32 inputs and FP32 arithmetic throughout (fused multiply-adds, one
- * rounding each; no reduced-precision input rounding of any kind).  Shapes
- * are restricted to multiples of the tile granule, as on that page.
+ * rounding each; no reduced-precision input rounding of any kind).  Any
+ * shape is accepted: that page restricts itself to multiples of the tile;
+ * ragged edges are handled as the pages "Vectorized Memory Access: Pushing
+ * CUDA SGEMM to 29 TFLOPS on H100" and "2D Block Tiling: Scaling Matrix
+ * Multiplication on NVIDIA H100" describe in their sections 5: values
+ * beyond the matrix read as zero, results beyond it are not written.
+ *
+ * Fast and general layouts
+ *   When N and K are multiples of 4, lda, ldb and ldc are multiples of 4
+ *   and A, B, C are 16-byte aligned, the 16-byte vector kernels run (tile
+ *   edges masked where the shape is not a multiple of the tile).  Any other
+ *   layout runs on a general kernel with element-wise bounds checks.
  *
  * Memory and ownership
  *   A, B, C are device pointers, caller-owned, allocated on the HIP device
@@ -48,16 +58,16 @@ extern "C" {
 
 /* Status codes. */
 #define SGEMM_OK            0  /* success (also for M == 0 or N == 0: nothing to do) */
-#define SGEMM_ERR_SHAPE     1  /* M, N or K negative or not a multiple of the granule */
+#define SGEMM_ERR_SHAPE     1  /* M, N or K negative */
 #define SGEMM_ERR_LD        2  /* lda < K, ldb < N or ldc < N */
-#define SGEMM_ERR_ALIGN     3  /* a pointer not 16-byte aligned, or an ld not a multiple of 4 */
+#define SGEMM_ERR_ALIGN     3  /* a pointer not aligned to a float (4 bytes) */
 #define SGEMM_ERR_NULL      4  /* a required pointer is NULL */
 #define SGEMM_ERR_ALIAS     5  /* the C region overlaps the A or B region */
 #define SGEMM_ERR_HIP       6  /* a HIP runtime call failed: see sgemm_f32_last_hip_error() */
 #define SGEMM_ERR_POINTER   7  /* a pointer is not device memory of the current device, or
                                   the matrix extent runs past the end of its allocation */
-#define SGEMM_ERR_CONFIG    8  /* unknown kernel configuration/schedule, or one whose tile
-                                  does not divide this shape */
+#define SGEMM_ERR_CONFIG    8  /* unknown kernel configuration/schedule, or a forced one that
+                                  cannot run this shape or layout */
 
 /* Kernel configurations (sgemm_f32_ex / sgemm_f32_plan).  "MFMA" configs
  * run the product on the FP32 matrix cores (v_mfma_f32_32x32x2_f32: full
@@ -88,7 +98,14 @@ extern "C" {
 #define SGEMM_CFG_DL_64x64x64       19 /* 256 threads, 4 waves of 32x32, 3 stages */
 #define SGEMM_CFG_DL_128x256x16     20 /* 256 threads, 4 waves of 64x128, 3 stages */
 #define SGEMM_CFG_DL_256x128x16     21 /* 256 threads, 4 waves of 128x64, 3 stages */
-#define SGEMM_NUM_CFGS              22 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
+/* Element-wise bounds-checked loads: any shape, leading dimension and
+ * (4-byte) alignment. */
+#define SGEMM_CFG_GENERIC_64x64x16  22 /* 256 threads, 4 waves of 32x32 */
+#define SGEMM_NUM_CFGS              23 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
+/* Configurations that run shapes which are not multiples of their tile
+ * (vector layout): DL_64x64x32, DL_64x64x64, DL_128x128x32_K2,
+ * DL_256x256x16, and GENERIC_64x64x16 (any layout).  The others need the
+ * vector layout and a shape their tile divides. */
 
 /* Schedules. */
 #define SGEMM_SCHED_AUTO     0  /* whole tiles in full waves, Stream-K for the rest */
@@ -96,11 +113,10 @@ extern "C" {
 #define SGEMM_SCHED_STREAMK  2  /* every tile's K range split evenly over a resident grid */
 
 /*
- * C = A * B.  Requirements: M, N multiples of gm, K a multiple of gk, where
- * sgemm_f32_granule() gives (gm, gn, gk); lda >= K, ldb >= N, ldc >= N, all
- * multiples of 4; A, B, C 16-byte aligned device pointers.  K == 0 writes
- * zeros to C (the empty sum); A, B, lda and ldb are then not used or checked.
- * Returns an SGEMM_* status code.
+ * C = A * B.  Requirements: M, N, K >= 0; lda >= K, ldb >= N, ldc >= N;
+ * A, B, C device pointers aligned to a float.  K == 0 writes zeros to C (the
+ * empty sum); A, B, lda and ldb are then not used or checked.  Returns an
+ * SGEMM_* status code.
  */
 int sgemm_f32(int M, int N, int K,
               const float *A, int lda,
@@ -120,7 +136,8 @@ int sgemm_f32_ex(int M, int N, int K,
                  float *C, int ldc,
                  hipStream_t stream, int config, int sched);
 
-/* Shape multiples accepted by sgemm_f32 (any pointer may be NULL). */
+/* Shape multiples accepted by sgemm_f32: 1, 1, 1 (any shape; any pointer
+ * may be NULL). */
 void sgemm_f32_granule(int *gm, int *gn, int *gk);
 
 /* Human-readable text for a status code (static storage, never NULL). */
@@ -136,8 +153,9 @@ int sgemm_f32_last_hip_error(void);
  * compute-unit count; occupancy[c] is the number of workgroups of
  * configuration c that fit on one compute unit (NULL: the library's
  * built-in figures); sk_wg_per_cu is the number of split workgroups per CU
- * (0: the library's default, one), capped by the occupancy.  Returns an
- * SGEMM_* status code; *out is filled on success.
+ * (0: the library's default, one), capped by the occupancy.  The plan
+ * assumes dense operands (lda = K, ldb = ldc = N) on 16-byte boundaries.
+ * Returns an SGEMM_* status code; *out is filled on success.
  */
 typedef struct sgemm_f32_plan_t {
     int config;          /* SGEMM_CFG_* chosen */
@@ -145,7 +163,7 @@ typedef struct sgemm_f32_plan_t {
     int tile_m, tile_n, tile_k;
     int threads;         /* threads per workgroup */
     int tiles_m, tiles_n;
-    int iters_per_tile;  /* K / tile_k */
+    int iters_per_tile;  /* K chunks per tile: ceil(K / tile_k) */
     int dp_tiles;        /* tiles computed whole, first in tile order */
     int sk_tiles;        /* remaining tiles, K-split over the grid */
     int grid;            /* workgroups launched */

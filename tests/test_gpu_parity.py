@@ -44,11 +44,23 @@ def gpu_matmul(A, B, dev, config=sg.CFG_AUTO, sched=sg.SCHED_AUTO):
     return C.cpu().numpy()
 
 
-def fits(config, M, N, K):
-    if config == sg.CFG_AUTO:
+# Configurations that run shapes their tile does not divide (the vector ones
+# when N and K are multiples of 4; the general one always).
+EDGE_CFGS = [sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_DL_256x256x16,
+             sg.CFG_GENERIC_64x64x16]
+
+
+def fits(config, M, N, K, vector=None):
+    """Whether a forced configuration runs this shape (dense operands: the
+    vector layout holds when N and K are multiples of 4)."""
+    if config in (sg.CFG_AUTO, sg.CFG_GENERIC_64x64x16):
         return True
+    if vector is None:
+        vector = N % 4 == 0 and K % 4 == 0
+    if not vector:
+        return False
     bm, bn, bk = sg.CFG_TILES[config]
-    return M % bm == 0 and N % bn == 0 and K % bk == 0
+    return config in EDGE_CFGS or (M % bm == 0 and N % bn == 0 and K % bk == 0)
 
 
 def check(C, C_ref, S, label):
@@ -134,6 +146,78 @@ def test_empty_m_is_a_no_op(dev):
     C = sg.matmul(A, B)
     torch.cuda.synchronize()
     assert C.shape == (0, 128)
+
+
+# ---------------------------------------------------------------------------
+# Arbitrary shapes: ragged edges in M, N and K (the edge-masking vector
+# kernels when N and K are multiples of 4, else the general kernel), odd
+# leading dimensions and pointers that are only float-aligned.
+# ---------------------------------------------------------------------------
+
+RAGGED = [(1, 1, 1), (7, 13, 5), (33, 68, 20), (100, 196, 36), (129, 260, 100), (300, 68, 1004),
+          (517, 384, 772), (257, 511, 129), (1000, 1000, 1000)]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("sched", SCHEDS, ids=lambda s: sg.SCHED_NAMES[s])
+@pytest.mark.parametrize("config", [sg.CFG_AUTO] + EDGE_CFGS, ids=lambda c: sg.CFG_NAMES[c])
+def test_parity_ragged(dev, config, sched, shape):
+    M, N, K = shape
+    log(f"case ragged config={sg.CFG_NAMES[config]} sched={sg.SCHED_NAMES[sched]} shape={shape}")
+    A, B = workloads.generate(M, N, K, "normal", 2000 + M + 3 * N + 7 * K)
+    if not fits(config, M, N, K):
+        import torch
+        with pytest.raises(sg.SgemmError) as e:
+            sg.matmul(to_dev(A, dev), to_dev(B, dev), config=config, sched=sched)
+        torch.cuda.synchronize()
+        assert e.value.status == sg.ERR_CONFIG
+        return
+    C = gpu_matmul(A, B, dev, config, sched)
+    C_ref, S = oracle.gemm(A, B)
+    check(C, C_ref, S, f"{sg.CFG_NAMES[config]}/{sg.SCHED_NAMES[sched]}")
+
+
+@pytest.mark.parametrize("config", [sg.CFG_AUTO] + EDGE_CFGS, ids=lambda c: sg.CFG_NAMES[c])
+def test_ragged_integer_inputs_bit_exact(dev, config):
+    M, N, K = 517, 772, 1004
+    log(f"case ragged int4 config={sg.CFG_NAMES[config]}")
+    A, B = workloads.generate(M, N, K, "int4", 78)
+    for sched in (sg.SCHED_DP, sg.SCHED_STREAMK):
+        C = gpu_matmul(A, B, dev, config, sched)
+        C_ref, _ = oracle.gemm(A, B)
+        assert np.array_equal(C.astype(np.float64), C_ref)
+
+
+@pytest.mark.parametrize("case", ["a_offset", "b_offset", "c_offset", "odd_ld"])
+def test_float_aligned_layouts_run_on_the_general_kernel(dev, case):
+    """Operands that start 4 bytes past a 16-byte boundary, and leading
+    dimensions that are not multiples of 4: correct results (the general
+    kernel), C's padding untouched; a forced vector kernel is refused."""
+    import torch
+    M, N, K = 130, 196, 72
+    log(f"case layout {case}")
+    A, B = workloads.generate(M, N, K, "normal", 13)
+    extra = {"a_offset": (1, 0, 0), "b_offset": (0, 1, 0), "c_offset": (0, 0, 1)}.get(case, (0, 0, 0))
+    pad = 3 if case == "odd_ld" else 0
+    Abuf = torch.full((M * (K + pad) + 4,), float("nan"), device=dev)
+    Bbuf = torch.full((K * (N + pad) + 4,), float("nan"), device=dev)
+    Cbuf = torch.full((M * (N + pad) + 4,), float("nan"), device=dev)
+    Av = Abuf[extra[0]:extra[0] + M * (K + pad)].view(M, K + pad)[:, :K]
+    Bv = Bbuf[extra[1]:extra[1] + K * (N + pad)].view(K, N + pad)[:, :N]
+    Cv = Cbuf[extra[2]:extra[2] + M * (N + pad)].view(M, N + pad)[:, :N]
+    Av.copy_(to_dev(A, dev))
+    Bv.copy_(to_dev(B, dev))
+    with pytest.raises(sg.SgemmError) as e:
+        sg.matmul(Av, Bv, out=Cv, config=sg.CFG_DL_64x64x32)
+    assert e.value.status == sg.ERR_CONFIG
+    for sched in (sg.SCHED_DP, sg.SCHED_STREAMK):
+        sg.matmul(Av, Bv, out=Cv, sched=sched)
+        torch.cuda.synchronize()
+        C_ref, S = oracle.gemm(A, B)
+        check(Cv.cpu().numpy(), C_ref, S, f"{case}/{sg.SCHED_NAMES[sched]}")
+    if pad:
+        full = Cbuf[:M * (N + pad)].view(M, N + pad).cpu().numpy()
+        assert np.all(np.isnan(full[:, N:])), "ldc padding was written"
 
 
 @pytest.mark.parametrize("config", [sg.CFG_AUTO, sg.CFG_MFMA_128x128x32, sg.CFG_VALU_128x128x8],

@@ -13,7 +13,9 @@ import pytest
 
 import fp32_sgemm_f32_amd as sg
 
-OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1, 2, 1, 1, 1, 2, 1, 1, 2, 2]
+OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1, 2, 1, 1, 1, 2, 1, 1, 2, 2, 2]
+EDGE_CFGS = {sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_DL_256x256x16,
+             sg.CFG_GENERIC_64x64x16}
 
 
 def logical_ids(p):
@@ -71,9 +73,13 @@ def walk(p):
             s += k1 - k0
 
 
+def ceil_div(a, b):
+    return -(-a // b)
+
+
 def check_plan(p, M, N, K):
-    assert p["tiles_m"] * p["tile_m"] == M and p["tiles_n"] * p["tile_n"] == N
-    assert p["iters_per_tile"] * p["tile_k"] == K
+    assert p["tiles_m"] == ceil_div(M, p["tile_m"]) and p["tiles_n"] == ceil_div(N, p["tile_n"])
+    assert p["iters_per_tile"] == ceil_div(K, p["tile_k"])
     assert sorted(logical_ids(p)) == list(range(p["grid"]))        # remap is a bijection
     assert p["sk_grid"] <= p["grid"]
     if p["sk_tiles"]:
@@ -102,7 +108,8 @@ def check_plan(p, M, N, K):
 
 
 SHAPES = [(128, 128, 32), (256, 256, 256), (512, 384, 96), (1024, 1024, 1024), (1024, 1024, 16384),
-          (2048, 2048, 2048), (4096, 4096, 4096), (1280, 768, 640), (3072, 2048, 352)]
+          (2048, 2048, 2048), (4096, 4096, 4096), (1280, 768, 640), (3072, 2048, 352),
+          (1, 1, 1), (7, 13, 5), (100, 196, 36), (1000, 1000, 1000), (4095, 4096, 4092), (300, 17, 9000)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -114,8 +121,15 @@ def test_every_step_covered_once(shape, config, sched, cus):
     try:
         p = sg.plan(M, N, K, config, sched, num_cus=cus, occupancy=OCC)
     except sg.SgemmError as e:
-        # Only a forced tile that does not divide the shape may be refused.
+        # Only a forced configuration that cannot run the shape may be
+        # refused: a tile that does not divide it on a kernel without edge
+        # masking, or the vector kernels when N or K is not a multiple of 4.
         assert e.status == sg.ERR_CONFIG and config != sg.CFG_AUTO
+        bm, bn, bk = sg.CFG_TILES[config]
+        divides = M % bm == 0 and N % bn == 0 and K % bk == 0
+        vector = N % 4 == 0 and K % 4 == 0
+        assert config != sg.CFG_GENERIC_64x64x16
+        assert not vector or (not divides and config not in EDGE_CFGS)
         return
     check_plan(p, M, N, K)
     if sched == sg.SCHED_DP:
@@ -179,6 +193,18 @@ def test_auto_choices_on_256_cus():
     assert p["config"] == sg.CFG_DL_64x64x32
     p = sg.plan(256, 256, 256, num_cus=256, occupancy=occ)
     assert p["config"] == sg.CFG_DL_64x64x64
+    # Ragged shapes: the edge-masking kernels of the same regimes, or the
+    # general kernel when N or K is not a multiple of 4.
+    p = sg.plan(4000, 4000, 4000, num_cus=256, occupancy=occ)
+    assert (p["config"], p["tiles_m"], p["iters_per_tile"]) == (sg.CFG_DL_256x256x16, 16, 250)
+    p = sg.plan(2000, 2000, 2000, num_cus=256, occupancy=occ)
+    assert p["config"] == sg.CFG_DL_128x128x32_K2
+    p = sg.plan(1000, 1000, 1000, num_cus=256, occupancy=occ)
+    assert p["config"] == sg.CFG_DL_64x64x64
+    p = sg.plan(1000, 1001, 1000, num_cus=256, occupancy=occ)
+    assert p["config"] == sg.CFG_GENERIC_64x64x16
+    p = sg.plan(7, 13, 5, num_cus=256, occupancy=occ)
+    assert p["config"] == sg.CFG_GENERIC_64x64x16
 
 
 def test_xcd_grouping_for_the_headline_shape():
@@ -195,10 +221,13 @@ def test_xcd_grouping_for_the_headline_shape():
 
 def test_plan_errors():
     with pytest.raises(sg.SgemmError) as e:
-        sg.plan(100, 128, 32)
+        sg.plan(-1, 128, 32)
     assert e.value.status == sg.ERR_SHAPE
     with pytest.raises(sg.SgemmError) as e:
         sg.plan(128, 128, 32, config=sg.CFG_MFMA_256x256x16)
+    assert e.value.status == sg.ERR_CONFIG
+    with pytest.raises(sg.SgemmError) as e:      # vector kernel, N not a multiple of 4
+        sg.plan(128, 130, 32, config=sg.CFG_DL_64x64x32)
     assert e.value.status == sg.ERR_CONFIG
     with pytest.raises(sg.SgemmError) as e:
         sg.plan(128, 128, 32, config=42)
