@@ -130,6 +130,11 @@ def library():
     lib.sgemm_f32.argtypes = [i, i, i, p, i, p, i, p, i, vp]
     lib.sgemm_f32_ex.restype = i
     lib.sgemm_f32_ex.argtypes = [i, i, i, p, i, p, i, p, i, vp, i, i]
+    f = ctypes.c_float
+    lib.sgemm_f32_gemm.restype = i
+    lib.sgemm_f32_gemm.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, vp]
+    lib.sgemm_f32_gemm_ex.restype = i
+    lib.sgemm_f32_gemm_ex.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, vp, i, i]
     lib.sgemm_f32_granule.restype = None
     lib.sgemm_f32_granule.argtypes = [ctypes.POINTER(i)] * 3
     lib.sgemm_f32_status_string.restype = ctypes.c_char_p
@@ -145,7 +150,7 @@ def library():
 
 
 def granule():
-    """(gm, gn, gk): M, N, K must be multiples of these."""
+    """(gm, gn, gk): M, N, K must be multiples of these (1, 1, 1: any shape)."""
     g = [ctypes.c_int() for _ in range(3)]
     library().sgemm_f32_granule(*[ctypes.byref(x) for x in g])
     return tuple(x.value for x in g)
@@ -187,6 +192,52 @@ def sgemm_raw(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream=0,
     if config == CFG_AUTO and sched == SCHED_AUTO:
         return lib.sgemm_f32(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream)
     return lib.sgemm_f32_ex(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream, config, sched)
+
+
+def gemm_raw(trans_a, trans_b, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc, stream=0,
+             config=CFG_AUTO, sched=SCHED_AUTO) -> int:
+    """C = alpha op(A) op(B) + beta C with integer device addresses; returns the status."""
+    lib = library()
+    if config == CFG_AUTO and sched == SCHED_AUTO:
+        return lib.sgemm_f32_gemm(trans_a, trans_b, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc,
+                                  stream)
+    return lib.sgemm_f32_gemm_ex(trans_a, trans_b, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc,
+                                 stream, config, sched)
+
+
+def gemm(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False, config=CFG_AUTO,
+         sched=SCHED_AUTO, stream=None):
+    """C = alpha * op(A) @ op(B) + beta * C for float32 HIP tensors.
+
+    A is the stored matrix: (M, K), or (K, M) with trans_a (op(A) = A^T);
+    B: (K, N), or (N, K) with trans_b.  All row-major (unit column stride;
+    padded rows allowed).  C (M, N) is allocated if None (then beta must be
+    0).  Returns C.
+    """
+    import torch
+
+    for t, n in ((A, "A"), (B, "B")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda:
+            raise TypeError(f"{n} must be a float32 tensor on a HIP device")
+    M, K = (A.shape[1], A.shape[0]) if trans_a else tuple(A.shape)
+    K2, N = (B.shape[1], B.shape[0]) if trans_b else tuple(B.shape)
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif C.dtype != torch.float32 or tuple(C.shape) != (M, N) or C.device != A.device:
+        raise ValueError("C must be float32 (M, N) on A's device")
+    lda, ldb, ldc = _row_major_ld(A, "A"), _row_major_ld(B, "B"), _row_major_ld(C, "C")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device)
+    with torch.cuda.device(A.device):
+        st = gemm_raw(int(bool(trans_a)), int(bool(trans_b)), M, N, K, float(alpha), A.data_ptr(), lda,
+                      B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc, stream.cuda_stream, config, sched)
+    if st != OK:
+        raise SgemmError(st, "sgemm_f32_gemm")
+    return C
 
 
 def _row_major_ld(t, name):

@@ -26,6 +26,10 @@ struct KernelArgs {
     int64_t lda, ldb, ldc;
     int M, N, K;      // the shape (the edge-masking kernels need it)
     int edge;         // the shape is not a multiple of the tile
+    int trans_a;      // A stored K x M (op(A) = A^T); else M x K
+    int trans_b;      // B stored N x K (op(B) = B^T); else K x N
+    int scaled;       // C = alpha * product + beta * C; else C = product
+    float alpha, beta;
     int tiles_m, tiles_n;
     int ipt;          // K chunks per tile
     int dp_tiles;     // tiles [0, dp_tiles) are computed whole
@@ -38,6 +42,17 @@ struct KernelArgs {
     int *counters;    // [sk_tiles] arrival counters, zero between calls
     float *partials;  // [sk_grid][2][tile floats] partial tiles
 };
+
+// Value stored to C at p for a product value v: v itself for the plain
+// product, else alpha * v + beta * C (C read only when beta != 0, so that C
+// need not hold numbers then, as in BLAS).
+template <class V>
+__device__ __forceinline__ V epilogue(const KernelArgs &a, V v, const float *p) {
+    if (!a.scaled) return v;
+    V r = a.alpha * v;
+    if (a.beta != 0.0f) r += a.beta * *(const V *)p;
+    return r;
+}
 
 // Workgroups are handed to the 8 XCDs round-robin by blockIdx.  With the
 // remap, XCD x runs logical ids [x*grid/8, (x+1)*grid/8): neighbouring tiles

@@ -1,4 +1,5 @@
-// FP32 GEMM for any shape and any (4-byte) alignment: the general path.
+// FP32 GEMM for any shape, any (4-byte) alignment and either storage order
+// of A and B: the general path.
 //
 // The fast kernels load 16-byte vectors and assume rows that start on
 // 16-byte boundaries; this one loads single floats, each checked against the
@@ -37,28 +38,56 @@ struct GenericCore {
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
     }
 
-    // Chunk c of tile (tm, tn): this thread's 4 A values (row t/4, k 4(t%4)
-    // .. +3) and 4 B values (k-row t/16, columns 4(t%16) .. +3).
+    // Chunk c of tile (tm, tn): this thread's 4 A values (k-consecutive, for
+    // one row) and 4 B values (k-consecutive for one column when B is stored
+    // transposed, else column-consecutive for one k), each bounds-checked.
+    // The thread map follows the stored layout so that neighbouring threads
+    // read neighbouring addresses.
     __device__ __forceinline__ static void load(const KernelArgs &a, int tm, int tn, int c, float (&ra)[4],
                                                 float (&rb)[4]) {
         const int t = threadIdx.x;
-        const int row = tm * BM + t / 4, ka = c * BK + 4 * (t % 4);
-        const bool row_ok = row < a.M;
+        if (!a.trans_a) {   // A[m * lda + k]: threads along k
+            const int row = tm * BM + t / 4, ka = c * BK + 4 * (t % 4);
+            const bool row_ok = row < a.M;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            ra[j] = (row_ok && ka + j < a.K) ? a.A[(int64_t)row * a.lda + ka + j] : 0.0f;
-        const int kb = c * BK + t / 16, col = tn * BN + 4 * (t % 16);
-        const bool k_ok = kb < a.K;
+            for (int j = 0; j < 4; ++j)
+                ra[j] = (row_ok && ka + j < a.K) ? a.A[(int64_t)row * a.lda + ka + j] : 0.0f;
+        } else {            // A[k * lda + m]: threads along m
+            const int row = tm * BM + t % 64, ka = c * BK + 4 * (t / 64);
+            const bool row_ok = row < a.M;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            rb[j] = (k_ok && col + j < a.N) ? a.B[(int64_t)kb * a.ldb + col + j] : 0.0f;
+            for (int j = 0; j < 4; ++j)
+                ra[j] = (row_ok && ka + j < a.K) ? a.A[(int64_t)(ka + j) * a.lda + row] : 0.0f;
+        }
+        if (!a.trans_b) {   // B[k * ldb + n]: threads along n
+            const int kb = c * BK + t / 16, col = tn * BN + 4 * (t % 16);
+            const bool k_ok = kb < a.K;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                rb[j] = (k_ok && col + j < a.N) ? a.B[(int64_t)kb * a.ldb + col + j] : 0.0f;
+        } else {            // B[n * ldb + k]: threads along k
+            const int col = tn * BN + t / 4, kb = c * BK + 4 * (t % 4);
+            const bool col_ok = col < a.N;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                rb[j] = (col_ok && kb + j < a.K) ? a.B[(int64_t)col * a.ldb + kb + j] : 0.0f;
+        }
     }
 
-    __device__ __forceinline__ static void store(float *s, const float (&ra)[4], const float (&rb)[4]) {
+    // A[row][k..k+3] of the thread's map to its LDS row; B likewise into
+    // the k-contiguous row of its column (a transposing scatter when B is
+    // stored k-major).
+    __device__ __forceinline__ static void store(const KernelArgs &a, float *s, const float (&ra)[4],
+                                                 const float (&rb)[4]) {
         const int t = threadIdx.x;
-        *(f32x4 *)(s + (t / 4) * LDK + 4 * (t % 4)) = f32x4{ra[0], ra[1], ra[2], ra[3]};
+        const int am = a.trans_a ? t % 64 : t / 4, ak = a.trans_a ? 4 * (t / 64) : 4 * (t % 4);
+        *(f32x4 *)(s + am * LDK + ak) = f32x4{ra[0], ra[1], ra[2], ra[3]};
+        if (a.trans_b) {
+            *(f32x4 *)(s + A_STAGE + (t / 4) * LDK + 4 * (t % 4)) = f32x4{rb[0], rb[1], rb[2], rb[3]};
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s[A_STAGE + (4 * (t % 16) + j) * LDK + t / 16] = rb[j];
+            for (int j = 0; j < 4; ++j) s[A_STAGE + (4 * (t % 16) + j) * LDK + t / 16] = rb[j];
+        }
     }
 
     __device__ __forceinline__ void mainloop(const KernelArgs &a, float *lds, int tm, int tn, int k0, int k1) {
@@ -70,7 +99,7 @@ struct GenericCore {
         load(a, tm, tn, k0, ra, rb);
         for (int c = k0; c < k1; ++c) {
             float *s = lds + ((c - k0) & 1) * STAGE;
-            store(s, ra, rb);
+            store(a, s, ra, rb);
             if (c + 1 < k1) load(a, tm, tn, c + 1, ra, rb);
             __syncthreads();
 #pragma unroll
@@ -93,7 +122,10 @@ struct GenericCore {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = row0 + 8 * (r >> 2) + (r & 3);
-            if (row < a.M) a.C[(int64_t)row * a.ldc + col] = acc[r];
+            if (row < a.M) {
+                float *p = a.C + (int64_t)row * a.ldc + col;
+                *p = epilogue(a, acc[r], p);
+            }
         }
     }
 

@@ -326,8 +326,10 @@ struct MfmaCore {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    c[(int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * a.ldc + j * 32] = acc[i][j][r];
+                for (int r = 0; r < 16; ++r) {
+                    float *p = c + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * a.ldc + j * 32;
+                    *p = epilogue(a, acc[i][j][r], p);
+                }
     }
 
     // Thread-private layout: value v of this thread at p[v * NT + tid].

@@ -517,11 +517,11 @@ struct MfmaDlCore {
                 if (EDGE && row0 + dr >= a.M) continue;
                 float *p = c + (int64_t)dr * a.ldc;
                 if constexpr (FN == 1) {
-                    *p = acc[i][0][r];
+                    *p = epilogue(a, acc[i][0][r], p);
                 } else if constexpr (FN == 2) {
-                    *(f32x2 *)p = f32x2{acc[i][0][r], acc[i][1][r]};
+                    *(f32x2 *)p = epilogue(a, f32x2{acc[i][0][r], acc[i][1][r]}, p);
                 } else {
-                    *(f32x4 *)p = f32x4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
+                    *(f32x4 *)p = epilogue(a, f32x4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]}, p);
                 }
             }
     }

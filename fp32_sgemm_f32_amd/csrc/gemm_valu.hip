@@ -111,8 +111,8 @@ struct Valu128x128x8 {
         for (int i = 0; i < 8; ++i) {
             const int row = tm * BM + (i < 4 ? ty * 4 + i : 64 + ty * 4 + (i - 4));
             float *c = a.C + (int64_t)row * a.ldc + (int64_t)tn * BN + tx * 4;
-            *(f32x4 *)c = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
-            *(f32x4 *)(c + 64) = f32x4{acc[i][4], acc[i][5], acc[i][6], acc[i][7]};
+            *(f32x4 *)c = epilogue(a, f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]}, c);
+            *(f32x4 *)(c + 64) = epilogue(a, f32x4{acc[i][4], acc[i][5], acc[i][6], acc[i][7]}, c + 64);
         }
     }
 
@@ -156,22 +156,25 @@ hipError_t occupancy_valu(int cfg, int *wg_per_cu) {
 }
 
 // C := 0 over the logical M x N region (the empty sum, K == 0).
-__global__ void sgemm_fill_zero_kernel(float *C, int M, int N, int64_t ldc) {
+// C = beta * C over the M x N region (the product is empty, K == 0, or
+// scaled by alpha == 0); beta == 0 writes zeros without reading C.
+__global__ void sgemm_scale_c_kernel(float *C, int M, int N, int64_t ldc, float beta) {
     const int64_t total = (int64_t)M * N;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t r = i / N, c = i - r * N;
-        C[r * ldc + c] = 0.0f;
+        float *p = C + r * ldc + c;
+        *p = beta == 0.0f ? 0.0f : beta * *p;
     }
 }
 
-hipError_t launch_fill_zero(float *C, int M, int N, int64_t ldc, hipStream_t s) {
+hipError_t launch_scale_c(float *C, int M, int N, int64_t ldc, float beta, hipStream_t s) {
     int64_t total = (int64_t)M * N;
     int blocks = (int)((total + 255) / 256);
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) return hipSuccess;
-    void *params[] = {&C, &M, &N, &ldc};
-    return hipLaunchKernel((const void *)sgemm_fill_zero_kernel, dim3(blocks), dim3(256), params, 0, s);
+    void *params[] = {&C, &M, &N, &ldc, &beta};
+    return hipLaunchKernel((const void *)sgemm_scale_c_kernel, dim3(blocks), dim3(256), params, 0, s);
 }
 
 }  // namespace sgemm

@@ -18,6 +18,6 @@ hipError_t launch_generic(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t occupancy_generic(int cfg, int *wg_per_cu);
 hipError_t launch_valu(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t occupancy_valu(int cfg, int *wg_per_cu);
-hipError_t launch_fill_zero(float *C, int M, int N, int64_t ldc, hipStream_t s);
+hipError_t launch_scale_c(float *C, int M, int N, int64_t ldc, float beta, hipStream_t s);
 
 }  // namespace sgemm

@@ -15,29 +15,29 @@
 namespace sgemm {
 
 const CfgInfo kCfgs[] = {
-    {SGEMM_CFG_AUTO, 0, 0, 0, 0, kKindValu, 0, false, "auto"},
-    {SGEMM_CFG_MFMA_256x256x16, 256, 256, 16, 512, kKindMfma, 1, false, "mfma_256x256x16"},
-    {SGEMM_CFG_MFMA_128x128x32, 128, 128, 32, 256, kKindMfma, 2, false, "mfma_128x128x32"},
-    {SGEMM_CFG_MFMA_256x256x32, 256, 256, 32, 256, kKindMfma, 1, false, "mfma_256x256x32"},
-    {SGEMM_CFG_MFMA_256x128x32, 256, 128, 32, 256, kKindMfma, 1, false, "mfma_256x128x32"},
-    {SGEMM_CFG_VALU_128x128x8, 128, 128, 8, 256, kKindValu, 2, false, "valu_128x128x8"},
-    {SGEMM_CFG_MFMA_256x256x32_W8, 256, 256, 32, 512, kKindMfma, 1, false, "mfma_256x256x32_w8"},
-    {SGEMM_CFG_MFMA_128x128x32_W8, 128, 128, 32, 512, kKindMfma, 2, false, "mfma_128x128x32_w8"},
-    {SGEMM_CFG_MFMA_64x64x32, 64, 64, 32, 256, kKindMfma, 4, false, "mfma_64x64x32"},
-    {SGEMM_CFG_MFMA_128x64x32, 128, 64, 32, 256, kKindMfma, 2, false, "mfma_128x64x32"},
-    {SGEMM_CFG_MFMA_64x64x64, 64, 64, 64, 256, kKindMfma, 2, false, "mfma_64x64x64"},
-    {SGEMM_CFG_MFMA_128x128x64, 128, 128, 64, 256, kKindMfma, 1, false, "mfma_128x128x64"},
-    {SGEMM_CFG_MFMA_64x64x128, 64, 64, 128, 256, kKindMfma, 1, false, "mfma_64x64x128"},
-    {SGEMM_CFG_DL_64x64x32, 64, 64, 32, 256, kKindMfmaDl, 2, true, "dl_64x64x32"},
-    {SGEMM_CFG_DL_64x64x64_K2, 64, 64, 64, 512, kKindMfmaDl, 1, false, "dl_64x64x64_k2"},
-    {SGEMM_CFG_DL_128x128x32, 128, 128, 32, 256, kKindMfmaDl, 1, false, "dl_128x128x32"},
-    {SGEMM_CFG_DL_256x256x16, 256, 256, 16, 512, kKindMfmaDl, 1, true, "dl_256x256x16"},
-    {SGEMM_CFG_DL_64x64x32_K2, 64, 64, 32, 512, kKindMfmaDl, 2, false, "dl_64x64x32_k2"},
-    {SGEMM_CFG_DL_128x128x32_K2, 128, 128, 32, 512, kKindMfmaDl, 1, true, "dl_128x128x32_k2"},
-    {SGEMM_CFG_DL_64x64x64, 64, 64, 64, 256, kKindMfmaDl, 1, true, "dl_64x64x64"},
-    {SGEMM_CFG_DL_128x256x16, 128, 256, 16, 256, kKindMfmaDl, 2, false, "dl_128x256x16"},
-    {SGEMM_CFG_DL_256x128x16, 256, 128, 16, 256, kKindMfmaDl, 2, false, "dl_256x128x16"},
-    {SGEMM_CFG_GENERIC_64x64x16, 64, 64, 16, 256, kKindGeneric, 2, true, "generic_64x64x16"},
+    {SGEMM_CFG_AUTO, 0, 0, 0, 0, kKindValu, 0, false, false, "auto"},
+    {SGEMM_CFG_MFMA_256x256x16, 256, 256, 16, 512, kKindMfma, 1, false, false, "mfma_256x256x16"},
+    {SGEMM_CFG_MFMA_128x128x32, 128, 128, 32, 256, kKindMfma, 2, false, false, "mfma_128x128x32"},
+    {SGEMM_CFG_MFMA_256x256x32, 256, 256, 32, 256, kKindMfma, 1, false, false, "mfma_256x256x32"},
+    {SGEMM_CFG_MFMA_256x128x32, 256, 128, 32, 256, kKindMfma, 1, false, false, "mfma_256x128x32"},
+    {SGEMM_CFG_VALU_128x128x8, 128, 128, 8, 256, kKindValu, 2, false, false, "valu_128x128x8"},
+    {SGEMM_CFG_MFMA_256x256x32_W8, 256, 256, 32, 512, kKindMfma, 1, false, false, "mfma_256x256x32_w8"},
+    {SGEMM_CFG_MFMA_128x128x32_W8, 128, 128, 32, 512, kKindMfma, 2, false, false, "mfma_128x128x32_w8"},
+    {SGEMM_CFG_MFMA_64x64x32, 64, 64, 32, 256, kKindMfma, 4, false, false, "mfma_64x64x32"},
+    {SGEMM_CFG_MFMA_128x64x32, 128, 64, 32, 256, kKindMfma, 2, false, false, "mfma_128x64x32"},
+    {SGEMM_CFG_MFMA_64x64x64, 64, 64, 64, 256, kKindMfma, 2, false, false, "mfma_64x64x64"},
+    {SGEMM_CFG_MFMA_128x128x64, 128, 128, 64, 256, kKindMfma, 1, false, false, "mfma_128x128x64"},
+    {SGEMM_CFG_MFMA_64x64x128, 64, 64, 128, 256, kKindMfma, 1, false, false, "mfma_64x64x128"},
+    {SGEMM_CFG_DL_64x64x32, 64, 64, 32, 256, kKindMfmaDl, 2, true, false, "dl_64x64x32"},
+    {SGEMM_CFG_DL_64x64x64_K2, 64, 64, 64, 512, kKindMfmaDl, 1, false, false, "dl_64x64x64_k2"},
+    {SGEMM_CFG_DL_128x128x32, 128, 128, 32, 256, kKindMfmaDl, 1, false, false, "dl_128x128x32"},
+    {SGEMM_CFG_DL_256x256x16, 256, 256, 16, 512, kKindMfmaDl, 1, true, false, "dl_256x256x16"},
+    {SGEMM_CFG_DL_64x64x32_K2, 64, 64, 32, 512, kKindMfmaDl, 2, false, false, "dl_64x64x32_k2"},
+    {SGEMM_CFG_DL_128x128x32_K2, 128, 128, 32, 512, kKindMfmaDl, 1, true, false, "dl_128x128x32_k2"},
+    {SGEMM_CFG_DL_64x64x64, 64, 64, 64, 256, kKindMfmaDl, 1, true, false, "dl_64x64x64"},
+    {SGEMM_CFG_DL_128x256x16, 128, 256, 16, 256, kKindMfmaDl, 2, false, false, "dl_128x256x16"},
+    {SGEMM_CFG_DL_256x128x16, 256, 128, 16, 256, kKindMfmaDl, 2, false, false, "dl_256x128x16"},
+    {SGEMM_CFG_GENERIC_64x64x16, 64, 64, 16, 256, kKindGeneric, 2, true, true, "generic_64x64x16"},
 };
 const int kNumCfgs = SGEMM_NUM_CFGS;
 
@@ -56,9 +56,9 @@ static bool divides(const CfgInfo &c, int M, int N, int K) {
 // Whether configuration c can run the shape: the generic kernel runs
 // anything; the others need the aligned fast-path layout, and a tile that
 // divides the shape unless they mask ragged edges.
-static bool fits(const CfgInfo &c, int M, int N, int K, bool aligned) {
+static bool fits(const CfgInfo &c, int M, int N, int K, bool aligned, bool transposed) {
     if (c.kind == kKindGeneric) return true;
-    if (!aligned) return false;
+    if (!aligned || (transposed && !c.layouts)) return false;
     return c.edge || divides(c, M, N, K);
 }
 
@@ -92,8 +92,8 @@ static int64_t tiles_of(int cfg, int M, int N) {
 //     when every CU gets one (138 at 2048^3);
 //   * else 64x64 tiles loaded straight into LDS (142 at 1024x1024x16384,
 //     99 at 1024^3), with a 64-deep K chunk where K allows.
-static int auto_config(int M, int N, int K, int cus, bool aligned) {
-    if (!aligned) return SGEMM_CFG_GENERIC_64x64x16;
+static int auto_config(int M, int N, int K, int cus, bool aligned, bool transposed) {
+    if (!aligned || transposed) return SGEMM_CFG_GENERIC_64x64x16;
     const int big = SGEMM_CFG_MFMA_256x256x16, big_edge = SGEMM_CFG_DL_256x256x16,
               mid = SGEMM_CFG_DL_128x128x32_K2, small = SGEMM_CFG_DL_64x64x64, small32 = SGEMM_CFG_DL_64x64x32;
     if (tiles_of(big, M, N) >= cus) return divides(kCfgs[big], M, N, K) ? big : big_edge;
@@ -129,10 +129,10 @@ int make_plan(const PlanRequest &req, Plan *out) {
     const int cus = req.num_cus > 0 ? req.num_cus : 1;
 
     int cfg = req.config;
-    const bool aligned = req.aligned != 0;
-    if (cfg == SGEMM_CFG_AUTO) cfg = auto_config(M, N, K, cus, aligned);
+    const bool aligned = req.aligned != 0, transposed = req.trans_a || req.trans_b;
+    if (cfg == SGEMM_CFG_AUTO) cfg = auto_config(M, N, K, cus, aligned, transposed);
     const CfgInfo &c = kCfgs[cfg];
-    if (!fits(c, M, N, K, aligned)) return SGEMM_ERR_CONFIG;
+    if (!fits(c, M, N, K, aligned, transposed)) return SGEMM_ERR_CONFIG;
 
     Plan p{};
     p.config = cfg;
@@ -140,7 +140,8 @@ int make_plan(const PlanRequest &req, Plan *out) {
     p.tiles_m = (M + c.bm - 1) / c.bm;
     p.tiles_n = (N + c.bn - 1) / c.bn;
     p.ipt = (K + c.bk - 1) / c.bk;
-    p.edge = (c.kind == kKindGeneric || !divides(c, M, N, K)) ? 1 : 0;
+    // Transposed operands run on the edge-masking variants as well.
+    p.edge = (c.kind == kKindGeneric || !divides(c, M, N, K) || transposed) ? 1 : 0;
     const int tiles = p.tiles_m * p.tiles_n;
     const int occ = occ_of(req, cfg);
     // Split workgroups per CU: one by default (measured faster than filling

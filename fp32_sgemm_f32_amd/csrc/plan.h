@@ -22,6 +22,7 @@ struct CfgInfo {
     int kind;           // CfgKind: which kernel family runs it
     int default_occ;    // workgroups per CU expected from its LDS/VGPR use
     bool edge;          // runs shapes that are not multiples of its tile
+    bool layouts;       // runs transposed A and/or B (else only A M x K, B K x N)
     const char *name;
 };
 
@@ -43,7 +44,10 @@ struct PlanRequest {
     int num_cus;
     const int *occupancy;  // [kNumCfgs] or nullptr
     int sk_wg_per_cu;    // Stream-K grid = num_cus * this (0: occupancy)
-    int aligned;         // 16-byte aligned A, B, C; lda, ldb, ldc, N and K multiples of 4
+    int aligned;         // 16-byte aligned A, B, C; lda, ldb, ldc and the contiguous
+                         // extents of A, B, C multiples of 4
+    int trans_a = 0;     // A stored K x M
+    int trans_b = 0;     // B stored N x K
 };
 
 struct Plan {

@@ -124,27 +124,51 @@ bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
     return a0 < b0 + (uint64_t)nb && b0 < a0 + (uint64_t)na;
 }
 
+// One call: C = op(A) op(B) (plain), or alpha op(A) op(B) + beta C (scaled).
+struct Call {
+    int M, N, K;
+    int ta, tb;                    // A stored K x M / B stored N x K
+    const float *A, *B;
+    float *C;
+    int lda, ldb, ldc;
+    int scaled;
+    float alpha, beta;
+    hipStream_t stream;
+    int config, sched;
+
+    // Rows and columns of A and B as stored.
+    int a_rows() const { return ta ? K : M; }
+    int a_cols() const { return ta ? M : K; }
+    int b_rows() const { return tb ? N : K; }
+    int b_cols() const { return tb ? K : N; }
+    // A and B are read only when the product contributes.
+    bool reads_ab() const { return K > 0 && !(scaled && alpha == 0.0f); }
+};
+
 // Host-only checks (no HIP call).  Order: shape, ld, null, alignment, alias.
-int check_args(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
-               const float *C, int ldc) {
-    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SHAPE;
-    if (M == 0 || N == 0) return SGEMM_OK;
-    // A and B (and their leading dimensions) are not read when K == 0.
-    if (ldc < N || (K > 0 && (lda < K || ldb < N))) return SGEMM_ERR_LD;
-    if (!C || (K > 0 && (!A || !B))) return SGEMM_ERR_NULL;
-    if (((uintptr_t)C & 3) || (K > 0 && (((uintptr_t)A & 3) || ((uintptr_t)B & 3)))) return SGEMM_ERR_ALIGN;
-    const int64_t nc = extent_bytes(M, N, ldc);
-    if (K > 0 && (overlap(C, nc, A, extent_bytes(M, K, lda)) ||
-                  overlap(C, nc, B, extent_bytes(K, N, ldb))))
+int check_args(const Call &c) {
+    if (c.M < 0 || c.N < 0 || c.K < 0) return SGEMM_ERR_SHAPE;
+    if (c.M == 0 || c.N == 0) return SGEMM_OK;
+    const bool ab = c.reads_ab();
+    // A and B (and their leading dimensions) are not read when the product
+    // does not contribute.
+    if (c.ldc < c.N || (ab && (c.lda < c.a_cols() || c.ldb < c.b_cols()))) return SGEMM_ERR_LD;
+    if (!c.C || (ab && (!c.A || !c.B))) return SGEMM_ERR_NULL;
+    if (((uintptr_t)c.C & 3) || (ab && (((uintptr_t)c.A & 3) || ((uintptr_t)c.B & 3)))) return SGEMM_ERR_ALIGN;
+    const int64_t nc = extent_bytes(c.M, c.N, c.ldc);
+    if (ab && (overlap(c.C, nc, c.A, extent_bytes(c.a_rows(), c.a_cols(), c.lda)) ||
+               overlap(c.C, nc, c.B, extent_bytes(c.b_rows(), c.b_cols(), c.ldb))))
         return SGEMM_ERR_ALIAS;
     return SGEMM_OK;
 }
 
-// The layout the vector (16-byte) kernels need; anything else runs on the
-// general kernel.
-bool vector_layout(int N, int K, const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
-    return (N & 3) == 0 && (K & 3) == 0 && (lda & 3) == 0 && (ldb & 3) == 0 && (ldc & 3) == 0 &&
-           ((uintptr_t)A & 15) == 0 && ((uintptr_t)B & 15) == 0 && ((uintptr_t)C & 15) == 0;
+// The layout the vector (16-byte) kernels need: the contiguous extent and
+// the leading dimension of every operand a multiple of 4, and 16-byte
+// aligned operands; anything else runs on the general kernel.
+bool vector_layout(const Call &c) {
+    return (c.a_cols() & 3) == 0 && (c.b_cols() & 3) == 0 && (c.N & 3) == 0 && (c.lda & 3) == 0 &&
+           (c.ldb & 3) == 0 && (c.ldc & 3) == 0 && ((uintptr_t)c.A & 15) == 0 && ((uintptr_t)c.B & 15) == 0 &&
+           ((uintptr_t)c.C & 15) == 0;
 }
 
 // Stream-K workspace of (dev, stream), grown to hold `plan`.  Counters are
@@ -179,50 +203,52 @@ int workspace_for(int dev, hipStream_t s, const Plan &p, Workspace *out) {
     return SGEMM_OK;
 }
 
-int run(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float *C,
-        int ldc, hipStream_t stream, int config, int sched) {
-    int st = check_args(M, N, K, A, lda, B, ldb, C, ldc);
+int run(const Call &c) {
+    int st = check_args(c);
     if (st != SGEMM_OK) return st;
-    if (config < 0 || config >= SGEMM_NUM_CFGS) return SGEMM_ERR_CONFIG;
-    if (sched < SGEMM_SCHED_AUTO || sched > SGEMM_SCHED_STREAMK) return SGEMM_ERR_CONFIG;
-    if (M == 0 || N == 0) return SGEMM_OK;
+    if (c.config < 0 || c.config >= SGEMM_NUM_CFGS) return SGEMM_ERR_CONFIG;
+    if (c.sched < SGEMM_SCHED_AUTO || c.sched > SGEMM_SCHED_STREAMK) return SGEMM_ERR_CONFIG;
+    if (c.M == 0 || c.N == 0) return SGEMM_OK;
 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e);
-    if ((st = check_device_range(C, extent_bytes(M, N, ldc), dev)) != SGEMM_OK) return st;
-    if (K > 0) {
-        if ((st = check_device_range(A, extent_bytes(M, K, lda), dev)) != SGEMM_OK) return st;
-        if ((st = check_device_range(B, extent_bytes(K, N, ldb), dev)) != SGEMM_OK) return st;
+    if ((st = check_device_range(c.C, extent_bytes(c.M, c.N, c.ldc), dev)) != SGEMM_OK) return st;
+    if (c.reads_ab()) {
+        if ((st = check_device_range(c.A, extent_bytes(c.a_rows(), c.a_cols(), c.lda), dev)) != SGEMM_OK) return st;
+        if ((st = check_device_range(c.B, extent_bytes(c.b_rows(), c.b_cols(), c.ldb), dev)) != SGEMM_OK) return st;
     }
 
     DeviceInfo info;
     if ((st = device_info(dev, &info)) != SGEMM_OK) return st;
-    PlanRequest req{M, N, K, config, sched, info.num_cus, info.occupancy,
-                    env_int("SGEMM_F32_SK_WG_PER_CU", 0),
-                    vector_layout(N, K, A, lda, B, ldb, C, ldc) ? 1 : 0};
+    PlanRequest req{c.M, c.N, c.K, c.config, c.sched, info.num_cus, info.occupancy,
+                    env_int("SGEMM_F32_SK_WG_PER_CU", 0), vector_layout(c) ? 1 : 0, c.ta, c.tb};
     Plan p;
     if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
-    if (K > 0 && !dl_offsets_fit(p.config, p.edge != 0, lda, ldb)) {
+    if (c.K > 0 && !dl_offsets_fit(p.config, p.edge != 0, c.lda, c.ldb)) {
         // Leading dimensions too large for the 32-bit source offsets of the
         // direct-to-LDS kernels: an automatic choice falls back to the
         // register-staged kernel of the same tile (the general one when the
         // tile does not divide the shape); a forced one is refused.
-        if (config != SGEMM_CFG_AUTO) return SGEMM_ERR_CONFIG;
+        if (c.config != SGEMM_CFG_AUTO) return SGEMM_ERR_CONFIG;
         req.config = p.edge ? SGEMM_CFG_GENERIC_64x64x16 : staged_equivalent(p.config);
         if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
     }
 
-    if (K == 0) {
-        e = launch_fill_zero(C, M, N, ldc, stream);
+    if (!c.reads_ab()) {
+        // No product: C = beta * C (zeros for the plain product, K == 0).
+        e = launch_scale_c(c.C, c.M, c.N, c.ldc, c.scaled ? c.beta : 0.0f, c.stream);
         return e == hipSuccess ? SGEMM_OK : hip_fail(e);
     }
 
     KernelArgs a{};
-    a.A = A; a.B = B; a.C = C;
-    a.lda = lda; a.ldb = ldb; a.ldc = ldc;
-    a.M = M; a.N = N; a.K = K;
+    a.A = c.A; a.B = c.B; a.C = c.C;
+    a.lda = c.lda; a.ldb = c.ldb; a.ldc = c.ldc;
+    a.M = c.M; a.N = c.N; a.K = c.K;
     a.edge = p.edge;
+    a.trans_a = c.ta; a.trans_b = c.tb;
+    a.scaled = c.scaled && !(c.alpha == 1.0f && c.beta == 0.0f);
+    a.alpha = c.alpha; a.beta = c.beta;
     a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n; a.ipt = p.ipt;
     a.dp_tiles = p.dp_tiles; a.sk_tiles = p.sk_tiles;
     a.grid = p.grid; a.sk_grid = p.sk_grid;
@@ -236,14 +262,24 @@ int run(int M, int N, int K, const float *A, int lda, const float *B, int ldb, f
         // between the two.
         std::lock_guard<std::mutex> lock(g_mu);
         Workspace w;
-        if ((st = workspace_for(dev, stream, p, &w)) != SGEMM_OK) return st;
+        if ((st = workspace_for(dev, c.stream, p, &w)) != SGEMM_OK) return st;
         a.counters = w.counters;
         a.partials = w.partials;
-        e = launch_cfg(p.config, a, stream);
+        e = launch_cfg(p.config, a, c.stream);
     } else {
-        e = launch_cfg(p.config, a, stream);
+        e = launch_cfg(p.config, a, c.stream);
     }
     return e == hipSuccess ? SGEMM_OK : hip_fail(e);
+}
+
+Call plain(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float *C, int ldc,
+           hipStream_t stream, int config, int sched) {
+    return Call{M, N, K, 0, 0, A, B, C, lda, ldb, ldc, 0, 1.0f, 0.0f, stream, config, sched};
+}
+
+Call blas(int ta, int tb, int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+          float beta, float *C, int ldc, hipStream_t stream, int config, int sched) {
+    return Call{M, N, K, ta != 0, tb != 0, A, B, C, lda, ldb, ldc, 1, alpha, beta, stream, config, sched};
 }
 
 }  // namespace
@@ -251,12 +287,28 @@ int run(int M, int N, int K, const float *A, int lda, const float *B, int ldb, f
 
 SGEMM_API int sgemm_f32(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
                         float *C, int ldc, hipStream_t stream) {
-    return sgemm::run(M, N, K, A, lda, B, ldb, C, ldc, stream, SGEMM_CFG_AUTO, SGEMM_SCHED_AUTO);
+    return sgemm::run(sgemm::plain(M, N, K, A, lda, B, ldb, C, ldc, stream, SGEMM_CFG_AUTO, SGEMM_SCHED_AUTO));
 }
 
 SGEMM_API int sgemm_f32_ex(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
                            float *C, int ldc, hipStream_t stream, int config, int sched) {
-    return sgemm::run(M, N, K, A, lda, B, ldb, C, ldc, stream, config, sched);
+    return sgemm::run(sgemm::plain(M, N, K, A, lda, B, ldb, C, ldc, stream, config, sched));
+}
+
+SGEMM_API int sgemm_f32_gemm(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+                             int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                             hipStream_t stream) {
+    if (trans_a < 0 || trans_a > 1 || trans_b < 0 || trans_b > 1) return SGEMM_ERR_CONFIG;
+    return sgemm::run(sgemm::blas(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                                  SGEMM_CFG_AUTO, SGEMM_SCHED_AUTO));
+}
+
+SGEMM_API int sgemm_f32_gemm_ex(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+                                int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                                hipStream_t stream, int config, int sched) {
+    if (trans_a < 0 || trans_a > 1 || trans_b < 0 || trans_b > 1) return SGEMM_ERR_CONFIG;
+    return sgemm::run(sgemm::blas(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                                  config, sched));
 }
 
 SGEMM_API void sgemm_f32_granule(int *gm, int *gn, int *gk) {
@@ -287,7 +339,7 @@ SGEMM_API int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num
     if (!out) return SGEMM_ERR_NULL;
     // Planned for dense operands (lda = K, ldb = ldc = N) on 16-byte boundaries.
     sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu,
-                           (N % 4 == 0 && K % 4 == 0) ? 1 : 0};
+                           (N % 4 == 0 && K % 4 == 0) ? 1 : 0, 0, 0};
     sgemm::Plan p;
     int st = sgemm::make_plan(req, &p);
     if (st != SGEMM_OK) return st;

@@ -105,7 +105,8 @@ extern "C" {
 /* Configurations that run shapes which are not multiples of their tile
  * (vector layout): DL_64x64x32, DL_64x64x64, DL_128x128x32_K2,
  * DL_256x256x16, and GENERIC_64x64x16 (any layout).  The others need the
- * vector layout and a shape their tile divides. */
+ * vector layout and a shape their tile divides.  Transposed operands
+ * (sgemm_f32_gemm): GENERIC_64x64x16. */
 
 /* Schedules. */
 #define SGEMM_SCHED_AUTO     0  /* whole tiles in full waves, Stream-K for the rest */
@@ -135,6 +136,44 @@ int sgemm_f32_ex(int M, int N, int K,
                  const float *B, int ldb,
                  float *C, int ldc,
                  hipStream_t stream, int config, int sched);
+
+/*
+ * General matrix multiply in the BLAS form, row-major:
+ *
+ *     C = alpha * op(A) * op(B) + beta * C
+ *
+ * op(A) is M x K: A stored M x K (A[m * lda + k], lda >= K) when trans_a
+ * is 0, or stored K x M (A[k * lda + m], lda >= M) when trans_a is 1, so
+ * that op(A) = A^T; likewise op(B) is K x N: B stored K x N (ldb >= N) or,
+ * with trans_b = 1, N x K (B[n * ldb + k], ldb >= K).  C is M x N, ldc >= N.
+ * The kernels of "Vectorized Memory Access: Pushing CUDA SGEMM to 29 TFLOPS
+ * on H100" and "2D Block Tiling: Scaling Matrix Multiplication on NVIDIA
+ * H100" take the same alpha and beta (their sections 5 show the scaled
+ * store); sgemm_f32 is the alpha = 1, beta = 0, untransposed case.
+ *
+ * Conventions (as in BLAS): beta == 0 means C is not read (it may hold
+ * anything); alpha == 0 or K == 0 means A and B are not read (they and
+ * their leading dimensions are then not checked) and C = beta * C.  The
+ * sum is computed once and scaled once per element; with Stream-K the
+ * partial sums are combined first.  Accepts every shape and layout; the
+ * 16-byte vector kernels need the contiguous extent (K or M of A, N or K
+ * of B, N of C) and every leading dimension to be multiples of 4 and the
+ * operands 16-byte aligned, else the general kernel runs.  trans_a or
+ * trans_b outside {0, 1}: SGEMM_ERR_CONFIG.  Other errors as sgemm_f32.
+ */
+int sgemm_f32_gemm(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                   const float *A, int lda,
+                   const float *B, int ldb, float beta,
+                   float *C, int ldc,
+                   hipStream_t stream);
+
+/* sgemm_f32_gemm with the configuration and schedule forced (tests and
+ * benchmarks), as sgemm_f32_ex. */
+int sgemm_f32_gemm_ex(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                      const float *A, int lda,
+                      const float *B, int ldb, float beta,
+                      float *C, int ldc,
+                      hipStream_t stream, int config, int sched);
 
 /* Shape multiples accepted by sgemm_f32: 1, 1, 1 (any shape; any pointer
  * may be NULL). */

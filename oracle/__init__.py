@@ -14,6 +14,12 @@ C[m, n] = sum_k A[m, k] * B[k, n], computed for AB only.
 Each call also returns S[m, n] = sum_k |A[m, k] * B[k, n]|, the scale of the
 per-element error bound |C_gpu - C_ref| <= 1e-5 * S.
 
+gemm_blas is the BLAS form the pages' kernels carry (alpha and beta in the
+scaled stores of "Vectorized Memory Access: Pushing CUDA SGEMM to 29 TFLOPS
+on H100" and "2D Block Tiling: Scaling Matrix Multiplication on NVIDIA
+H100", sections 5), with either storage order of A and B:
+C = alpha * op(A) op(B) + beta * C0, the product from the same triple loop.
+
 Parity pins: see tests/test_oracle_pins.py (identity, all-ones, integer
 exactness, rank-1 closed form, transpose invariance, exact rational brute
 force, planted-mistake detection).
@@ -87,6 +93,31 @@ def gemm(A, B, threads=None):
         C.ctypes.data, N, S.ctypes.data, N, int(threads or default_threads()))
     if rc != 0:
         raise RuntimeError("oracle_gemm_f64 failed")
+    return C, S
+
+
+def gemm_blas(A, B, C0=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False, threads=None):
+    """Return (C_ref, S) for C = alpha * op(A) op(B) + beta * C0, in FP64.
+
+    op(A) = A^T when trans_a (A stored K x M), else A; likewise B.  C0 is
+    read only when beta != 0 (BLAS convention).  S = |alpha| * sum_k
+    |op(A)[m,k] op(B)[k,n]| + |beta| * |C0[m,n]| scales the error bound.
+    alpha and beta are taken as the float32 values a GPU call receives."""
+    A = _as_f32_2d(A, "A")
+    B = _as_f32_2d(B, "B")
+    opA = np.ascontiguousarray(A.T) if trans_a else A
+    opB = np.ascontiguousarray(B.T) if trans_b else B
+    P, S = gemm(opA, opB, threads)
+    a = float(np.float32(alpha))
+    b = float(np.float32(beta))
+    C = a * P
+    S = abs(a) * S
+    if b != 0.0:
+        C0 = np.asarray(C0, dtype=np.float64)
+        if C0.shape != C.shape:
+            raise ValueError("C0 shape")
+        C = C + b * C0
+        S = S + abs(b) * np.abs(C0)
     return C, S
 
 

@@ -220,6 +220,97 @@ def test_float_aligned_layouts_run_on_the_general_kernel(dev, case):
         assert np.all(np.isnan(full[:, N:])), "ldc padding was written"
 
 
+# ---------------------------------------------------------------------------
+# The BLAS form: C = alpha op(A) op(B) + beta C, either storage order of A
+# and B (sgemm_f32_gemm).
+# ---------------------------------------------------------------------------
+
+LAYOUTS = [(0, 0), (0, 1), (1, 0), (1, 1)]
+SCALINGS = [(1.0, 0.0), (2.5, 0.0), (1.5, -0.75), (0.0, 2.0), (-1.0, 1.0)]
+
+
+def stored(X, trans):
+    return np.ascontiguousarray(X.T) if trans else X
+
+
+def c0_of(M, N, seed):
+    return workloads.generate(M, 1, N, "normal", seed)[0]      # M x N
+
+
+@pytest.mark.parametrize("shape", [(200, 136, 100), (517, 384, 772), (256, 256, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("scaling", SCALINGS, ids=lambda ab: f"a{ab[0]}_b{ab[1]}")
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: f"ta{l[0]}tb{l[1]}")
+def test_blas_form(dev, layout, scaling, shape):
+    import torch
+    (ta, tb), (alpha, beta), (M, N, K) = layout, scaling, shape
+    log(f"case blas ta={ta} tb={tb} alpha={alpha} beta={beta} shape={shape}")
+    A, B = workloads.generate(M, N, K, "normal", 3000 + M + N + K)
+    As, Bs = stored(A, ta), stored(B, tb)
+    C0 = c0_of(M, N, 3100 + M)
+    C_ref, S = oracle.gemm_blas(As, Bs, C0, alpha, beta, ta, tb)
+    for sched in (sg.SCHED_DP, sg.SCHED_STREAMK):
+        C = to_dev(C0, dev).clone()
+        sg.gemm(to_dev(As, dev), to_dev(Bs, dev), C, alpha, beta, ta, tb, sched=sched)
+        torch.cuda.synchronize()
+        check(C.cpu().numpy(), C_ref, S, f"blas/{sg.SCHED_NAMES[sched]}")
+
+
+@pytest.mark.parametrize("config", [sg.CFG_MFMA_256x256x16, sg.CFG_MFMA_128x128x32, sg.CFG_VALU_128x128x8,
+                                    sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_GENERIC_64x64x16],
+                         ids=lambda c: sg.CFG_NAMES[c])
+def test_blas_scaling_on_every_kernel_family(dev, config):
+    """alpha / beta in the epilogue of each kernel family, whole tiles and
+    Stream-K (the scaling is applied once, after the partial sums)."""
+    import torch
+    M, N, K = 512, 512, 768
+    log(f"case blas scaling config={sg.CFG_NAMES[config]}")
+    A, B = workloads.generate(M, N, K, "int4", 61)
+    C0 = workloads.generate(M, 1, N, "int4", 62)[0]
+    C_ref, _ = oracle.gemm_blas(A, B, C0, 2.0, -3.0)
+    for sched in (sg.SCHED_DP, sg.SCHED_STREAMK):
+        C = to_dev(C0, dev).clone()
+        sg.gemm(to_dev(A, dev), to_dev(B, dev), C, 2.0, -3.0, config=config, sched=sched)
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref)   # integers: exact
+
+
+def test_blas_beta_zero_does_not_read_c(dev):
+    import torch
+    M, N, K = 300, 260, 200
+    log("case blas beta=0 with NaN C")
+    A, B = workloads.generate(M, N, K, "normal", 63)
+    C = torch.full((M, N), float("nan"), device=dev)
+    sg.gemm(to_dev(A, dev), to_dev(B, dev), C, 1.25, 0.0)
+    torch.cuda.synchronize()
+    C_ref, S = oracle.gemm_blas(A, B, None, 1.25, 0.0)
+    check(C.cpu().numpy(), C_ref, S, "beta=0")
+
+
+def test_blas_alpha_zero_and_empty_k_scale_c(dev):
+    """alpha = 0 or K = 0: C = beta C, and A, B are not read (null here)."""
+    import torch
+    M, N = 130, 70
+    log("case blas alpha=0 / K=0")
+    C0 = c0_of(M, N, 64)
+    for K, alpha in ((50, 0.0), (0, 3.0)):
+        C = to_dev(C0, dev).clone()
+        st = sg.gemm_raw(0, 0, M, N, K, alpha, 0, max(K, 1), 0, N, -0.5, C.data_ptr(), N,
+                         torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert st == sg.OK
+        assert np.array_equal(C.cpu().numpy(), (np.float32(-0.5) * C0).astype(np.float32))
+    C = to_dev(C0, dev).clone()
+    st = sg.gemm_raw(0, 0, M, N, 0, 1.0, 0, 1, 0, N, 0.0, C.data_ptr(), N,
+                     torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == sg.OK and torch.count_nonzero(C).item() == 0
+
+
+def test_blas_rejects_bad_transpose_flag(dev):
+    assert sg.gemm_raw(2, 0, 64, 64, 64, 1.0, 0, 64, 0, 64, 0.0, 0, 64) == sg.ERR_CONFIG
+
+
 @pytest.mark.parametrize("config", [sg.CFG_AUTO, sg.CFG_MFMA_128x128x32, sg.CFG_VALU_128x128x8],
                          ids=lambda c: sg.CFG_NAMES[c])
 def test_padded_leading_dimensions_and_untouched_gap(dev, config):

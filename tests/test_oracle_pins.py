@@ -250,3 +250,109 @@ def test_planted_mistake_is_caught(mistake):
     fn = lambda A, B: _loop_oracle(A, B, mistake)  # noqa: E731
     failed = [p.__name__ for p in PINS if not p(fn)]
     assert failed, f"planted mistake {mistake!r} passed every pin"
+
+
+# ----------------------------------------------------------------------------
+# The BLAS form, C = alpha op(A) op(B) + beta C0 (oracle.gemm_blas).  Pins
+# take blas_fn(A, B, C0, alpha, beta, trans_a, trans_b) -> (C, S).
+# ----------------------------------------------------------------------------
+
+def _stored(X, trans):
+    """The array to pass for op(...) = X: X itself, or X^T stored."""
+    return np.ascontiguousarray(X.T) if trans else X
+
+
+def pin_blas_integer_exact(blas_fn):
+    """Integer entries, alpha = 3, beta = -2, integer C0, every storage order:
+    C = 3 (A @ B) - 2 C0 exactly (numpy int64), S = 3 |A| @ |B| + 2 |C0|."""
+    A, B = workloads.generate(9, 11, 45, "int4", 51)
+    C0 = workloads.generate(9, 11, 1, "int4", 52)[0][:, :1] * np.ones((1, 11), np.float32)
+    Ai, Bi, C0i = A.astype(np.int64), B.astype(np.int64), C0.astype(np.int64)
+    ref = 3 * (Ai @ Bi) - 2 * C0i
+    sref = 3 * (np.abs(Ai) @ np.abs(Bi)) + 2 * np.abs(C0i)
+    ok = True
+    for ta in (False, True):
+        for tb in (False, True):
+            C, S = blas_fn(_stored(A, ta), _stored(B, tb), C0, 3.0, -2.0, ta, tb)
+            ok &= np.array_equal(C, ref.astype(np.float64)) and np.array_equal(S, sref.astype(np.float64))
+    return bool(ok)
+
+
+def pin_blas_beta_zero_leaves_c0_unread(blas_fn):
+    """beta = 0: C0 is not read, so NaNs in it do not reach C = alpha A B."""
+    A, B = workloads.generate(6, 5, 13, "int4", 53)
+    C0 = np.full((6, 5), np.nan, np.float32)
+    C, _ = blas_fn(A, B, C0, 2.0, 0.0, False, False)
+    return np.array_equal(C, 2.0 * (A.astype(np.int64) @ B.astype(np.int64)).astype(np.float64))
+
+
+def pin_blas_alpha_zero(blas_fn):
+    """alpha = 0: C = beta C0 exactly (here beta = 0.5, exact in binary)."""
+    A, B = workloads.generate(4, 7, 9, "normal", 54)
+    C0 = workloads.generate(4, 7, 1, "normal", 55)[0][:, :1] * np.ones((1, 7), np.float32)
+    C, _ = blas_fn(A, B, C0, 0.0, 0.5, False, False)
+    return np.array_equal(C, 0.5 * C0.astype(np.float64))
+
+
+def pin_blas_rank1_transposed(blas_fn):
+    """op(A)[m, k] = u[m] stored as A^T (K x M), op(B)[k, n] = v[n] stored as
+    B^T (N x K): C = alpha K u[m] v[n] (closed form)."""
+    M, N, K = 4, 3, 21
+    u = np.array([1, -3, 2, 5], dtype=np.float32)
+    v = np.array([-2, 1, 3], dtype=np.float32)
+    A_stored = np.repeat(u[None, :], K, axis=0)     # K x M: row k holds u
+    B_stored = np.repeat(v[:, None], K, axis=1)     # N x K: row n holds v[n]
+    C, _ = blas_fn(A_stored, B_stored, None, 2.0, 0.0, True, True)
+    return np.array_equal(C, 2.0 * K * np.outer(u.astype(np.float64), v.astype(np.float64)))
+
+
+BLAS_PINS = [pin_blas_integer_exact, pin_blas_beta_zero_leaves_c0_unread, pin_blas_alpha_zero,
+             pin_blas_rank1_transposed]
+
+
+def _blas_oracle(A, B, C0, alpha, beta, ta, tb):
+    return oracle.gemm_blas(A, B, C0, alpha, beta, ta, tb)
+
+
+@pytest.mark.parametrize("pin", BLAS_PINS, ids=[p.__name__ for p in BLAS_PINS])
+def test_oracle_blas_form_satisfies_pin(pin):
+    assert pin(_blas_oracle)
+
+
+def _blas_with_mistake(mistake):
+    """oracle.gemm_blas with one plausible bookkeeping error planted."""
+    def fn(A, B, C0, alpha, beta, ta, tb):
+        if mistake == "ignore_trans_a":
+            ta = False
+            A = np.ascontiguousarray(A.T) if A.shape[1] != B.shape[0] and not tb else A
+        if mistake == "ignore_trans_b":
+            tb = False
+        if mistake == "swap_alpha_beta":
+            alpha, beta = beta, alpha
+        if mistake == "read_c0_always":
+            C, S = oracle.gemm_blas(A, B, None, alpha, 0.0, ta, tb)
+            return C + float(np.float32(beta)) * np.asarray(C0, np.float64), S
+        if mistake == "beta_unscaled" and beta != 0.0:
+            C, S = oracle.gemm_blas(A, B, C0, alpha, beta, ta, tb)
+            return C - float(np.float32(beta)) * np.asarray(C0, np.float64) + np.asarray(C0, np.float64), S
+        try:
+            return oracle.gemm_blas(A, B, C0, alpha, beta, ta, tb)
+        except ValueError:
+            return np.full((1, 1), np.nan), np.full((1, 1), np.nan)
+    return fn
+
+
+BLAS_MISTAKES = ["ignore_trans_a", "ignore_trans_b", "swap_alpha_beta", "read_c0_always", "beta_unscaled"]
+
+
+@pytest.mark.parametrize("mistake", BLAS_MISTAKES)
+def test_planted_blas_mistake_is_caught(mistake):
+    fn = _blas_with_mistake(mistake)
+    failed = []
+    for p in BLAS_PINS:
+        try:
+            if not p(fn):
+                failed.append(p.__name__)
+        except (ValueError, TypeError):
+            failed.append(p.__name__)
+    assert failed, f"planted mistake {mistake!r} passed every BLAS pin"
