@@ -143,6 +143,8 @@ def library():
     lib.sgemm_f32_last_hip_error.argtypes = []
     lib.sgemm_f32_plan.restype = i
     lib.sgemm_f32_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), i, ctypes.POINTER(_Plan)]
+    lib.sgemm_f32_gemm_plan.restype = i
+    lib.sgemm_f32_gemm_plan.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i), i, ctypes.POINTER(_Plan)]
     lib.sgemm_f32_release.restype = i
     lib.sgemm_f32_release.argtypes = []
     _lib = lib
@@ -171,17 +173,19 @@ def release() -> None:
 
 
 def plan(M, N, K, config=CFG_AUTO, sched=SCHED_AUTO, num_cus=256, occupancy=None,
-         sk_wg_per_cu=0) -> dict:
-    """The launch plan for a shape (host computation only, no GPU needed)."""
+         sk_wg_per_cu=0, trans_a=0, trans_b=0) -> dict:
+    """The launch plan for a shape (host computation only, no GPU needed);
+    trans_a / trans_b: the storage orders of the BLAS form (gemm)."""
     occ = None
     if occupancy is not None:
         if len(occupancy) != NUM_CFGS:
             raise ValueError(f"occupancy needs {NUM_CFGS} entries")
         occ = (ctypes.c_int * NUM_CFGS)(*occupancy)
     out = _Plan()
-    st = library().sgemm_f32_plan(M, N, K, config, sched, num_cus, occ, sk_wg_per_cu, ctypes.byref(out))
+    st = library().sgemm_f32_gemm_plan(trans_a, trans_b, M, N, K, config, sched, num_cus, occ, sk_wg_per_cu,
+                                       ctypes.byref(out))
     if st != OK:
-        raise SgemmError(st, "sgemm_f32_plan")
+        raise SgemmError(st, "sgemm_f32_gemm_plan")
     return {name: getattr(out, name) for name, _ in _Plan._fields_}
 
 

@@ -13,19 +13,24 @@
 // 8, the multi-stage pipeline).
 //
 // LDS layout of one stage (a DMA instruction fills 1 KiB in lane order, so
-// the layout is chosen through the global address each lane loads):
-//   * A (BM x BK, k-contiguous rows of BK floats, no padding): the 16-byte
-//     quad Q of row r is stored at quad position Q ^ swz(r).  With the XOR
-//     the operand reads below (one quad of 8 or 16 consecutive rows per
-//     phase) hit distinct banks in both a 32-bank and a 64-bank LDS.
-//   * B (BK x BN, n-contiguous rows as in memory).
+// the layout is chosen through the global address each lane loads).  Each
+// operand is kept in LDS the way it is stored in memory:
+//   * k-contiguous (A stored M x K, B stored N x K): rows of BK floats, one
+//     per m (n), no padding; the 16-byte quad Q of row r is stored at quad
+//     position Q ^ swz(r).  With the XOR the operand reads below (one quad
+//     of 8 or 16 consecutive rows per phase) hit distinct banks in both a
+//     32-bank and a 64-bank LDS.
+//   * m/n-contiguous (A stored K x M, B stored K x N): BK rows of BM (BN)
+//     floats, one per k, as in memory.
 // Operands: as in the register-staged core, lane half h (lanes 32h..32h+31)
-// handles k in [h*BK/2, (h+1)*BK/2), so one ds_read_b128 of A feeds four
-// MFMA steps.  B is read along n: the wave's FN column blocks are
-// interleaved, column FN*l + j of the wave tile belonging to block j, so a
-// lane's FN columns for one k are adjacent (one b32/b64/b128 read per step),
-// and the epilogue writes FN adjacent floats per store.
-//
+// handles k in [h*BK/2, (h+1)*BK/2).  A k-contiguous operand gives four
+// consecutive k of one row per ds_read_b128 (four MFMA steps).  An m/n-
+// contiguous one is read along m (n): the wave's F fragments are
+// interleaved, row (column) F*l + f of the wave tile belonging to fragment f,
+// so a lane's F values for one k are adjacent (one b32/b64/b128 read per
+// step).  B always uses the interleaved column order (a k-contiguous B gets
+// it by loading its rows permuted), so the epilogue writes FN adjacent
+// floats per store.
 // Synchronisation of the ring (chunk c in stage c % S, S >= 3): chunks
 // 0 .. S-2 are loaded up front; during chunk c the loads of chunk c+S-1 go
 // out, spread over its groups, into the stage of chunk c-1.  Each chunk has
@@ -129,24 +134,59 @@ __device__ __forceinline__ int scalar_eq(int a, int b) {
     return r;
 }
 
-template <int FN>
-struct BVec;
+template <int F>
+struct FVec;
 template <>
-struct BVec<1> { typedef float T; };
+struct FVec<1> { typedef float T; };
 template <>
-struct BVec<2> { typedef f32x2 T; };
+struct FVec<2> { typedef f32x2 T; };
 template <>
-struct BVec<4> { typedef f32x4 T; };
+struct FVec<4> { typedef f32x4 T; };
+
+template <int F, int OFF>
+__device__ __forceinline__ typename FVec<F>::T lds_read_vec(uint32_t addr) {
+    if constexpr (F == 1) return lds_read1<OFF>(addr);
+    else if constexpr (F == 2) return lds_read2<OFF>(addr);
+    else return lds_read4<OFF>(addr);
+}
+
+// One operand's registers for a group of four MFMA steps, F fragments.
+// k-contiguous in LDS: a quad of four consecutive k per fragment.
+// m/n-contiguous: per step, the F fragments' values at that step's k.
+template <bool KC, int F>
+struct GroupOps;
+template <int F>
+struct GroupOps<true, F> {
+    f32x4 v[F];
+    __device__ __forceinline__ float at(int u, int f) const { return v[f][u]; }
+    __device__ __forceinline__ void keep() const {
+#pragma unroll
+        for (int f = 0; f < F; ++f) asm volatile("" ::"v"(v[f]));
+    }
+};
+template <int F>
+struct GroupOps<false, F> {
+    typename FVec<F>::T v[4];
+    __device__ __forceinline__ float at(int u, int f) const {
+        if constexpr (F == 1) return v[u];
+        else return v[u][f];
+    }
+    __device__ __forceinline__ void keep() const {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(v[u]));
+    }
+};
 
 // KSPLIT = 2 splits every chunk's K range between two groups of waves
 // (sliced K): with one tile per CU the SIMDs then hold two waves each, one
 // issuing MFMAs while the other waits; the groups' sums are added through
 // LDS at the end of the tile.
-// EDGE: the shape need not be a multiple of the tile (N and K multiples of
-// 4): loads through buffer resources with rows / columns / k beyond the
-// matrix masked to zeros, stores masked.
+// EDGE: the shape need not be a multiple of the tile (the contiguous extent
+// of each operand, and N, multiples of 4): loads through buffer resources
+// with rows / columns / k beyond the matrix masked to zeros, stores masked.
+// TA: A stored K x M (m-contiguous); TB: B stored N x K (k-contiguous).
 template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int S_, int KSPLIT = 1, int LA_ = 1,
-          bool EDGE = false>
+          bool EDGE = false, bool TA = false, bool TB = false>
 struct MfmaDlCore {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
     static constexpr int LA = LA_;                  // groups of operand reads ahead of the MFMAs
@@ -160,24 +200,27 @@ struct MfmaDlCore {
     static constexpr int KW = BK / KSPLIT;         // k values per wave per chunk
     static constexpr int KH = KW / 2;              // k values per lane half per chunk
     static constexpr int G = KH / 4;               // groups of four MFMA steps per chunk
-    static constexpr int QPR = BK / 4;             // quads per A row
+    static constexpr int QPR = BK / 4;             // quads per k-contiguous row
+    static constexpr bool AKC = !TA, BKC = TB;     // operand kept k-contiguous in LDS
     static constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int LDS_FLOATS = S * STAGE;
     static constexpr int A_INSTR = A_STAGE / 256, B_INSTR = B_STAGE / 256;   // 1 KiB DMA blocks
     static constexpr int A_PW = A_INSTR / NW, B_PW = B_INSTR / NW;           // per wave
     static constexpr int L = A_PW + B_PW;          // loads per wave per chunk
-    static constexpr int A_RPI = 256 / BK;         // A rows per DMA block
-    static constexpr int B_RPI = 256 / BN;         // B k-rows per DMA block
     static constexpr int TILE_FLOATS = BM * BN;
-    typedef typename BVec<FN>::T bvec;
+    typedef GroupOps<AKC, FM> AOps;
+    typedef GroupOps<BKC, FN> BOps;
 
-    static_assert(WTM % 32 == 0 && (FN == 1 || FN == 2 || FN == 4), "wave tile");
-    static_assert(BK == 16 || BK == 32 || BK == 64, "A swizzle defined for BK 16/32/64");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && (FM == 1 || FM == 2 || FM == 4) &&
+                      (FN == 1 || FN == 2 || FN == 4),
+                  "wave tile");
+    static_assert(BK == 16 || BK == 32 || BK == 64, "swizzle defined for BK 16/32/64");
     static_assert(KSPLIT == 1 || KSPLIT == 2, "K groups");
     static_assert(LA == 1 || LA == 2, "read-ahead depth");
     static_assert(G > LA && G % NS == 0, "operand register sets rotate by group; the rotation must carry");
-    static_assert(BN <= 256 && 256 % BN == 0, "B DMA block = whole k-rows");
+    static_assert((AKC || (BM <= 256 && 256 % BM == 0)) && (BKC || (BN <= 256 && 256 % BN == 0)),
+                  "DMA block = whole rows of an m/n-contiguous operand");
     static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0 && A_PW >= 1 && B_PW >= 1,
                   "DMA blocks must split evenly over the waves");
     static_assert(S >= 3 && L * (S - 2) < 64, "ring depth (loads run S-2 chunks ahead) / vmcnt range");
@@ -202,6 +245,14 @@ struct MfmaDlCore {
         else return r & 15;
     }
 
+    // Tile column held by row r of a k-contiguous B stage: the rows are
+    // loaded permuted so that fragment j's 32 columns (FN*l + j of the wave
+    // tile, l = 0..31) sit in consecutive rows, read like A's.
+    __device__ __forceinline__ static int b_kc_col(int r) {
+        const int w = r / WTN, f = (r % WTN) / 32, l = r % 32;
+        return w * WTN + FN * l + f;
+    }
+
     // Per-lane addressing, computed once per tile.  The main loop holds no
     // vector ALU instruction: on gfx950 one between two dependent MFMAs
     // stalls the second for most of an MFMA's duration, so every address
@@ -214,46 +265,76 @@ struct MfmaDlCore {
         uint32_t vb[B_PW];
         uint32_t va_t[A_PW];     // EDGE: the same for the tile's last chunk (K tail masked)
         uint32_t vb_t[B_PW];
-        uint32_t ra[S][FM][G];   // LDS byte address of the A operands of group q, per stage
-        uint32_t rb[S];          // LDS byte address of the B operand of step 0, per stage
+        // LDS byte addresses of the operand reads, per stage: per fragment
+        // and group for a k-contiguous operand (the swizzle moves each
+        // quad), one base for an m/n-contiguous one (steps at fixed offsets).
+        uint32_t ra[S][AKC ? FM : 1][AKC ? G : 1];
+        uint32_t rb[S][BKC ? FN : 1][BKC ? G : 1];
         uint32_t lds;            // uniform: LDS byte address of the ring
         int wave;
     };
+
+    // Source byte offset of this lane's 16 bytes in DMA block blk of an
+    // operand (within the tile at chunk 0), whether it lies inside the matrix,
+    // and whether it does in the tile's last chunk (k < kt).  KC: LDS row r
+    // holds tile row src(r) (length BK); MC: LDS row kr holds k row kr
+    // (length BX).  `lim` = valid rows (KC) or columns (MC) from the tile's
+    // first.
+    template <bool KC, int BX, class Src>
+    __device__ __forceinline__ static void dma_lane(int blk, int lane, int64_t ld, int lim, int kt, Src src,
+                                                    uint32_t &off, uint32_t &off_t) {
+        uint32_t o;
+        bool ok, ok_t;
+        if constexpr (KC) {
+            const int r = blk * (256 / BK) + lane / QPR;
+            const int q = (lane % QPR) ^ swz(r);
+            const int row = src(r);
+            o = (uint32_t)(((int64_t)row * ld + 4 * q) * 4);
+            ok = row < lim;
+            ok_t = ok && 4 * q < kt;
+        } else {
+            const int kr = blk * (256 / BX) + lane / (BX / 4), cq = lane % (BX / 4);
+            o = (uint32_t)(((int64_t)kr * ld + 4 * cq) * 4);
+            ok = 4 * cq < lim;
+            ok_t = ok && kr < kt;
+        }
+        off = !EDGE || ok ? o : kOutOfRange;
+        off_t = !EDGE || ok_t ? o : kOutOfRange;
+    }
 
     __device__ __forceinline__ void setup(Geo &g, const KernelArgs &a, float *lds, int tm, int tn, int k0) const {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        // EDGE: valid k values in the tile's last chunk (K and every chunk
-        // boundary are multiples of 4, so a quad is all in or all out).
+        // EDGE: valid k values in the tile's last chunk (a k-contiguous
+        // operand needs K a multiple of 4, so its quads are all in or out).
         const int kt = EDGE ? a.K - (a.ipt - 1) * BK : BK;
+        const int m_lim = a.M - tm * BM, n_lim = a.N - tn * BN;
 #pragma unroll
-        for (int u = 0; u < A_PW; ++u) {
-            const int blk = g.wave + NW * u;
-            const int r = blk * A_RPI + lane / QPR;
-            const int q = (lane % QPR) ^ swz(r);
-            const uint32_t off = (uint32_t)(((int64_t)r * a.lda + 4 * q) * 4);
-            const bool row_ok = !EDGE || tm * BM + r < a.M;
-            g.va[u] = row_ok ? off : kOutOfRange;
-            g.va_t[u] = row_ok && 4 * q < kt ? off : kOutOfRange;
-        }
+        for (int u = 0; u < A_PW; ++u)
+            dma_lane<AKC, BM>(g.wave + NW * u, lane, a.lda, m_lim, kt, [](int r) { return r; }, g.va[u], g.va_t[u]);
 #pragma unroll
-        for (int u = 0; u < B_PW; ++u) {
-            const int blk = g.wave + NW * u;
-            const int kr = blk * B_RPI + lane / (BN / 4);
-            const uint32_t off = (uint32_t)(((int64_t)kr * a.ldb + 4 * (lane % (BN / 4))) * 4);
-            const bool col_ok = !EDGE || tn * BN + 4 * (lane % (BN / 4)) < a.N;
-            g.vb[u] = col_ok ? off : kOutOfRange;
-            g.vb_t[u] = col_ok && kr < kt ? off : kOutOfRange;
+        for (int u = 0; u < B_PW; ++u)
+            dma_lane<BKC, BN>(g.wave + NW * u, lane, a.ldb, n_lim, kt, [](int r) { return b_kc_col(r); }, g.vb[u],
+                              g.vb_t[u]);
+        if constexpr (AKC) {
+            g.ga = (const char *)(a.A + (int64_t)tm * BM * a.lda + (int64_t)k0 * BK);
+            g.a_step = (int64_t)BK * 4;
+        } else {
+            g.ga = (const char *)(a.A + (int64_t)k0 * BK * a.lda + (int64_t)tm * BM);
+            g.a_step = (int64_t)BK * a.lda * 4;
         }
-        g.ga = (const char *)(a.A + (int64_t)tm * BM * a.lda + (int64_t)k0 * BK);
-        g.gb = (const char *)(a.B + (int64_t)k0 * BK * a.ldb + (int64_t)tn * BN);
+        if constexpr (BKC) {
+            g.gb = (const char *)(a.B + (int64_t)tn * BN * a.ldb + (int64_t)k0 * BK);
+            g.b_step = (int64_t)BK * 4;
+        } else {
+            g.gb = (const char *)(a.B + (int64_t)k0 * BK * a.ldb + (int64_t)tn * BN);
+            g.b_step = (int64_t)BK * a.ldb * 4;
+        }
         if constexpr (EDGE) {
             g.rsa = buffer_rsrc(g.ga);
             g.rsb = buffer_rsrc(g.gb);
         }
-        g.a_step = (int64_t)BK * 4;
-        g.b_step = (int64_t)BK * a.ldb * 4;
         const int kg = g.wave / NW_MN, wmn = g.wave % NW_MN;
         const int wm = wmn / WAVES_N, wn = wmn % WAVES_N;
         const int lr = lane & 31, lh = lane >> 5;
@@ -261,14 +342,29 @@ struct MfmaDlCore {
         g.lds = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
         for (int st = 0; st < S; ++st) {
+            const uint32_t sa = base + 4 * st * STAGE, sb = sa + 4 * A_STAGE;
+            if constexpr (AKC) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int r = wm * WTM + i * 32 + lr;
+                for (int i = 0; i < FM; ++i) {
+                    const int r = wm * WTM + i * 32 + lr;
 #pragma unroll
-                for (int q = 0; q < G; ++q)
-                    g.ra[st][i][q] = base + 4 * (st * STAGE + r * BK + 4 * ((kg * (KW / 4) + lh * G + q) ^ swz(r)));
+                    for (int q = 0; q < G; ++q)
+                        g.ra[st][i][q] = sa + 4 * (r * BK + 4 * ((kg * (KW / 4) + lh * G + q) ^ swz(r)));
+                }
+            } else {
+                g.ra[st][0][0] = sa + 4 * ((kg * KW + lh * KH) * BM + wm * WTM + FM * lr);
             }
-            g.rb[st] = base + 4 * (st * STAGE + A_STAGE + (kg * KW + lh * KH) * BN + wn * WTN + FN * lr);
+            if constexpr (BKC) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int r = wn * WTN + j * 32 + lr;
+#pragma unroll
+                    for (int q = 0; q < G; ++q)
+                        g.rb[st][j][q] = sb + 4 * (r * BK + 4 * ((kg * (KW / 4) + lh * G + q) ^ swz(r)));
+                }
+            } else {
+                g.rb[st][0][0] = sb + 4 * ((kg * KW + lh * KH) * BN + wn * WTN + FN * lr);
+            }
         }
     }
 
@@ -309,36 +405,34 @@ struct MfmaDlCore {
         }
     }
 
-    // Operands of group TQ (four MFMA steps) from stage ST: R = FM + 4
-    // read instructions.
-    static constexpr int R = FM + 4;
-    template <int OFF>
-    __device__ __forceinline__ static bvec read_bvec(uint32_t addr) {
-        if constexpr (FN == 1) return lds_read1<OFF>(addr);
-        else if constexpr (FN == 2) return lds_read2<OFF>(addr);
-        else return lds_read4<OFF>(addr);
+    // Operands of group TQ (four MFMA steps) from stage ST: R read
+    // instructions (one per fragment for a k-contiguous operand, one per
+    // step for an m/n-contiguous one).
+    static constexpr int R = (AKC ? FM : 4) + (BKC ? FN : 4);
+    template <bool KC, int F, int BX, int ST, int TQ, int NF, int NQ>
+    __device__ __forceinline__ static void read_ops(GroupOps<KC, F> &o, const uint32_t (&addr)[S][NF][NQ]) {
+        if constexpr (KC) {
+#pragma unroll
+            for (int f = 0; f < F; ++f) o.v[f] = lds_read4<0>(addr[ST][f][TQ]);
+        } else {
+            o.v[0] = lds_read_vec<F, (4 * TQ + 0) * BX * 4>(addr[ST][0][0]);
+            o.v[1] = lds_read_vec<F, (4 * TQ + 1) * BX * 4>(addr[ST][0][0]);
+            o.v[2] = lds_read_vec<F, (4 * TQ + 2) * BX * 4>(addr[ST][0][0]);
+            o.v[3] = lds_read_vec<F, (4 * TQ + 3) * BX * 4>(addr[ST][0][0]);
+        }
     }
     template <int ST, int TQ>
-    __device__ __forceinline__ static void read_group(const Geo &g, f32x4 (&av)[FM], bvec (&bv)[4]) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) av[i] = lds_read4<0>(g.ra[ST][i][TQ]);
-        bv[0] = read_bvec<(4 * TQ + 0) * BN * 4>(g.rb[ST]);
-        bv[1] = read_bvec<(4 * TQ + 1) * BN * 4>(g.rb[ST]);
-        bv[2] = read_bvec<(4 * TQ + 2) * BN * 4>(g.rb[ST]);
-        bv[3] = read_bvec<(4 * TQ + 3) * BN * 4>(g.rb[ST]);
+    __device__ __forceinline__ static void read_group(const Geo &g, AOps &av, BOps &bv) {
+        read_ops<AKC, FM, BM, ST, TQ>(av, g.ra);
+        read_ops<BKC, FN, BN, ST, TQ>(bv, g.rb);
     }
 
-    __device__ __forceinline__ static float bcomp(const bvec &v, int j) {
-        if constexpr (FN == 1) return v;
-        else return v[j];
-    }
-
-    __device__ __forceinline__ void mfma_step(const f32x4 (&av)[FM], const bvec &b, int u) {
+    __device__ __forceinline__ void mfma_step(const AOps &av, const BOps &bv, int u) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][u], bcomp(b, j), acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.at(u, i), bv.at(u, j), acc[i][j], 0, 0, 0);
     }
 
     // DMA instructions [dma_lo(q), dma_lo(q+1)) go out in group q: the
@@ -360,8 +454,7 @@ struct MfmaDlCore {
     //   * The reads for group Q+LA (of this chunk or the next), then the
     //     group's DMA instructions, then the other three MFMA steps.
     template <int ST, int Q>
-    __device__ __forceinline__ void group(Geo &g, int c, int nch, int tail_ch, f32x4 (&av)[NS][FM],
-                                          bvec (&bv)[NS][4]) {
+    __device__ __forceinline__ void group(Geo &g, int c, int nch, int tail_ch, AOps (&av)[NS], BOps (&bv)[NS]) {
         // Whether this chunk still loads (c <= nch - S), as a scalar register:
         // a boolean carried across blocks would be kept in a vector register,
         // and set and tested with vector ALU instructions.
@@ -372,7 +465,7 @@ struct MfmaDlCore {
         constexpr int NXT = (ST + 1) % S, PRV = (ST + S - 1) % S;
         wait_counts<63, (LA - 1) * R>();
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step(av[cs], bv[cs][0], 0);
+        mfma_step(av[cs], bv[cs], 0);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (TQ < G) {
             read_group<ST, TQ>(g, av[ts], bv[ts]);
@@ -395,21 +488,21 @@ struct MfmaDlCore {
 #undef SGEMM_DL_STEADY
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 1; u < 4; ++u) mfma_step(av[cs], bv[cs][u], u);
+        for (int u = 1; u < 4; ++u) mfma_step(av[cs], bv[cs], u);
         __builtin_amdgcn_sched_barrier(0);
     }
 
     template <int ST, int... Qs>
     __device__ __forceinline__ void chunk_groups(std::integer_sequence<int, Qs...>, Geo &g, int c, int nch,
-                                                 int tail_ch, f32x4 (&av)[NS][FM], bvec (&bv)[NS][4]) {
+                                                 int tail_ch, AOps (&av)[NS], BOps (&bv)[NS]) {
         (group<ST, Qs>(g, c, nch, tail_ch, av, bv), ...);
     }
 
     // Chunks ST, ST+1, ... of the ring from chunk c on; true once chunk
     // nch-1 is done.  Chunk c loads chunk c+S-1 while c <= nch-S.
     template <int ST>
-    __device__ __forceinline__ bool chunks_from(int &c, int nch, int tail_ch, Geo &g, f32x4 (&av)[NS][FM],
-                                                bvec (&bv)[NS][4]) {
+    __device__ __forceinline__ bool chunks_from(int &c, int nch, int tail_ch, Geo &g, AOps (&av)[NS],
+                                                BOps (&bv)[NS]) {
         chunk_groups<ST>(std::make_integer_sequence<int, G>{}, g, c, nch, tail_ch, av, bv);
         if (++c >= nch) return true;
         if constexpr (ST + 1 < S) return chunks_from<ST + 1>(c, nch, tail_ch, g, av, bv);
@@ -449,8 +542,8 @@ struct MfmaDlCore {
         else wait_counts<0, 0>();
         lds_barrier();
 
-        f32x4 av[NS][FM];
-        bvec bv[NS][4];
+        AOps av[NS];
+        BOps bv[NS];
         read_group<0, 0>(g, av[0], bv[0]);
         if constexpr (LA == 2) read_group<0, 1>(g, av[1], bv[1]);
 
@@ -462,10 +555,8 @@ struct MfmaDlCore {
         wait_counts<0, 0>();
 #pragma unroll
         for (int v = 0; v < NS; ++v) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i) asm volatile("" ::"v"(av[v][i]));
-#pragma unroll
-            for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(bv[v][u]));
+            av[v].keep();
+            bv[v].keep();
         }
 
         if constexpr (KSPLIT == 2) {
@@ -495,8 +586,10 @@ struct MfmaDlCore {
         }
     }
 
-    // C element of block (i, j), register r, for this lane:
-    //   row = 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,  col = FN (lane % 32) + j.
+    // C element of block (i, j), register r, for this lane, with
+    // rho = 8 (r / 4) + 4 (lane / 32) + r % 4 the MFMA's output row:
+    //   row = 32 i + rho (A k-contiguous) or FM rho + i (A m-contiguous,
+    //   fragments interleaved), col = FN (lane % 32) + j.
     // Only the first K group holds the result.  EDGE: rows beyond M and
     // columns beyond N are not written (N is a multiple of 4, so a lane's FN
     // adjacent columns are all in or all out).
@@ -506,14 +599,15 @@ struct MfmaDlCore {
         const int wave = tid >> 6, lane = tid & 63;
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
         const int lr = lane & 31, lh = lane >> 5;
-        const int row0 = tm * BM + wm * WTM + 4 * lh, col0 = tn * BN + wn * WTN + FN * lr;
+        const int row0 = tm * BM + wm * WTM + (AKC ? 4 : 4 * FM) * lh, col0 = tn * BN + wn * WTN + FN * lr;
         if (EDGE && col0 >= a.N) return;
         float *c = a.C + (int64_t)row0 * a.ldc + col0;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int dr = i * 32 + 8 * (r >> 2) + (r & 3);
+                const int rho = 8 * (r >> 2) + (r & 3);
+                const int dr = AKC ? i * 32 + rho : FM * rho + i;
                 if (EDGE && row0 + dr >= a.M) continue;
                 float *p = c + (int64_t)dr * a.ldc;
                 if constexpr (FN == 1) {
@@ -571,11 +665,18 @@ using Dl128x128x32K2 = MfmaDlCore<128, 128, 32, 2, 2, 3, 2>;
 using Dl64x64x64 = MfmaDlCore<64, 64, 64, 2, 2, 3, 1, 2>;
 using Dl128x256x16 = MfmaDlCore<128, 256, 16, 2, 2, 3>;
 using Dl256x128x16 = MfmaDlCore<256, 128, 16, 2, 2, 3>;
-// Edge-masking variants of the configurations the automatic choice uses.
-using Dl64x64x32E = MfmaDlCore<64, 64, 32, 2, 2, 4, 1, 2, true>;
-using Dl64x64x64E = MfmaDlCore<64, 64, 64, 2, 2, 3, 1, 2, true>;
-using Dl128x128x32K2E = MfmaDlCore<128, 128, 32, 2, 2, 3, 2, 1, true>;
-using Dl256x256x16E = MfmaDlCore<256, 256, 16, 4, 2, 3, 1, 1, true>;
+// Edge-masking variants of the configurations the automatic choice uses,
+// for each storage order of A and B (NN, TN, NT, TT).
+#define SGEMM_DL_EDGE_CORES(name, BM, BN, BK, WM, WN, S, KS, LA)            \
+    using name##E = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true>;          \
+    using name##TN = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, true>;   \
+    using name##NT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, false, true>; \
+    using name##TT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, true, true>;
+SGEMM_DL_EDGE_CORES(Dl64x64x32, 64, 64, 32, 2, 2, 4, 1, 2)
+SGEMM_DL_EDGE_CORES(Dl64x64x64, 64, 64, 64, 2, 2, 3, 1, 2)
+SGEMM_DL_EDGE_CORES(Dl128x128x32K2, 128, 128, 32, 2, 2, 3, 2, 1)
+SGEMM_DL_EDGE_CORES(Dl256x256x16, 256, 256, 16, 4, 2, 3, 1, 1)
+#undef SGEMM_DL_EDGE_CORES
 
 template <class Core>
 static hipError_t launch(const KernelArgs &a, hipStream_t s) {
@@ -603,22 +704,30 @@ static hipError_t occ(int *n) {
     X(SGEMM_CFG_DL_128x256x16, Dl128x256x16)        \
     X(SGEMM_CFG_DL_256x128x16, Dl256x128x16)
 
-#define SGEMM_DL_EDGE_CONFIGS(X)                    \
-    X(SGEMM_CFG_DL_64x64x32, Dl64x64x32E)           \
-    X(SGEMM_CFG_DL_64x64x64, Dl64x64x64E)           \
-    X(SGEMM_CFG_DL_128x128x32_K2, Dl128x128x32K2E)  \
-    X(SGEMM_CFG_DL_256x256x16, Dl256x256x16E)
+#define SGEMM_DL_EDGE_CONFIGS(X)                  \
+    X(SGEMM_CFG_DL_64x64x32, Dl64x64x32)          \
+    X(SGEMM_CFG_DL_64x64x64, Dl64x64x64)          \
+    X(SGEMM_CFG_DL_128x128x32_K2, Dl128x128x32K2) \
+    X(SGEMM_CFG_DL_256x256x16, Dl256x256x16)
 
 hipError_t launch_mfma_dl(int cfg, const KernelArgs &a, hipStream_t s) {
     if (a.edge) {
+        const int layout = (a.trans_a ? 1 : 0) | (a.trans_b ? 2 : 0);
         switch (cfg) {
-#define X(id, core) \
-    case id: return launch<core>(a, s);
+#define X(id, core)                                \
+    case id:                                       \
+        switch (layout) {                          \
+        case 0: return launch<core##E>(a, s);      \
+        case 1: return launch<core##TN>(a, s);     \
+        case 2: return launch<core##NT>(a, s);     \
+        default: return launch<core##TT>(a, s);    \
+        }
             SGEMM_DL_EDGE_CONFIGS(X)
 #undef X
         default: return hipErrorInvalidValue;
         }
     }
+    if (a.trans_a || a.trans_b) return hipErrorInvalidValue;
     switch (cfg) {
 #define X(id, core) \
     case id: return launch<core>(a, s);

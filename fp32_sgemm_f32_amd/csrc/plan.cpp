@@ -28,13 +28,13 @@ const CfgInfo kCfgs[] = {
     {SGEMM_CFG_MFMA_64x64x64, 64, 64, 64, 256, kKindMfma, 2, false, false, "mfma_64x64x64"},
     {SGEMM_CFG_MFMA_128x128x64, 128, 128, 64, 256, kKindMfma, 1, false, false, "mfma_128x128x64"},
     {SGEMM_CFG_MFMA_64x64x128, 64, 64, 128, 256, kKindMfma, 1, false, false, "mfma_64x64x128"},
-    {SGEMM_CFG_DL_64x64x32, 64, 64, 32, 256, kKindMfmaDl, 2, true, false, "dl_64x64x32"},
+    {SGEMM_CFG_DL_64x64x32, 64, 64, 32, 256, kKindMfmaDl, 2, true, true, "dl_64x64x32"},
     {SGEMM_CFG_DL_64x64x64_K2, 64, 64, 64, 512, kKindMfmaDl, 1, false, false, "dl_64x64x64_k2"},
     {SGEMM_CFG_DL_128x128x32, 128, 128, 32, 256, kKindMfmaDl, 1, false, false, "dl_128x128x32"},
-    {SGEMM_CFG_DL_256x256x16, 256, 256, 16, 512, kKindMfmaDl, 1, true, false, "dl_256x256x16"},
+    {SGEMM_CFG_DL_256x256x16, 256, 256, 16, 512, kKindMfmaDl, 1, true, true, "dl_256x256x16"},
     {SGEMM_CFG_DL_64x64x32_K2, 64, 64, 32, 512, kKindMfmaDl, 2, false, false, "dl_64x64x32_k2"},
-    {SGEMM_CFG_DL_128x128x32_K2, 128, 128, 32, 512, kKindMfmaDl, 1, true, false, "dl_128x128x32_k2"},
-    {SGEMM_CFG_DL_64x64x64, 64, 64, 64, 256, kKindMfmaDl, 1, true, false, "dl_64x64x64"},
+    {SGEMM_CFG_DL_128x128x32_K2, 128, 128, 32, 512, kKindMfmaDl, 1, true, true, "dl_128x128x32_k2"},
+    {SGEMM_CFG_DL_64x64x64, 64, 64, 64, 256, kKindMfmaDl, 1, true, true, "dl_64x64x64"},
     {SGEMM_CFG_DL_128x256x16, 128, 256, 16, 256, kKindMfmaDl, 2, false, false, "dl_128x256x16"},
     {SGEMM_CFG_DL_256x128x16, 256, 128, 16, 256, kKindMfmaDl, 2, false, false, "dl_256x128x16"},
     {SGEMM_CFG_GENERIC_64x64x16, 64, 64, 16, 256, kKindGeneric, 2, true, true, "generic_64x64x16"},
@@ -87,16 +87,18 @@ static int64_t tiles_of(int cfg, int M, int N) {
 
 // Automatic choice, from timings of the configurations on MI355X (256 CUs):
 //   * 256x256x16 tiles (8 waves) when every CU gets at least one (149
-//     TFLOP/s at 4096^3);
+//     TFLOP/s at 4096^3), the register-staged kernel when the tile divides
+//     the shape and A and B are stored M x K and K x N;
 //   * else 128x128 tiles loaded straight into LDS, two K groups of waves,
 //     when every CU gets one (138 at 2048^3);
 //   * else 64x64 tiles loaded straight into LDS (142 at 1024x1024x16384,
 //     99 at 1024^3), with a 64-deep K chunk where K allows.
+// Layouts the vector kernels cannot load go to the general kernel.
 static int auto_config(int M, int N, int K, int cus, bool aligned, bool transposed) {
-    if (!aligned || transposed) return SGEMM_CFG_GENERIC_64x64x16;
+    if (!aligned) return SGEMM_CFG_GENERIC_64x64x16;
     const int big = SGEMM_CFG_MFMA_256x256x16, big_edge = SGEMM_CFG_DL_256x256x16,
               mid = SGEMM_CFG_DL_128x128x32_K2, small = SGEMM_CFG_DL_64x64x64, small32 = SGEMM_CFG_DL_64x64x32;
-    if (tiles_of(big, M, N) >= cus) return divides(kCfgs[big], M, N, K) ? big : big_edge;
+    if (tiles_of(big, M, N) >= cus) return !transposed && divides(kCfgs[big], M, N, K) ? big : big_edge;
     if (tiles_of(mid, M, N) >= cus) return mid;
     if (K % 64 == 0 || K % 32 != 0) return small;
     return small32;
@@ -115,10 +117,14 @@ int staged_equivalent(int cfg) {
     }
 }
 
-bool dl_offsets_fit(int cfg, bool edge, int64_t lda, int64_t ldb) {
+bool dl_offsets_fit(int cfg, bool edge, int64_t lda, int64_t ldb, bool trans_a, bool trans_b) {
     if (kCfgs[cfg].kind != kKindMfmaDl) return true;
     const int64_t lim = (int64_t)1 << (edge ? 31 : 32);
-    return (int64_t)kCfgs[cfg].bm * lda * 4 < lim && (int64_t)kCfgs[cfg].bk * ldb * 4 < lim;
+    // Rows a lane's offset spans from the operand's base: the tile's rows of
+    // a k-contiguous operand, the chunk's k rows of an m/n-contiguous one.
+    const int64_t rows_a = trans_a ? kCfgs[cfg].bk : kCfgs[cfg].bm;
+    const int64_t rows_b = trans_b ? kCfgs[cfg].bn : kCfgs[cfg].bk;
+    return rows_a * lda * 4 < lim && rows_b * ldb * 4 < lim;
 }
 
 int make_plan(const PlanRequest &req, Plan *out) {

@@ -66,11 +66,12 @@ struct Plan {
 int make_plan(const PlanRequest &req, Plan *out);
 
 // The configurations that load tiles straight into LDS address a lane's
-// source as a 32-bit byte offset from the tile's first row (A) or the
-// chunk's first row (B): they need BM * lda and BK * ldb under 2^30 floats
-// (2^29 for the edge-masking variants, whose offsets mark a masked lane
-// with the top bit).
-bool dl_offsets_fit(int cfg, bool edge, int64_t lda, int64_t ldb);
+// source as a 32-bit byte offset from the tile's first row (an operand stored
+// k-contiguous: A M x K, B N x K) or the chunk's first k row (stored
+// m/n-contiguous): they need BM * lda or BK * lda, and BK * ldb or BN * ldb,
+// under 2^30 floats (2^29 for the edge-masking variants, whose offsets mark a
+// masked lane with the top bit).
+bool dl_offsets_fit(int cfg, bool edge, int64_t lda, int64_t ldb, bool trans_a = false, bool trans_b = false);
 
 // The register-staged configuration with the same tile as `cfg` (itself
 // for those).

@@ -225,7 +225,7 @@ int run(const Call &c) {
                     env_int("SGEMM_F32_SK_WG_PER_CU", 0), vector_layout(c) ? 1 : 0, c.ta, c.tb};
     Plan p;
     if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
-    if (c.K > 0 && !dl_offsets_fit(p.config, p.edge != 0, c.lda, c.ldb)) {
+    if (c.K > 0 && !dl_offsets_fit(p.config, p.edge != 0, c.lda, c.ldb, c.ta != 0, c.tb != 0)) {
         // Leading dimensions too large for the 32-bit source offsets of the
         // direct-to-LDS kernels: an automatic choice falls back to the
         // register-staged kernel of the same tile (the general one when the
@@ -334,12 +334,15 @@ SGEMM_API const char *sgemm_f32_status_string(int status) {
 
 SGEMM_API int sgemm_f32_last_hip_error(void) { return sgemm::g_last_hip_error; }
 
-SGEMM_API int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,
-                             const int *occupancy, int sk_wg_per_cu, sgemm_f32_plan_t *out) {
+static int plan_for(int ta, int tb, int M, int N, int K, int config, int sched, int num_cus,
+                    const int *occupancy, int sk_wg_per_cu, sgemm_f32_plan_t *out) {
     if (!out) return SGEMM_ERR_NULL;
-    // Planned for dense operands (lda = K, ldb = ldc = N) on 16-byte boundaries.
+    if ((ta != 0 && ta != 1) || (tb != 0 && tb != 1)) return SGEMM_ERR_CONFIG;
+    // Dense operands on 16-byte boundaries: the vector layout holds when
+    // the stored row lengths of A and B, and N, are multiples of 4.
+    const int a_cols = ta ? M : K, b_cols = tb ? K : N;
     sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu,
-                           (N % 4 == 0 && K % 4 == 0) ? 1 : 0, 0, 0};
+                           (a_cols % 4 == 0 && b_cols % 4 == 0 && N % 4 == 0) ? 1 : 0, ta, tb};
     sgemm::Plan p;
     int st = sgemm::make_plan(req, &p);
     if (st != SGEMM_OK) return st;
@@ -361,6 +364,16 @@ SGEMM_API int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num
     out->sk_iters = p.sk_iters;
     out->workspace_bytes = p.workspace_bytes;
     return SGEMM_OK;
+}
+
+SGEMM_API int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,
+                             const int *occupancy, int sk_wg_per_cu, sgemm_f32_plan_t *out) {
+    return plan_for(0, 0, M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu, out);
+}
+
+SGEMM_API int sgemm_f32_gemm_plan(int trans_a, int trans_b, int M, int N, int K, int config, int sched,
+                                  int num_cus, const int *occupancy, int sk_wg_per_cu, sgemm_f32_plan_t *out) {
+    return plan_for(trans_a, trans_b, M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu, out);
 }
 
 SGEMM_API int sgemm_f32_release(void) {

@@ -216,6 +216,14 @@ typedef struct sgemm_f32_plan_t {
 int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,
                    const int *occupancy, int sk_wg_per_cu, sgemm_f32_plan_t *out);
 
+/* sgemm_f32_plan for the BLAS form (sgemm_f32_gemm) with A and B in the
+ * storage orders trans_a / trans_b (0 or 1, as there), dense operands (each
+ * leading dimension equal to its stored row length) on 16-byte boundaries.
+ * SGEMM_ERR_CONFIG for a transpose flag outside {0, 1}. */
+int sgemm_f32_gemm_plan(int trans_a, int trans_b, int M, int N, int K, int config, int sched,
+                        int num_cus, const int *occupancy, int sk_wg_per_cu,
+                        sgemm_f32_plan_t *out);
+
 /*
  * Free every workspace the library holds (all devices, all streams).  The
  * caller must ensure no sgemm call is still executing.  Returns SGEMM_OK or

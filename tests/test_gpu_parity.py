@@ -256,6 +256,62 @@ def test_blas_form(dev, layout, scaling, shape):
         check(C.cpu().numpy(), C_ref, S, f"blas/{sg.SCHED_NAMES[sched]}")
 
 
+# The direct-to-LDS kernels load each operand in its storage order (A
+# stored K x M, B stored N x K); they need the stored row lengths of A and B,
+# and N, to be multiples of 4.  Shapes: tile multiples, ragged in every
+# dimension, K not a multiple of 4 (only A K x M with B K x N qualifies), M
+# not a multiple of 4 (only A stored M x K qualifies).
+DL_LAYOUT_CFGS = [sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_DL_256x256x16]
+LAYOUT_SHAPES = [(512, 512, 512), (260, 196, 100), (516, 388, 772), (132, 68, 1004), (64, 1028, 36),
+                 (130, 196, 100), (128, 196, 102)]
+
+
+def vector_layout(M, N, K, ta, tb):
+    return (M if ta else K) % 4 == 0 and (K if tb else N) % 4 == 0 and N % 4 == 0
+
+
+@pytest.mark.parametrize("shape", LAYOUT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: f"ta{l[0]}tb{l[1]}")
+@pytest.mark.parametrize("config", [sg.CFG_AUTO] + DL_LAYOUT_CFGS, ids=lambda c: sg.CFG_NAMES[c])
+def test_storage_orders_on_direct_to_lds_kernels(dev, config, layout, shape):
+    import torch
+    (ta, tb), (M, N, K) = layout, shape
+    alpha, beta = 1.5, -0.5
+    log(f"case layout config={sg.CFG_NAMES[config]} ta={ta} tb={tb} shape={shape}")
+    A, B = workloads.generate(M, N, K, "normal", 4000 + M + 3 * N + 7 * K)
+    As, Bs = stored(A, ta), stored(B, tb)
+    C0 = c0_of(M, N, 4100 + K)
+    if config != sg.CFG_AUTO and not vector_layout(M, N, K, ta, tb):
+        with pytest.raises(sg.SgemmError) as e:
+            sg.gemm(to_dev(As, dev), to_dev(Bs, dev), to_dev(C0, dev), alpha, beta, ta, tb, config=config)
+        torch.cuda.synchronize()
+        assert e.value.status == sg.ERR_CONFIG
+        return
+    C_ref, S = oracle.gemm_blas(As, Bs, C0, alpha, beta, ta, tb)
+    for sched in (sg.SCHED_DP, sg.SCHED_STREAMK):
+        C = to_dev(C0, dev).clone()
+        sg.gemm(to_dev(As, dev), to_dev(Bs, dev), C, alpha, beta, ta, tb, config=config, sched=sched)
+        torch.cuda.synchronize()
+        check(C.cpu().numpy(), C_ref, S, f"{sg.CFG_NAMES[config]}/ta{ta}tb{tb}/{sg.SCHED_NAMES[sched]}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS[1:], ids=lambda l: f"ta{l[0]}tb{l[1]}")
+@pytest.mark.parametrize("config", DL_LAYOUT_CFGS, ids=lambda c: sg.CFG_NAMES[c])
+def test_storage_orders_integer_inputs_bit_exact(dev, config, layout):
+    import torch
+    ta, tb = layout
+    M, N, K = 516, 772, 1004
+    log(f"case layout int4 config={sg.CFG_NAMES[config]} ta={ta} tb={tb}")
+    A, B = workloads.generate(M, N, K, "int4", 79)
+    As, Bs = stored(A, ta), stored(B, tb)
+    C_ref, _ = oracle.gemm_blas(As, Bs, None, 1.0, 0.0, ta, tb)
+    for sched in (sg.SCHED_DP, sg.SCHED_STREAMK):
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+        sg.gemm(to_dev(As, dev), to_dev(Bs, dev), C, 1.0, 0.0, ta, tb, config=config, sched=sched)
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref)
+
+
 @pytest.mark.parametrize("config", [sg.CFG_MFMA_256x256x16, sg.CFG_MFMA_128x128x32, sg.CFG_VALU_128x128x8,
                                     sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_GENERIC_64x64x16],
                          ids=lambda c: sg.CFG_NAMES[c])

@@ -207,6 +207,50 @@ def test_auto_choices_on_256_cus():
     assert p["config"] == sg.CFG_GENERIC_64x64x16
 
 
+# Configurations that also run A stored K x M and / or B stored N x K.
+LAYOUT_CFGS = EDGE_CFGS
+
+
+@pytest.mark.parametrize("layout", [(1, 0), (0, 1), (1, 1)], ids=["TN", "NT", "TT"])
+def test_auto_choices_for_transposed_storage(layout):
+    """The same regimes as A M x K, B K x N, on the edge-masking kernels
+    (the register-staged 256 x 256 one loads only that order), and the
+    general kernel when a stored row length is not a multiple of 4."""
+    ta, tb = layout
+    occ = OCC
+
+    def cfg(M, N, K):
+        return sg.plan(M, N, K, num_cus=256, occupancy=occ, trans_a=ta, trans_b=tb)["config"]
+
+    assert cfg(4096, 4096, 4096) == sg.CFG_DL_256x256x16
+    assert cfg(2048, 2048, 2048) == sg.CFG_DL_128x128x32_K2
+    assert cfg(1024, 1024, 1024) == sg.CFG_DL_64x64x64
+    assert cfg(1024, 1024, 16384) == sg.CFG_DL_64x64x64
+    assert cfg(1024, 1024, 96) == sg.CFG_DL_64x64x32
+    # A stored K x M has rows of M floats; B stored N x K rows of K floats.
+    assert cfg(1022, 1024, 1024) == (sg.CFG_GENERIC_64x64x16 if ta else sg.CFG_DL_64x64x64)
+    assert cfg(1024, 1024, 1022) == (sg.CFG_DL_64x64x64 if (ta and not tb) else
+                                     sg.CFG_GENERIC_64x64x16)
+    assert cfg(1024, 1022, 1024) == sg.CFG_GENERIC_64x64x16          # C rows
+    p = sg.plan(4096, 4096, 4096, num_cus=256, occupancy=occ, trans_a=ta, trans_b=tb)
+    assert p["tiles_m"] == 16 and p["sched"] == sg.SCHED_DP
+
+
+@pytest.mark.parametrize("config", range(1, sg.NUM_CFGS))
+def test_transposed_storage_runs_only_on_layout_configs(config):
+    for ta, tb in [(1, 0), (0, 1), (1, 1)]:
+        if config in LAYOUT_CFGS:
+            p = sg.plan(512, 512, 512, config, num_cus=256, occupancy=OCC, trans_a=ta, trans_b=tb)
+            check_plan(p, 512, 512, 512)
+        else:
+            with pytest.raises(sg.SgemmError) as e:
+                sg.plan(512, 512, 512, config, num_cus=256, occupancy=OCC, trans_a=ta, trans_b=tb)
+            assert e.value.status == sg.ERR_CONFIG
+    with pytest.raises(sg.SgemmError) as e:
+        sg.plan(512, 512, 512, config, trans_a=2)
+    assert e.value.status == sg.ERR_CONFIG
+
+
 def test_xcd_grouping_for_the_headline_shape():
     """4096^3 on 256 CUs: each XCD's 32 consecutive tiles form a 4 x 8 block."""
     p = sg.plan(4096, 4096, 4096, num_cus=256, occupancy=OCC)
