@@ -2,15 +2,19 @@
 
 Prints ONE JSON line on stdout: FP32 SGEMM TFLOP/s (2*M*N*K / t) of the
 headline 4096^3 workload (or --workload), with inputs resident in HBM, K
-back-to-back calls timed between two device synchronisations, plus:
+back-to-back calls timed between two device synchronisations (after W
+untimed calls, continued to at least --warm-seconds so that the shader clock
+has ramped up), plus:
   * "roofline": per-launch kernel time from HIP events recorded on the
     launch stream, against the MI355X FP32 matrix peak (157.3 TFLOP/s);
   * "cpu_baseline": the FP64 CPU oracle timed on a bounded row sample of the
     same product, on this host's cores.
-Details (every workload with --all, cold-cache timings, the plan, a
-torch.matmul context figure) go to stderr and to --detail FILE.
+The line also carries the median single-call time with a 512 MiB buffer
+written before each call (caches flushed: "cold_median_event_tflops").
+Details (every workload with --all, the plan, a torch.matmul context figure)
+go to stderr and to --detail FILE.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--warm-seconds 0.5] [--workload NAME]
                        [--config N] [--sched N] [--all] [--no-cpu-baseline]
 """
 import argparse
@@ -40,8 +44,8 @@ PAGES_4096_TFLOPS = 49.8
 # the kernel sources they were taken on (digest below); otherwise reported null.
 TRAFFIC = {
     "kernel": "mfma_256x256x16", "workload": "sgemm_4096",
-    "source_digest": "366698cf35f68534",
-    "bytes": 469861879,
+    "source_digest": "778b6394e5c442d2",
+    "bytes": 469929457,
 }
 KERNEL_SOURCES = ("fp32_sgemm_f32_amd/csrc/gemm_mfma.hip", "fp32_sgemm_f32_amd/csrc/gemm_common.h")
 
@@ -64,11 +68,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warm-seconds", type=float, default=0.5,
+                    help="keep making untimed warm-up calls until this long has passed (clock ramp)")
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--config", type=int, default=0)
     ap.add_argument("--sched", type=int, default=0)
     ap.add_argument("--all", action="store_true", help="also time every workload (details only)")
-    ap.add_argument("--cold", action="store_true", help="also time with caches flushed before each call")
+    ap.add_argument("--cold", action="store_true", help="with --all: also time the other workloads with "
+                    "caches flushed before each call (the headline always is)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed timing of the headline")
     ap.add_argument("--torch", action="store_true", help="also time torch.matmul (context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -88,12 +96,46 @@ def ensure_library():
     return sg
 
 
-def time_calls(fn, stream, steps, warmup, flush=None):
-    """Per-call HIP-event times (ms) on `stream`, plus the total wall of the
-    back-to-back run between two synchronisations."""
+def warm_up(fn, calls, min_seconds):
+    """`calls` untimed calls, continued until at least min_seconds of them
+    have run: the shader clock ramps up over tens of milliseconds, longer
+    than a few calls of a small product take.  Returns the calls made."""
     import torch
-    for _ in range(warmup):
+    done = 0
+    t0 = time.perf_counter()
+    while done < calls or time.perf_counter() - t0 < min_seconds:
+        for _ in range(max(1, min(calls, 8))):
+            fn()
+            done += 1
+        torch.cuda.synchronize()
+    return done
+
+
+def time_region(fn, stream, steps, warmup, min_warm_s=0.0):
+    """The timed region: `steps` back-to-back calls between two device
+    synchronisations, with one HIP event pair recorded on `stream` around
+    them (nothing between the calls).  Returns (wall s, event ms, warm-up
+    calls made)."""
+    import torch
+    warm = warm_up(fn, warmup, min_warm_s)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
         fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(end), warm
+
+
+def time_calls(fn, stream, steps, warmup, flush=None, min_warm_s=0.0):
+    """Per-call HIP-event times (ms) on `stream` (an event pair around each
+    call: the distribution of single-call times), plus the total wall of the
+    run and the warm-up calls made."""
+    import torch
+    warm = warm_up(fn, warmup, min_warm_s)
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -107,7 +149,7 @@ def time_calls(fn, stream, steps, warmup, flush=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return per, wall
+    return per, wall, warm
 
 
 def bench_workload(sg, w, args, dev, stream, cold=False, with_torch=False):
@@ -137,15 +179,20 @@ def bench_workload(sg, w, args, dev, stream, cold=False, with_torch=False):
     del ref, scale, err
 
     with torch.cuda.stream(stream):
-        per, wall = time_calls(call, stream, args.steps, args.warmup)
+        wall, region_ms, warm = time_region(call, stream, args.steps, args.warmup, args.warm_seconds)
+        # Single-call distribution, in a second pass (the event pairs around
+        # each call put gaps between the kernels, so they stay out of the
+        # timed region).
+        per, _, _ = time_calls(call, stream, args.steps, 0)
     flops = w.flops
     res = {
         "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist, "seed": w.seed,
         "sane": sane,
-        "steps": args.steps, "warmup": args.warmup,
+        "steps": args.steps, "warmup": args.warmup, "warmup_calls": warm,
         "wall_s": wall,
         "ms_per_step": wall / args.steps * 1e3,
         "tflops": flops * args.steps / wall / 1e12,
+        "region_event_ms_per_call": region_ms / args.steps,
         "event_ms_median": statistics.median(per),
         "event_ms_mean": statistics.fmean(per),
         "event_ms_min": min(per),
@@ -157,8 +204,8 @@ def bench_workload(sg, w, args, dev, stream, cold=False, with_torch=False):
     if cold:
         flush_buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
         with torch.cuda.stream(stream):
-            per_c, _ = time_calls(call, stream, max(20, args.steps // 2), 3,
-                                  flush=lambda: flush_buf.fill_(1.0))
+            per_c, _, _ = time_calls(call, stream, max(20, args.steps // 2), 3,
+                                  flush=lambda: flush_buf.fill_(1.0), min_warm_s=args.warm_seconds)
         res["cold_event_ms_median"] = statistics.median(per_c)
         res["cold_tflops_median"] = flops / (statistics.median(per_c) * 1e-3) / 1e12
         del flush_buf
@@ -166,7 +213,8 @@ def bench_workload(sg, w, args, dev, stream, cold=False, with_torch=False):
         torch.backends.cuda.matmul.allow_tf32 = False
         out = torch.empty_like(Cd)
         with torch.cuda.stream(stream):
-            per_t, _ = time_calls(lambda: torch.matmul(Ad, Bd, out=out), stream, args.steps, args.warmup)
+            per_t, _, _ = time_calls(lambda: torch.matmul(Ad, Bd, out=out), stream, args.steps, args.warmup,
+                                  min_warm_s=args.warm_seconds)
         res["torch_matmul_event_ms_median"] = statistics.median(per_t)
         res["torch_matmul_tflops_median"] = flops / (statistics.median(per_t) * 1e-3) / 1e12
     del Ad, Bd, Cd
@@ -215,7 +263,7 @@ def main():
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         with torch.cuda.stream(stream):
-            per, wall = time_calls(lambda: dst.copy_(src), stream, args.steps, args.warmup)
+            per, wall, _ = time_calls(lambda: dst.copy_(src), stream, args.steps, args.warmup)
         t = statistics.median(per) * 1e-3
         print(json.dumps({"metric": "device copy GB/s (read + write)", "value": round(2 * n * 4 / t / 1e9, 1),
                           "unit": "GB/s", "bytes_read": n * 4, "bytes_written": n * 4,
@@ -223,7 +271,7 @@ def main():
         return
 
     w = workloads.WORKLOADS[args.workload]
-    head = bench_workload(sg, w, args, dev, stream, cold=args.cold, with_torch=args.torch)
+    head = bench_workload(sg, w, args, dev, stream, cold=not args.no_cold, with_torch=args.torch)
     log(json.dumps(head))
     detail = {"headline": head, "device": props.name, "cus": props.multi_processor_count}
     if args.all:
@@ -236,7 +284,7 @@ def main():
             rest.append(r)
         detail["others"] = rest
 
-    achieved = w.flops / (head["event_ms_mean"] * 1e-3) / 1e12
+    achieved = w.flops / (head["region_event_ms_per_call"] * 1e-3) / 1e12
     traffic = None
     if (TRAFFIC["kernel"] == sg.CFG_NAMES[head["plan"]["config"]] and TRAFFIC["workload"] == w.name
             and TRAFFIC["source_digest"] == kernel_source_digest()):
@@ -256,6 +304,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls": head["warmup_calls"],
         "ms_per_step": round(head["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -267,6 +316,8 @@ def main():
                    "grid": head["plan"]["grid"], "parallelism": "single-gpu"},
         "frac_of_fp32_peak": round(head["tflops"] / PEAK_FP32_TFLOPS, 4),
         "median_event_tflops": round(head["tflops_median"], 3),
+        "cold_median_event_tflops": (round(head["cold_tflops_median"], 3) if "cold_tflops_median" in head
+                                     else None),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sane": head["sane"],

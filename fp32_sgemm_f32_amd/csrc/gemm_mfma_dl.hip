@@ -37,9 +37,11 @@
 // one barrier, LA groups before its end: before it a wave waits until its
 // loads of chunk c+1 have landed (S-3 later chunks and the part of chunk
 // c+S-1 issued so far may stay in flight) and its LDS reads of chunk c are
-// done; after it the waves read chunk c+1.  The compiler does not order
-// these loads against LDS reads, so the waits and the barrier are explicit
-// (s_waitcnt vmcnt(N)).
+// done; after it the waves read chunk c+1.  A two-stage double buffer (loads
+// of chunk c+1 waited for within chunk c) measured 6-17% slower on MI355X:
+// one chunk of MFMAs does not cover the load latency.  The compiler does not
+// order these loads against LDS reads, so the waits and the barrier are
+// explicit (s_waitcnt vmcnt(N)).
 #include <utility>
 
 #include "gemm_common.h"
@@ -440,6 +442,9 @@ struct MfmaDlCore {
     // wave issues one such load every few dozen cycles; a burst would
     // stall its MFMAs).
     __device__ __forceinline__ static constexpr int dma_lo(int q) { return q * L / G; }
+    // Loads that may still be in flight at chunk c's barrier: S-3 whole
+    // chunks and what was issued of chunk c+S-1.
+    static constexpr int VM_AT_BARRIER = L * (S - 3) + dma_lo(G - LA);
 
     // Group Q of chunk c, in stage ST.  Stage ST+1 holds chunk c+1; stage
     // ST-1 (free since the barrier of chunk c-1) receives chunk c+S-1 over
@@ -471,7 +476,7 @@ struct MfmaDlCore {
             read_group<ST, TQ>(g, av[ts], bv[ts]);
         } else {
             if constexpr (TQ == G) {
-                if (SGEMM_DL_STEADY) wait_counts<L * (S - 3) + dma_lo(G - LA), 0>();
+                if (SGEMM_DL_STEADY) wait_counts<VM_AT_BARRIER, 0>();
                 else wait_counts<0, 0>();
                 lds_barrier();
             }

@@ -253,7 +253,7 @@ int run(const Call &c) {
     a.dp_tiles = p.dp_tiles; a.sk_tiles = p.sk_tiles;
     a.grid = p.grid; a.sk_grid = p.sk_grid;
     a.xcd_remap = env_int("SGEMM_F32_XCD_REMAP", 1) ? p.xcd_remap : 0;
-    a.group_m = p.group_m;
+    a.group_m = env_int("SGEMM_F32_GROUP_M", 0) > 0 ? env_int("SGEMM_F32_GROUP_M", 0) : p.group_m;
     a.sk_iters = p.sk_iters;
 
     if (p.sk_tiles > 0) {

@@ -46,6 +46,15 @@
  *   Calls that run concurrently on the SAME stream are impossible by stream
  *   order; calls from several host threads on one stream are serialised by
  *   the stream as well.
+ *
+ * Environment (read on every call; for tuning and measurement, not needed
+ * for correct results):
+ *   SGEMM_F32_SK_WG_PER_CU  split workgroups per compute unit in Stream-K
+ *                           schedules (default 1, capped by occupancy);
+ *   SGEMM_F32_XCD_REMAP     0 turns off the remapping of workgroup ids that
+ *                           gives each XCD a contiguous run of tiles;
+ *   SGEMM_F32_GROUP_M       tile rows per group of the tile order (default:
+ *                           chosen by the planner).
  */
 #ifndef SGEMM_F32_H
 #define SGEMM_F32_H
