@@ -457,7 +457,10 @@ struct MfmaDlCore {
     //     what the groups before issued of chunk c+S-1) and this wave's
     //     reads of chunk c are done, the waves may move on to chunk c+1.
     //   * The reads for group Q+LA (of this chunk or the next), then the
-    //     group's DMA instructions, then the other three MFMA steps.
+    //     other three MFMA steps with the group's DMA instructions spread
+    //     after them.  Issuing an LDS-DMA load holds the wave for a few dozen
+    //     cycles; behind the operand reads in one MFMA's shadow it delayed
+    //     the next dependent MFMA (3% at one wave per SIMD).
     template <int ST, int Q>
     __device__ __forceinline__ void group(Geo &g, int c, int nch, int tail_ch, AOps (&av)[NS], BOps (&bv)[NS]) {
         // Whether this chunk still loads (c <= nch - S), as a scalar register:
@@ -482,19 +485,40 @@ struct MfmaDlCore {
             }
             read_group<NXT, TQ - G>(g, av[ts], bv[ts]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(av[cs], bv[cs], 1);
+        __builtin_amdgcn_sched_barrier(0);
         if (SGEMM_DL_STEADY) {
             if constexpr (EDGE && Q == 0) {
                 if (scalar_eq(c + S - 1, tail_ch)) mask_k_tail(g);
             }
-#pragma unroll
-            for (int d = dma_lo(Q); d < dma_lo(Q + 1); ++d) issue_one<PRV>(g, d);
+            dma_slot<PRV, Q, 0>(g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(av[cs], bv[cs], 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (dma_lo(Q + 1) - dma_lo(Q) > 1) {
+            if (SGEMM_DL_STEADY) dma_slot<PRV, Q, 1>(g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(av[cs], bv[cs], 3);
+        __builtin_amdgcn_sched_barrier(0);
+        if (SGEMM_DL_STEADY) {
+            if constexpr (dma_lo(Q + 1) - dma_lo(Q) > 2) dma_slot<PRV, Q, 2>(g);
             if constexpr (Q == G - 1) advance(g);
         }
 #undef SGEMM_DL_STEADY
         __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // The group's DMA instructions d with (d - dma_lo(Q)) % 3 == SLOT: each
+    // slot follows its own MFMA step, so that no step waits behind more
+    // than a third of the group's loads.
+    template <int PRV, int Q, int SLOT>
+    __device__ __forceinline__ static void dma_slot(const Geo &g) {
 #pragma unroll
-        for (int u = 1; u < 4; ++u) mfma_step(av[cs], bv[cs], u);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int d = dma_lo(Q); d < dma_lo(Q + 1); ++d)
+            if ((d - dma_lo(Q)) % 3 == SLOT) issue_one<PRV>(g, d);
     }
 
     template <int ST, int... Qs>
