@@ -506,3 +506,31 @@ def test_workload_full_size(dev, name):
     worst = float(np.max(np.abs(Cs - C_ref) / S))
     log(f"  {name}: {len(r)} sampled elements, max|err|/S = {worst:.3e}")
     assert ok
+
+
+@pytest.mark.parametrize("layout", LAYOUTS[1:], ids=lambda l: f"ta{l[0]}tb{l[1]}")
+@pytest.mark.parametrize("name", ["sgemm_4096", "sgemm_2048", "sgemm_1024x1024x16384"])
+def test_workload_full_size_storage_orders(dev, name, layout):
+    """The measured workloads with A stored K x M and / or B stored N x K, at
+    full size, in the automatic choice (the direct-to-LDS kernels)."""
+    import torch
+    ta, tb = layout
+    w = workloads.WORKLOADS[name]
+    log(f"case workload {name} ta={ta} tb={tb}")
+    A, B = workloads.generate_workload(w)
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    sg.gemm(to_dev(stored(A, ta), dev), to_dev(stored(B, tb), dev), C, 1.0, 0.0, ta, tb)
+    torch.cuda.synchronize()
+    C = C.cpu().numpy()
+    assert np.all(np.isfinite(C))
+    rng = np.random.default_rng(w.seed + 10 * ta + 20 * tb)
+    rows_full = rng.choice(w.M, 2, replace=False)
+    cols_full = rng.choice(w.N, 2, replace=False)
+    r = [np.repeat(rows_full, w.N), np.tile(np.arange(w.M), 2), rng.integers(0, w.M, 20000)]
+    c = [np.tile(np.arange(w.N), 2), np.repeat(cols_full, w.M), rng.integers(0, w.N, 20000)]
+    r, c = np.concatenate(r), np.concatenate(c)
+    C_ref, S = oracle.gemm_points(A, B, r, c)
+    Cs = C[r, c].astype(np.float64)
+    worst = float(np.max(np.abs(Cs - C_ref) / S))
+    log(f"  {name} ta={ta} tb={tb}: {len(r)} sampled elements, max|err|/S = {worst:.3e}")
+    assert np.all(np.abs(Cs - C_ref) <= TOL * S)
