@@ -40,14 +40,14 @@ PAGES_4096_TFLOPS = 49.8
 # HBM-side bytes per launch of the headline kernel, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by what the
 # same counter reads for a plain 256 MiB device copy (FETCH_SIZE 2.0, WRITE_SIZE
-# 1.0); see profiles/sgemm_4096_mfma_256x256x16_counters.md.  Valid only for
-# the kernel sources they were taken on (digest below); otherwise reported null.
+# 1.0); see profiles/sgemm_4096_dl_256x256x16_counters.md.  Valid only for the
+# kernel sources they were taken on (digest below); otherwise reported null.
 TRAFFIC = {
-    "kernel": "mfma_256x256x16", "workload": "sgemm_4096",
-    "source_digest": "778b6394e5c442d2",
-    "bytes": 469929457,
+    "kernel": "dl_256x256x16", "workload": "sgemm_4096",
+    "source_digest": "01e3954aa68fcffa",
+    "bytes": 469864950,
 }
-KERNEL_SOURCES = ("fp32_sgemm_f32_amd/csrc/gemm_mfma.hip", "fp32_sgemm_f32_amd/csrc/gemm_common.h")
+KERNEL_SOURCES = ("fp32_sgemm_f32_amd/csrc/gemm_mfma_dl.hip", "fp32_sgemm_f32_amd/csrc/gemm_common.h")
 
 
 def kernel_source_digest() -> str:

@@ -703,7 +703,7 @@ using Dl256x128x16 = MfmaDlCore<256, 128, 16, 2, 2, 3>;
     using name##TT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, true, true>;
 SGEMM_DL_EDGE_CORES(Dl64x64x32, 64, 64, 32, 2, 2, 4, 1, 2)
 SGEMM_DL_EDGE_CORES(Dl64x64x64, 64, 64, 64, 2, 2, 3, 1, 2)
-SGEMM_DL_EDGE_CORES(Dl128x128x32K2, 128, 128, 32, 2, 2, 3, 2, 1)
+SGEMM_DL_EDGE_CORES(Dl128x128x32, 128, 128, 32, 2, 2, 3, 1, 2)
 SGEMM_DL_EDGE_CORES(Dl256x256x16, 256, 256, 16, 4, 2, 3, 1, 1)
 #undef SGEMM_DL_EDGE_CORES
 
@@ -736,7 +736,7 @@ static hipError_t occ(int *n) {
 #define SGEMM_DL_EDGE_CONFIGS(X)                  \
     X(SGEMM_CFG_DL_64x64x32, Dl64x64x32)          \
     X(SGEMM_CFG_DL_64x64x64, Dl64x64x64)          \
-    X(SGEMM_CFG_DL_128x128x32_K2, Dl128x128x32K2) \
+    X(SGEMM_CFG_DL_128x128x32, Dl128x128x32)     \
     X(SGEMM_CFG_DL_256x256x16, Dl256x256x16)
 
 hipError_t launch_mfma_dl(int cfg, const KernelArgs &a, hipStream_t s) {

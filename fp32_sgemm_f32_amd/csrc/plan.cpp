@@ -30,10 +30,10 @@ const CfgInfo kCfgs[] = {
     {SGEMM_CFG_MFMA_64x64x128, 64, 64, 128, 256, kKindMfma, 1, false, false, "mfma_64x64x128"},
     {SGEMM_CFG_DL_64x64x32, 64, 64, 32, 256, kKindMfmaDl, 2, true, true, "dl_64x64x32"},
     {SGEMM_CFG_DL_64x64x64_K2, 64, 64, 64, 512, kKindMfmaDl, 1, false, false, "dl_64x64x64_k2"},
-    {SGEMM_CFG_DL_128x128x32, 128, 128, 32, 256, kKindMfmaDl, 1, false, false, "dl_128x128x32"},
+    {SGEMM_CFG_DL_128x128x32, 128, 128, 32, 256, kKindMfmaDl, 1, true, true, "dl_128x128x32"},
     {SGEMM_CFG_DL_256x256x16, 256, 256, 16, 512, kKindMfmaDl, 1, true, true, "dl_256x256x16"},
     {SGEMM_CFG_DL_64x64x32_K2, 64, 64, 32, 512, kKindMfmaDl, 2, false, false, "dl_64x64x32_k2"},
-    {SGEMM_CFG_DL_128x128x32_K2, 128, 128, 32, 512, kKindMfmaDl, 1, true, true, "dl_128x128x32_k2"},
+    {SGEMM_CFG_DL_128x128x32_K2, 128, 128, 32, 512, kKindMfmaDl, 1, false, false, "dl_128x128x32_k2"},
     {SGEMM_CFG_DL_64x64x64, 64, 64, 64, 256, kKindMfmaDl, 1, true, true, "dl_64x64x64"},
     {SGEMM_CFG_DL_128x256x16, 128, 256, 16, 256, kKindMfmaDl, 2, false, false, "dl_128x256x16"},
     {SGEMM_CFG_DL_256x128x16, 256, 128, 16, 256, kKindMfmaDl, 2, false, false, "dl_256x128x16"},
@@ -85,21 +85,24 @@ static int64_t tiles_of(int cfg, int M, int N) {
     return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
-// Automatic choice, from timings of the configurations on MI355X (256 CUs):
+// Automatic choice, from timings of the configurations on MI355X (256 CUs;
+// all direct-to-LDS, every storage order):
 //   * 256x256x16 tiles (8 waves) when every CU gets at least one (149
-//     TFLOP/s at 4096^3), the register-staged kernel when the tile divides
-//     the shape and A and B are stored M x K and K x N;
-//   * else 128x128 tiles loaded straight into LDS, two K groups of waves,
-//     when every CU gets one (138 at 2048^3);
-//   * else 64x64 tiles loaded straight into LDS (142 at 1024x1024x16384,
-//     99 at 1024^3), with a 64-deep K chunk where K allows.
+//     TFLOP/s at 4096^3, 142 at 6144^3; the register-staged kernel of the
+//     same tile measured 0-5% slower);
+//   * else 128x128x32 tiles when they fill whole waves (140 at 2048^3,
+//     143 at 2048x4096x2048);
+//   * else 64x64 tiles (146 at 1024x1024x16384, 106 at 1024^3, 141 at
+//     3072^3, where 128x128 tiles leave a part wave: 137), with a 64-deep
+//     K chunk where K allows.
 // Layouts the vector kernels cannot load go to the general kernel.
-static int auto_config(int M, int N, int K, int cus, bool aligned, bool transposed) {
+static int auto_config(int M, int N, int K, int cus, bool aligned) {
     if (!aligned) return SGEMM_CFG_GENERIC_64x64x16;
-    const int big = SGEMM_CFG_MFMA_256x256x16, big_edge = SGEMM_CFG_DL_256x256x16,
-              mid = SGEMM_CFG_DL_128x128x32_K2, small = SGEMM_CFG_DL_64x64x64, small32 = SGEMM_CFG_DL_64x64x32;
-    if (tiles_of(big, M, N) >= cus) return !transposed && divides(kCfgs[big], M, N, K) ? big : big_edge;
-    if (tiles_of(mid, M, N) >= cus) return mid;
+    const int big = SGEMM_CFG_DL_256x256x16, mid = SGEMM_CFG_DL_128x128x32, small = SGEMM_CFG_DL_64x64x64,
+              small32 = SGEMM_CFG_DL_64x64x32;
+    if (tiles_of(big, M, N) >= cus) return big;
+    const int64_t mid_tiles = tiles_of(mid, M, N);
+    if (mid_tiles >= cus && mid_tiles % cus == 0) return mid;
     if (K % 64 == 0 || K % 32 != 0) return small;
     return small32;
 }
@@ -136,7 +139,7 @@ int make_plan(const PlanRequest &req, Plan *out) {
 
     int cfg = req.config;
     const bool aligned = req.aligned != 0, transposed = req.trans_a || req.trans_b;
-    if (cfg == SGEMM_CFG_AUTO) cfg = auto_config(M, N, K, cus, aligned, transposed);
+    if (cfg == SGEMM_CFG_AUTO) cfg = auto_config(M, N, K, cus, aligned);
     const CfgInfo &c = kCfgs[cfg];
     if (!fits(c, M, N, K, aligned, transposed)) return SGEMM_ERR_CONFIG;
 

@@ -46,7 +46,7 @@ def gpu_matmul(A, B, dev, config=sg.CFG_AUTO, sched=sg.SCHED_AUTO):
 
 # Configurations that run shapes their tile does not divide (the vector ones
 # when N and K are multiples of 4; the general one always).
-EDGE_CFGS = [sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_DL_256x256x16,
+EDGE_CFGS = [sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32, sg.CFG_DL_256x256x16,
              sg.CFG_GENERIC_64x64x16]
 
 
@@ -261,7 +261,7 @@ def test_blas_form(dev, layout, scaling, shape):
 # and N, to be multiples of 4.  Shapes: tile multiples, ragged in every
 # dimension, K not a multiple of 4 (only A K x M with B K x N qualifies), M
 # not a multiple of 4 (only A stored M x K qualifies).
-DL_LAYOUT_CFGS = [sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_DL_256x256x16]
+DL_LAYOUT_CFGS = [sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32, sg.CFG_DL_256x256x16]
 LAYOUT_SHAPES = [(512, 512, 512), (260, 196, 100), (516, 388, 772), (132, 68, 1004), (64, 1028, 36),
                  (130, 196, 100), (128, 196, 102)]
 

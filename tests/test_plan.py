@@ -14,7 +14,7 @@ import pytest
 import fp32_sgemm_f32_amd as sg
 
 OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1, 2, 1, 1, 1, 2, 1, 1, 2, 2, 2]
-EDGE_CFGS = {sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_DL_256x256x16,
+EDGE_CFGS = {sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32, sg.CFG_DL_256x256x16,
              sg.CFG_GENERIC_64x64x16}
 
 
@@ -182,9 +182,16 @@ def test_full_waves_first_then_split():
 def test_auto_choices_on_256_cus():
     occ = OCC
     p = sg.plan(4096, 4096, 4096, num_cus=256, occupancy=occ)
-    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_MFMA_256x256x16, sg.SCHED_DP, 256)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_DL_256x256x16, sg.SCHED_DP, 256)
+    p = sg.plan(6144, 6144, 6144, num_cus=256, occupancy=occ)
+    assert p["config"] == sg.CFG_DL_256x256x16
     p = sg.plan(2048, 2048, 2048, num_cus=256, occupancy=occ)
-    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_DL_128x128x32_K2, sg.SCHED_DP, 256)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_DL_128x128x32, sg.SCHED_DP, 256)
+    p = sg.plan(2048, 4096, 2048, num_cus=256, occupancy=occ)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_DL_128x128x32, sg.SCHED_DP, 512)
+    # 128 x 128 tiles that leave a part wave (576 at 3072^3): 64 x 64 tiles.
+    p = sg.plan(3072, 3072, 3072, num_cus=256, occupancy=occ)
+    assert p["config"] == sg.CFG_DL_64x64x64
     p = sg.plan(1024, 1024, 1024, num_cus=256, occupancy=occ)
     assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_DL_64x64x64, sg.SCHED_DP, 256)
     p = sg.plan(1024, 1024, 16384, num_cus=256, occupancy=occ)
@@ -198,7 +205,7 @@ def test_auto_choices_on_256_cus():
     p = sg.plan(4000, 4000, 4000, num_cus=256, occupancy=occ)
     assert (p["config"], p["tiles_m"], p["iters_per_tile"]) == (sg.CFG_DL_256x256x16, 16, 250)
     p = sg.plan(2000, 2000, 2000, num_cus=256, occupancy=occ)
-    assert p["config"] == sg.CFG_DL_128x128x32_K2
+    assert p["config"] == sg.CFG_DL_128x128x32
     p = sg.plan(1000, 1000, 1000, num_cus=256, occupancy=occ)
     assert p["config"] == sg.CFG_DL_64x64x64
     p = sg.plan(1000, 1001, 1000, num_cus=256, occupancy=occ)
@@ -213,9 +220,9 @@ LAYOUT_CFGS = EDGE_CFGS
 
 @pytest.mark.parametrize("layout", [(1, 0), (0, 1), (1, 1)], ids=["TN", "NT", "TT"])
 def test_auto_choices_for_transposed_storage(layout):
-    """The same regimes as A M x K, B K x N, on the edge-masking kernels
-    (the register-staged 256 x 256 one loads only that order), and the
-    general kernel when a stored row length is not a multiple of 4."""
+    """The same choices as for A M x K, B K x N (the direct-to-LDS kernels
+    load every storage order), and the general kernel when a stored row
+    length is not a multiple of 4."""
     ta, tb = layout
     occ = OCC
 
@@ -223,7 +230,7 @@ def test_auto_choices_for_transposed_storage(layout):
         return sg.plan(M, N, K, num_cus=256, occupancy=occ, trans_a=ta, trans_b=tb)["config"]
 
     assert cfg(4096, 4096, 4096) == sg.CFG_DL_256x256x16
-    assert cfg(2048, 2048, 2048) == sg.CFG_DL_128x128x32_K2
+    assert cfg(2048, 2048, 2048) == sg.CFG_DL_128x128x32
     assert cfg(1024, 1024, 1024) == sg.CFG_DL_64x64x64
     assert cfg(1024, 1024, 16384) == sg.CFG_DL_64x64x64
     assert cfg(1024, 1024, 96) == sg.CFG_DL_64x64x32
