@@ -446,6 +446,14 @@ struct MfmaDlCore {
     // chunks and what was issued of chunk c+S-1.
     static constexpr int VM_AT_BARRIER = L * (S - 3) + dma_lo(G - LA);
 
+    // 1 while chunk c still loads (c <= nch - S), else 0, in a scalar
+    // register; volatile, so that each test gets its own.
+    __device__ __forceinline__ static int steady_now(int c, int nch) {
+        int r;
+        asm volatile("s_cmp_le_i32 %1, %2\n\ts_cselect_b32 %0, 1, 0" : "=s"(r) : "s"(c), "s"(nch - S) : "scc");
+        return r;
+    }
+
     // Group Q of chunk c, in stage ST.  Stage ST+1 holds chunk c+1; stage
     // ST-1 (free since the barrier of chunk c-1) receives chunk c+S-1 over
     // the course of the chunk (STEADY only: the last S-1 chunks load
@@ -463,12 +471,11 @@ struct MfmaDlCore {
     //     the next dependent MFMA (3% at one wave per SIMD).
     template <int ST, int Q>
     __device__ __forceinline__ void group(Geo &g, int c, int nch, int tail_ch, AOps (&av)[NS], BOps (&bv)[NS]) {
-        // Whether this chunk still loads (c <= nch - S), as a scalar register:
-        // a boolean carried across blocks would be kept in a vector register,
-        // and set and tested with vector ALU instructions.
-        int steady_s;
-        asm("s_cmp_le_i32 %1, %2\n\ts_cselect_b32 %0, 1, 0" : "=s"(steady_s) : "s"(c), "s"(nch - S) : "scc");
-#define SGEMM_DL_STEADY (steady_s != 0)
+        // Whether this chunk still loads (c <= nch - S), computed afresh in a
+        // scalar register at every test: one boolean shared by the group's
+        // several tests would be carried across blocks in a vector register,
+        // set and tested with vector ALU instructions.
+#define SGEMM_DL_STEADY (steady_now(c, nch) != 0)
         constexpr int cs = Q % NS, TQ = Q + LA, ts = TQ % NS;
         constexpr int NXT = (ST + 1) % S, PRV = (ST + S - 1) % S;
         wait_counts<63, (LA - 1) * R>();
