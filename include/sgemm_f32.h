@@ -1,11 +1,13 @@
 /*
- * sgemm_f32: single-precision GEMM C = A * B for AMD Instinct MI355X (gfx950).
+ * sgemm_f32: single-precision GEMM for AMD Instinct MI355X (gfx950):
+ * C = A * B (sgemm_f32) and C = alpha * op(A) * op(B) + beta * C
+ * (sgemm_f32_gemm).
  *
  * The operation (page "Beyond Kernel 7: Closing the Gap to cuBLAS on an H100
  * FP32 GEMM", section "The operation: GEMM and the precision of the
  * comparison"): for row-major FP32 matrices A (M x K) and B (K x N),
  *
- *     C[m][n] = sum over k of A[m][k] * B[k][n]        (AB only: no alpha/beta)
+ *     C[m][n] = sum over k of A[m][k] * B[k][n]
  *
  * with FP32 inputs and FP32 arithmetic throughout (fused multiply-adds, one
  * rounding each; no reduced-precision input rounding of any kind).  Any
@@ -16,10 +18,11 @@
  * beyond the matrix read as zero, results beyond it are not written.
  *
  * Fast and general layouts
- *   When N and K are multiples of 4, lda, ldb and ldc are multiples of 4
- *   and A, B, C are 16-byte aligned, the 16-byte vector kernels run (tile
- *   edges masked where the shape is not a multiple of the tile).  Any other
- *   layout runs on a general kernel with element-wise bounds checks.
+ *   When the stored row lengths of A and B (K and N for sgemm_f32) and N
+ *   are multiples of 4, lda, ldb and ldc are multiples of 4 and A, B, C are
+ *   16-byte aligned, the 16-byte vector kernels run (tile edges masked
+ *   where the shape is not a multiple of the tile).  Any other layout runs
+ *   on a general kernel with element-wise bounds checks.
  *
  * Memory and ownership
  *   A, B, C are device pointers, caller-owned, allocated on the HIP device
@@ -27,7 +30,7 @@
  *   them.  Layout is row-major with leading dimensions:
  *       A[m * lda + k],  B[k * ldb + n],  C[m * ldc + n].
  *   Only the logical M x N region of C is written; the ldc padding is left
- *   untouched.  C is overwritten, never read.  C must not overlap A or B.
+ *   untouched.  sgemm_f32 overwrites C without reading it (sgemm_f32_gemm reads it when beta != 0).  C must not overlap A or B.
  *
  * Asynchrony
  *   Every call only enqueues work on `stream` (0 = the null stream) and
@@ -97,7 +100,12 @@ extern "C" {
 #define SGEMM_CFG_MFMA_64x64x128    12 /* 256 threads, 4 waves of 32x32 */
 /* Tiles loaded straight from global memory into LDS (no register staging),
  * with a ring of LDS stages; _k2: two groups of waves split each chunk's K
- * range (two waves per SIMD with one tile per CU). */
+ * range (two waves per SIMD with one tile per CU).  DL_64x64x32,
+ * DL_64x64x64, DL_128x128x32 and DL_256x256x16 also run shapes their tile
+ * does not divide and A / B in either storage order (sgemm_f32_gemm), when
+ * the stored row lengths of A and B, N and every leading dimension are
+ * multiples of 4 and A, B, C are 16-byte aligned; the automatic choice
+ * (SGEMM_CFG_AUTO) uses only these four and the general kernel. */
 #define SGEMM_CFG_DL_64x64x32       13 /* 256 threads, 4 waves of 32x32, 4 stages */
 #define SGEMM_CFG_DL_64x64x64_K2    14 /* 512 threads, 2 x 4 waves of 32x32, 3 stages */
 #define SGEMM_CFG_DL_128x128x32     15 /* 256 threads, 4 waves of 64x64, 3 stages */
@@ -111,11 +119,9 @@ extern "C" {
  * (4-byte) alignment. */
 #define SGEMM_CFG_GENERIC_64x64x16  22 /* 256 threads, 4 waves of 32x32 */
 #define SGEMM_NUM_CFGS              23 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
-/* Configurations that run shapes which are not multiples of their tile
- * (vector layout): DL_64x64x32, DL_64x64x64, DL_128x128x32_K2,
- * DL_256x256x16, and GENERIC_64x64x16 (any layout).  The others need the
- * vector layout and a shape their tile divides.  Transposed operands
- * (sgemm_f32_gemm): GENERIC_64x64x16. */
+/* The configurations not named above as running other shapes or storage
+ * orders need A stored M x K, B stored K x N, the vector layout and a shape
+ * their tile divides. */
 
 /* Schedules. */
 #define SGEMM_SCHED_AUTO     0  /* whole tiles in full waves, Stream-K for the rest */
