@@ -30,7 +30,8 @@
  *   them.  Layout is row-major with leading dimensions:
  *       A[m * lda + k],  B[k * ldb + n],  C[m * ldc + n].
  *   Only the logical M x N region of C is written; the ldc padding is left
- *   untouched.  sgemm_f32 overwrites C without reading it (sgemm_f32_gemm reads it when beta != 0).  C must not overlap A or B.
+ *   untouched.  sgemm_f32 overwrites C without reading it (sgemm_f32_gemm
+ *   reads it when beta != 0).  C must not overlap A or B.
  *
  * Asynchrony
  *   Every call only enqueues work on `stream` (0 = the null stream) and
