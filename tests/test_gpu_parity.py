@@ -534,3 +534,49 @@ def test_workload_full_size_storage_orders(dev, name, layout):
     worst = float(np.max(np.abs(Cs - C_ref) / S))
     log(f"  {name} ta={ta} tb={tb}: {len(r)} sampled elements, max|err|/S = {worst:.3e}")
     assert np.all(np.abs(Cs - C_ref) <= TOL * S)
+
+
+# Leading dimensions just beyond the reach of the direct-to-LDS kernels'
+# 32-bit source offsets (BM or BK rows of A, BK or BN rows of B, times the
+# leading dimension, under 2^32 bytes; 2^31 for the edge-masking ones): the
+# automatic choice falls back (register-staged kernel for whole tiles, the
+# general kernel otherwise) and a forced direct-to-LDS configuration is
+# refused.  Buffers of 2-4 GiB.
+LD_CASES = {
+    # name: (trans_a, trans_b, M, N, K, lda, ldb)
+    "nn_lda": (0, 0, 64, 128, 64, 2 ** 24 + 4, 128),
+    "nn_ldb": (0, 0, 128, 64, 64, 64, 2 ** 24 + 4),
+    "tn_lda": (1, 0, 128, 128, 64, 2 ** 23 + 4, 128),
+    "nt_ldb": (0, 1, 128, 64, 64, 64, 2 ** 23 + 4),
+}
+
+
+@pytest.mark.parametrize("case", list(LD_CASES))
+def test_leading_dimensions_beyond_32bit_offsets(dev, case):
+    import torch
+    ta, tb, M, N, K, lda, ldb = LD_CASES[case]
+    log(f"case large ld {case}: ta={ta} tb={tb} shape=({M},{N},{K}) lda={lda} ldb={ldb}")
+    A, B = workloads.generate(M, N, K, "int4", 90)
+    As, Bs = stored(A, ta), stored(B, tb)
+
+    def padded(X, ld):
+        rows, cols = X.shape
+        buf = torch.zeros((rows - 1) * ld + cols, dtype=torch.float32, device=dev)
+        view = torch.as_strided(buf, (rows, cols), (ld, 1))
+        view.copy_(to_dev(X, dev))
+        return buf, view
+
+    Abuf, Av = padded(As, lda)
+    Bbuf, Bv = padded(Bs, ldb)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    with pytest.raises(sg.SgemmError) as e:
+        sg.gemm(Av, Bv, C, 1.0, 0.0, ta, tb, config=sg.CFG_DL_64x64x64)
+    assert e.value.status == sg.ERR_CONFIG
+    for sched in (sg.SCHED_DP, sg.SCHED_STREAMK):
+        C.fill_(float("nan"))
+        sg.gemm(Av, Bv, C, 1.0, 0.0, ta, tb, sched=sched)
+        torch.cuda.synchronize()
+        C_ref, _ = oracle.gemm_blas(As, Bs, None, 1.0, 0.0, ta, tb)
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref)   # integers: exact
+    del Abuf, Bbuf, Av, Bv
+    torch.cuda.empty_cache()
