@@ -31,6 +31,7 @@
 // step).  B always uses the interleaved column order (a k-contiguous B gets
 // it by loading its rows permuted), so the epilogue writes FN adjacent
 // floats per store.
+//
 // Synchronisation of the ring (chunk c in stage c % S, S >= 3): chunks
 // 0 .. S-2 are loaded up front; during chunk c the loads of chunk c+S-1 go
 // out, spread over its groups, into the stage of chunk c-1.  Each chunk has
