@@ -580,3 +580,65 @@ def test_leading_dimensions_beyond_32bit_offsets(dev, case):
         assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref)   # integers: exact
     del Abuf, Bbuf, Av, Bv
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Seeded random cases across the whole interface: shape, storage orders,
+# alpha / beta, padded leading dimensions, float-offset pointers, forced
+# configuration and schedule.  A forced configuration may refuse
+# (SGEMM_ERR_CONFIG) only if it is neither the automatic choice nor the
+# general kernel; every result is checked element by element against the
+# FP64 oracle, and C's padding must stay untouched.
+# ---------------------------------------------------------------------------
+
+def random_case(rng):
+    def dim():
+        r = rng.random()
+        if r < 0.3:
+            return int(rng.integers(1, 40))
+        if r < 0.6:
+            return int(rng.choice([64, 128, 192, 256, 384, 512]))
+        return int(rng.integers(40, 600))
+    M, N, K = dim(), dim(), dim()
+    ta, tb = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+    alpha, beta = [(1.0, 0.0), (1.0, 0.0), (-0.5, 0.0), (1.5, 2.0), (0.0, -1.0), (2.0, 1.0)][int(rng.integers(0, 6))]
+    pads = [int(rng.choice([0, 0, 0, 4, 1, 3])) for _ in range(3)]
+    offs = [int(rng.choice([0, 0, 0, 0, 1, 2])) for _ in range(3)]
+    config = int(rng.choice([sg.CFG_AUTO] * 4 + list(range(1, sg.NUM_CFGS))))
+    sched = int(rng.choice(SCHEDS))
+    return M, N, K, ta, tb, alpha, beta, pads, offs, config, sched
+
+
+@pytest.mark.parametrize("seed", range(160))
+def test_random_interface_cases(dev, seed):
+    import torch
+    rng = np.random.default_rng(7000 + seed)
+    M, N, K, ta, tb, alpha, beta, pads, offs, config, sched = random_case(rng)
+    log(f"case random seed={seed}: shape=({M},{N},{K}) ta={ta} tb={tb} alpha={alpha} beta={beta} "
+        f"pads={pads} offs={offs} config={sg.CFG_NAMES[config]} sched={sg.SCHED_NAMES[sched]}")
+    A, B = workloads.generate(M, N, K, "normal", 8000 + seed)
+    As, Bs = stored(A, ta), stored(B, tb)
+    C0 = c0_of(M, N, 8100 + seed)
+
+    def placed(X, pad, off):
+        rows, cols = X.shape
+        ld = cols + pad
+        buf = torch.full((rows * ld + off + 4,), float("nan"), dtype=torch.float32, device=dev)
+        view = torch.as_strided(buf, (rows, cols), (ld, 1), off)
+        view.copy_(to_dev(X, dev))
+        return buf, view, ld
+
+    _, Av, _ = placed(As, pads[0], offs[0])
+    _, Bv, _ = placed(Bs, pads[1], offs[1])
+    Cbuf, Cv, ldc = placed(C0, pads[2], offs[2])
+    try:
+        sg.gemm(Av, Bv, Cv, alpha, beta, ta, tb, config=config, sched=sched)
+    except sg.SgemmError as e:
+        assert e.status == sg.ERR_CONFIG and config not in (sg.CFG_AUTO, sg.CFG_GENERIC_64x64x16), e
+        assert np.array_equal(Cv.cpu().numpy(), C0), "C changed on an error"
+        return
+    torch.cuda.synchronize()
+    C_ref, S = oracle.gemm_blas(As, Bs, C0, alpha, beta, ta, tb)
+    check(Cv.cpu().numpy(), C_ref, S, f"random {seed}")
+    full = torch.as_strided(Cbuf, (M, ldc), (ldc, 1), offs[2]).cpu().numpy()
+    assert np.all(np.isnan(full[:, N:])), "ldc padding was written"
