@@ -51,6 +51,14 @@
  *   order; calls from several host threads on one stream are serialised by
  *   the stream as well.
  *
+ * Graph capture
+ *   A call only enqueues kernels (no memset, no copy), so it can be captured
+ *   into a HIP graph, provided it allocates nothing during capture: make one
+ *   eager call with the same stream and a shape at least as large first (the
+ *   Stream-K workspace is then in place; shapes that run whole tiles need
+ *   none).  Replays reuse the workspace of the capturing stream, so replays
+ *   of graphs captured on one stream must not run concurrently.
+ *
  * Environment (read on every call; for tuning and measurement, not needed
  * for correct results):
  *   SGEMM_F32_SK_WG_PER_CU  split workgroups per compute unit in Stream-K

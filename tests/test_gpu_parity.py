@@ -424,6 +424,67 @@ def test_non_default_stream(dev):
     check(C.cpu().numpy(), C_ref, S, "side stream")
 
 
+def test_concurrent_streams_with_split_tiles(dev):
+    """Stream-K calls on two streams with no host synchronisation between
+    them: each stream has its own workspace, so the partial tiles and
+    arrival counters of one never meet the other's (integer inputs: every
+    result exact, every repeat identical)."""
+    import torch
+    log("case two streams, Stream-K")
+    shapes = [(512, 512, 4096), (384, 640, 2048)]
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    data = []
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = workloads.generate(M, N, K, "int4", 95 + i)
+        data.append((A, B, to_dev(A, dev), to_dev(B, dev)))
+    torch.cuda.synchronize()
+    outs = [[], []]
+    for rep in range(4):
+        for i, s in enumerate(streams):
+            _, _, Ad, Bd = data[i]
+            with torch.cuda.stream(s):
+                outs[i].append(sg.matmul(Ad, Bd, sched=sg.SCHED_STREAMK))
+    torch.cuda.synchronize()
+    for i in range(2):
+        A, B, _, _ = data[i]
+        C_ref, _ = oracle.gemm(A, B)
+        for C in outs[i]:
+            assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref)
+
+
+@pytest.mark.parametrize("sched", [sg.SCHED_DP, sg.SCHED_STREAMK], ids=lambda s: sg.SCHED_NAMES[s])
+def test_graph_capture_and_replay(dev, sched):
+    """Calls captured into a HIP graph (after one eager call has set up the
+    Stream-K workspace) replay correctly: new inputs are written between the
+    replays, with eager work and synchronisations in between, and every
+    replay matches the oracle and the eager result exactly (integer inputs)."""
+    import torch
+    M, N, K = 768, 512, 1024
+    log(f"case graph capture sched={sg.SCHED_NAMES[sched]}")
+    s = torch.cuda.Stream(device=dev)
+    A0, B = workloads.generate(M, N, K, "int4", 96)
+    Ad, Bd = to_dev(A0, dev), to_dev(B, dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    with torch.cuda.stream(s):
+        sg.gemm(Ad, Bd, C, 1.0, 0.0, sched=sched)          # eager: workspace ready
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        sg.gemm(Ad, Bd, C, 1.0, 0.0, sched=sched)
+    torch.cuda.synchronize()
+    for r in range(3):
+        A_r = workloads.generate(M, N, K, "int4", 200 + r)[0]
+        Ad.copy_(to_dev(A_r, dev))
+        E = sg.matmul(Ad, Bd, sched=sched)                 # eager reference on the device
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        C_ref, _ = oracle.gemm(A_r, B)
+        got = C.cpu().numpy()
+        assert np.array_equal(got.astype(np.float64), C_ref), f"replay {r}"
+        assert np.array_equal(got, E.cpu().numpy()), f"replay {r} vs eager"
+
+
 def test_rejects_bad_memory_and_leaves_c_untouched(dev):
     import ctypes
 
