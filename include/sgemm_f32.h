@@ -56,8 +56,12 @@
  *   into a HIP graph, provided it allocates nothing during capture: make one
  *   eager call with the same stream and a shape at least as large first (the
  *   Stream-K workspace is then in place; shapes that run whole tiles need
- *   none).  Replays reuse the workspace of the capturing stream, so replays
- *   of graphs captured on one stream must not run concurrently.
+ *   none).  Replays use the workspace the capturing stream had at capture
+ *   time: replays of graphs captured on one stream must not run
+ *   concurrently, and a later call on that stream that needs a larger
+ *   workspace (it replaces the buffers) or sgemm_f32_release() invalidates
+ *   those graphs — size the workspace with the largest shape before
+ *   capturing.
  *
  * Environment (read on every call; for tuning and measurement, not needed
  * for correct results):
