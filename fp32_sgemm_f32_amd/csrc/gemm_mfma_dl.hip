@@ -702,18 +702,22 @@ using Dl128x128x32K2 = MfmaDlCore<128, 128, 32, 2, 2, 3, 2>;
 using Dl64x64x64 = MfmaDlCore<64, 64, 64, 2, 2, 3, 1, 2>;
 using Dl128x256x16 = MfmaDlCore<128, 256, 16, 2, 2, 3>;
 using Dl256x128x16 = MfmaDlCore<256, 128, 16, 2, 2, 3>;
-// Edge-masking variants of the configurations the automatic choice uses,
-// for each storage order of A and B (NN, TN, NT, TT).
-#define SGEMM_DL_EDGE_CORES(name, BM, BN, BK, WM, WN, S, KS, LA)            \
-    using name##E = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true>;          \
-    using name##TN = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, true>;   \
-    using name##NT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, false, true>; \
-    using name##TT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, true, true>;
-SGEMM_DL_EDGE_CORES(Dl64x64x32, 64, 64, 32, 2, 2, 4, 1, 2)
-SGEMM_DL_EDGE_CORES(Dl64x64x64, 64, 64, 64, 2, 2, 3, 1, 2)
-SGEMM_DL_EDGE_CORES(Dl128x128x32, 128, 128, 32, 2, 2, 3, 1, 2)
-SGEMM_DL_EDGE_CORES(Dl256x256x16, 256, 256, 16, 4, 2, 3, 1, 1)
-#undef SGEMM_DL_EDGE_CORES
+// The configurations the automatic choice uses, for each storage order of A
+// and B (NN, TN, NT, TT): whole-tile variants (the NN one is defined above)
+// and edge-masking ones.
+#define SGEMM_DL_LAYOUT_CORES(name, BM, BN, BK, WM, WN, S, KS, LA)                  \
+    using name##TN = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, false, true>;        \
+    using name##NT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, false, false, true>; \
+    using name##TT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, false, true, true>;  \
+    using name##E = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true>;                \
+    using name##ETN = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, true>;        \
+    using name##ENT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, false, true>; \
+    using name##ETT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, true, true>;
+SGEMM_DL_LAYOUT_CORES(Dl64x64x32, 64, 64, 32, 2, 2, 4, 1, 2)
+SGEMM_DL_LAYOUT_CORES(Dl64x64x64, 64, 64, 64, 2, 2, 3, 1, 2)
+SGEMM_DL_LAYOUT_CORES(Dl128x128x32, 128, 128, 32, 2, 2, 3, 1, 2)
+SGEMM_DL_LAYOUT_CORES(Dl256x256x16, 256, 256, 16, 4, 2, 3, 1, 1)
+#undef SGEMM_DL_LAYOUT_CORES
 
 template <class Core>
 static hipError_t launch(const KernelArgs &a, hipStream_t s) {
@@ -741,30 +745,33 @@ static hipError_t occ(int *n) {
     X(SGEMM_CFG_DL_128x256x16, Dl128x256x16)        \
     X(SGEMM_CFG_DL_256x128x16, Dl256x128x16)
 
-#define SGEMM_DL_EDGE_CONFIGS(X)                  \
+#define SGEMM_DL_LAYOUT_CONFIGS(X)                \
     X(SGEMM_CFG_DL_64x64x32, Dl64x64x32)          \
     X(SGEMM_CFG_DL_64x64x64, Dl64x64x64)          \
     X(SGEMM_CFG_DL_128x128x32, Dl128x128x32)     \
     X(SGEMM_CFG_DL_256x256x16, Dl256x256x16)
 
 hipError_t launch_mfma_dl(int cfg, const KernelArgs &a, hipStream_t s) {
-    if (a.edge) {
-        const int layout = (a.trans_a ? 1 : 0) | (a.trans_b ? 2 : 0);
-        switch (cfg) {
-#define X(id, core)                                \
-    case id:                                       \
-        switch (layout) {                          \
-        case 0: return launch<core##E>(a, s);      \
-        case 1: return launch<core##TN>(a, s);     \
-        case 2: return launch<core##NT>(a, s);     \
-        default: return launch<core##TT>(a, s);    \
+    const int layout = (a.trans_a ? 1 : 0) | (a.trans_b ? 2 : 0);
+    switch (cfg) {
+#define X(id, core)                                                   \
+    case id:                                                          \
+        switch (layout | (a.edge ? 4 : 0)) {                          \
+        case 0: return launch<core>(a, s);                            \
+        case 1: return launch<core##TN>(a, s);                        \
+        case 2: return launch<core##NT>(a, s);                        \
+        case 3: return launch<core##TT>(a, s);                        \
+        case 4: return launch<core##E>(a, s);                         \
+        case 5: return launch<core##ETN>(a, s);                       \
+        case 6: return launch<core##ENT>(a, s);                       \
+        default: return launch<core##ETT>(a, s);                      \
         }
-            SGEMM_DL_EDGE_CONFIGS(X)
+        SGEMM_DL_LAYOUT_CONFIGS(X)
 #undef X
-        default: return hipErrorInvalidValue;
-        }
+    default: break;
     }
-    if (a.trans_a || a.trans_b) return hipErrorInvalidValue;
+    // The other configurations: whole tiles, A M x K and B K x N only.
+    if (a.edge || layout) return hipErrorInvalidValue;
     switch (cfg) {
 #define X(id, core) \
     case id: return launch<core>(a, s);

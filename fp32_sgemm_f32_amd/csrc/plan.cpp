@@ -149,8 +149,7 @@ int make_plan(const PlanRequest &req, Plan *out) {
     p.tiles_m = (M + c.bm - 1) / c.bm;
     p.tiles_n = (N + c.bn - 1) / c.bn;
     p.ipt = (K + c.bk - 1) / c.bk;
-    // Transposed operands run on the edge-masking variants as well.
-    p.edge = (c.kind == kKindGeneric || !divides(c, M, N, K) || transposed) ? 1 : 0;
+    p.edge = (c.kind == kKindGeneric || !divides(c, M, N, K)) ? 1 : 0;
     const int tiles = p.tiles_m * p.tiles_n;
     const int occ = occ_of(req, cfg);
     // Split workgroups per CU: one by default (measured faster than filling

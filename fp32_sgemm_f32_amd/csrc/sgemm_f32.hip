@@ -229,9 +229,10 @@ int run(const Call &c) {
         // Leading dimensions too large for the 32-bit source offsets of the
         // direct-to-LDS kernels: an automatic choice falls back to the
         // register-staged kernel of the same tile (the general one when the
-        // tile does not divide the shape); a forced one is refused.
+        // tile does not divide the shape or an operand is transposed, which
+        // the staged kernels do not load); a forced one is refused.
         if (c.config != SGEMM_CFG_AUTO) return SGEMM_ERR_CONFIG;
-        req.config = p.edge ? SGEMM_CFG_GENERIC_64x64x16 : staged_equivalent(p.config);
+        req.config = p.edge || c.ta || c.tb ? SGEMM_CFG_GENERIC_64x64x16 : staged_equivalent(p.config);
         if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
     }
 

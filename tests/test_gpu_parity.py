@@ -601,14 +601,14 @@ def test_workload_full_size_storage_orders(dev, name, layout):
 # 32-bit source offsets (BM or BK rows of A, BK or BN rows of B, times the
 # leading dimension, under 2^32 bytes; 2^31 for the edge-masking ones): the
 # automatic choice falls back (register-staged kernel for whole tiles, the
-# general kernel otherwise) and a forced direct-to-LDS configuration is
-# refused.  Buffers of 2-4 GiB.
+# general kernel for edges and transposed operands) and a forced
+# direct-to-LDS configuration is refused.  Buffers of 2-4 GiB.
 LD_CASES = {
     # name: (trans_a, trans_b, M, N, K, lda, ldb)
     "nn_lda": (0, 0, 64, 128, 64, 2 ** 24 + 4, 128),
     "nn_ldb": (0, 0, 128, 64, 64, 64, 2 ** 24 + 4),
-    "tn_lda": (1, 0, 128, 128, 64, 2 ** 23 + 4, 128),
-    "nt_ldb": (0, 1, 128, 64, 64, 64, 2 ** 23 + 4),
+    "tn_lda": (1, 0, 128, 128, 64, 2 ** 24 + 4, 128),        # whole tiles: 2^32 limit
+    "nt_ldb_ragged": (0, 1, 100, 64, 64, 64, 2 ** 23 + 4),   # edge masking: 2^31 limit
 }
 
 
