@@ -214,9 +214,10 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False, config
     """C = alpha * op(A) @ op(B) + beta * C for float32 HIP tensors.
 
     A is the stored matrix: (M, K), or (K, M) with trans_a (op(A) = A^T);
-    B: (K, N), or (N, K) with trans_b.  All row-major (unit column stride;
-    padded rows allowed).  C (M, N) is allocated if None (then beta must be
-    0).  Returns C.
+    B: (K, N), or (N, K) with trans_b.  Row-major (unit column stride; padded
+    rows allowed); a column-major view (X.t() of a row-major X) is taken as
+    the other storage order, without a copy.  C (M, N) must be row-major and
+    is allocated if None (then beta must be 0).  Returns C.
     """
     import torch
 
@@ -233,15 +234,30 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False, config
         C = torch.empty((M, N), dtype=torch.float32, device=A.device)
     elif C.dtype != torch.float32 or tuple(C.shape) != (M, N) or C.device != A.device:
         raise ValueError("C must be float32 (M, N) on A's device")
-    lda, ldb, ldc = _row_major_ld(A, "A"), _row_major_ld(B, "B"), _row_major_ld(C, "C")
+    As, ta, lda = _stored(A, "A", trans_a)
+    Bs, tb, ldb = _stored(B, "B", trans_b)
+    ldc = _row_major_ld(C, "C")
     if stream is None:
         stream = torch.cuda.current_stream(A.device)
     with torch.cuda.device(A.device):
-        st = gemm_raw(int(bool(trans_a)), int(bool(trans_b)), M, N, K, float(alpha), A.data_ptr(), lda,
-                      B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc, stream.cuda_stream, config, sched)
+        st = gemm_raw(ta, tb, M, N, K, float(alpha), As.data_ptr(), lda, Bs.data_ptr(), ldb, float(beta),
+                      C.data_ptr(), ldc, stream.cuda_stream, config, sched)
     if st != OK:
         raise SgemmError(st, "sgemm_f32_gemm")
     return C
+
+
+def _stored(t, name, trans):
+    """(row-major tensor, transpose flag, leading dimension) for operand t as
+    given with flag `trans`: a column-major view (t.t() of a row-major
+    matrix) is the same memory stored the other way, so the flag flips and
+    nothing is copied."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.numel() > 0 and t.shape[1] > 1 and t.stride(1) != 1 and t.stride(0) == 1:
+        s = t.t()
+        return s, int(not trans), _row_major_ld(s, name)
+    return t, int(bool(trans)), _row_major_ld(t, name)
 
 
 def _row_major_ld(t, name):
@@ -257,8 +273,10 @@ def _row_major_ld(t, name):
 def matmul(A, B, out=None, config=CFG_AUTO, sched=SCHED_AUTO, stream=None):
     """C = A @ B for float32 CUDA (HIP) tensors, on the current (or given) stream.
 
-    A: (M, K), B: (K, N), row-major (unit column stride; padded rows allowed).
-    Returns `out` (allocated if None).  Raises SgemmError on a library error.
+    A: (M, K), B: (K, N), each row-major (unit column stride; padded rows
+    allowed) or column-major (a transposed view such as X.t(), run as the
+    other storage order without a copy).  `out` must be row-major.  Returns
+    `out` (allocated if None).  Raises SgemmError on a library error.
     """
     import torch
 
@@ -273,12 +291,18 @@ def matmul(A, B, out=None, config=CFG_AUTO, sched=SCHED_AUTO, stream=None):
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or out.device != A.device:
         raise ValueError("out must be float32 (M, N) on A's device")
-    lda, ldb, ldc = _row_major_ld(A, "A"), _row_major_ld(B, "B"), _row_major_ld(out, "out")
+    As, ta, lda = _stored(A, "A", False)
+    Bs, tb, ldb = _stored(B, "B", False)
+    ldc = _row_major_ld(out, "out")
     if stream is None:
         stream = torch.cuda.current_stream(A.device)
     with torch.cuda.device(A.device):
-        st = sgemm_raw(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc,
-                       stream.cuda_stream, config, sched)
+        if ta or tb:
+            st = gemm_raw(ta, tb, M, N, K, 1.0, As.data_ptr(), lda, Bs.data_ptr(), ldb, 0.0, out.data_ptr(), ldc,
+                          stream.cuda_stream, config, sched)
+        else:
+            st = sgemm_raw(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc,
+                           stream.cuda_stream, config, sched)
     if st != OK:
         raise SgemmError(st)
     return out

@@ -703,3 +703,34 @@ def test_random_interface_cases(dev, seed):
     check(Cv.cpu().numpy(), C_ref, S, f"random {seed}")
     full = torch.as_strided(Cbuf, (M, ldc), (ldc, 1), offs[2]).cpu().numpy()
     assert np.all(np.isnan(full[:, N:])), "ldc padding was written"
+
+
+@pytest.mark.parametrize("views", ["a_t", "b_t", "both_t", "gemm_flip"])
+def test_python_binding_takes_transposed_views(dev, views):
+    """Column-major views (X.t() of a row-major X, padded rows included) run
+    as the other storage order, without a copy, and give the product of the
+    logical matrices."""
+    import torch
+    M, N, K = 200, 136, 260
+    log(f"case binding views {views}")
+    A, B = workloads.generate(M, N, K, "int4", 97)
+    C_ref, _ = oracle.gemm(A, B)
+    # Row-major storage of A^T and B^T with padded rows; their .t() views
+    # are the logical A (M x K) and B (K x N), column-major.
+    At = torch.zeros((K, M + 12), dtype=torch.float32, device=dev)[:, :M]
+    At.copy_(to_dev(np.ascontiguousarray(A.T), dev))
+    Bt = torch.zeros((N, K + 4), dtype=torch.float32, device=dev)[:, :K]
+    Bt.copy_(to_dev(np.ascontiguousarray(B.T), dev))
+    Ad, Bd = to_dev(A, dev), to_dev(B, dev)
+    if views == "a_t":
+        C = sg.matmul(At.t(), Bd)
+    elif views == "b_t":
+        C = sg.matmul(Ad, Bt.t())
+    elif views == "both_t":
+        C = sg.matmul(At.t(), Bt.t())
+    else:
+        # gemm with trans_a on a column-major view: the view is A^T (K x M),
+        # so op of it is A, run as A stored M x K.
+        C = sg.gemm(Ad.t(), Bt.t(), trans_a=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref)
