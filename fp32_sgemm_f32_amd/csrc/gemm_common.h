@@ -23,7 +23,7 @@ struct KernelArgs {
     const float *A;
     const float *B;
     float *C;
-    int64_t lda, ldb, ldc;
+    int lda, ldb, ldc;      // leading dimensions in elements (the API takes int)
     int M, N, K;      // the shape (the edge-masking kernels need it)
     int edge;         // the shape is not a multiple of the tile
     int trans_a;      // A stored K x M (op(A) = A^T); else M x K
