@@ -298,6 +298,16 @@ def main():
             log(json.dumps(r))
             rest.append(r)
         detail["others"] = rest
+        if not args.no_cpu_baseline:
+            # The FP64 oracle on each workload (a bounded row sample, whole
+            # product where it fits the budget) beside the GPU's median.
+            for r in [head] + rest:
+                ww = workloads.WORKLOADS[r["workload"]]
+                cpu_r = cpu_baseline(ww, min(args.cpu_seconds, 6.0))
+                r["cpu_oracle"] = cpu_r
+                r["gpu_over_oracle"] = r["tflops_median"] / cpu_r["value"]
+                log(f"{ww.name}: oracle {cpu_r['value'] * 1e3:.1f} GFLOP/s ({cpu_r['sample']}); "
+                    f"GPU median {r['tflops_median']:.1f} TFLOP/s = {r['gpu_over_oracle']:.0f}x")
 
     achieved = w.flops / (head["region_event_ms_per_call"] * 1e-3) / 1e12
     traffic = None
