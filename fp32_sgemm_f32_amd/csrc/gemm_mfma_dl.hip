@@ -17,9 +17,8 @@
 // operand is kept in LDS the way it is stored in memory:
 //   * k-contiguous (A stored M x K, B stored N x K): rows of BK floats, one
 //     per m (n), no padding; the 16-byte quad Q of row r is stored at quad
-//     position Q ^ swz(r).  With the XOR the operand reads below (one quad
-//     of 8 or 16 consecutive rows per phase) hit distinct banks in both a
-//     32-bank and a 64-bank LDS.
+//     position Q ^ swz(r), chosen so that the operand reads below hit
+//     distinct banks (measured with the bank-conflict counter).
 //   * m/n-contiguous (A stored K x M, B stored K x N): BK rows of BM (BN)
 //     floats, one per k, as in memory.
 // Operands: as in the register-staged core, lane half h (lanes 32h..32h+31)
@@ -241,9 +240,14 @@ struct MfmaDlCore {
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     }
 
-    // Quad position of quad Q of A row r is Q ^ swz(r).
+    // Quad position of quad Q of a k-contiguous row r is Q ^ swz(r).  Each
+    // was checked on gfx950 with the SQ_LDS_BANK_CONFLICT counter for the
+    // operand reads below: none.  (For BK = 16, ((r >> 1) ^ (r >> 3)) & 3,
+    // conflict-free in 32-bank and 64-bank models of the LDS, measured 4
+    // extra cycles per ds_read_b128 on the hardware; (r >> 2) & 3 measured
+    // none.)
     __device__ __forceinline__ static int swz(int r) {
-        if constexpr (BK == 16) return ((r >> 1) ^ (r >> 3)) & 3;
+        if constexpr (BK == 16) return (r >> 2) & 3;
         else if constexpr (BK == 32) return (r ^ (r >> 3)) & 7;
         else return r & 15;
     }
