@@ -19,5 +19,9 @@ hipError_t occupancy_generic(int cfg, int *wg_per_cu);
 hipError_t launch_valu(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t occupancy_valu(int cfg, int *wg_per_cu);
 hipError_t launch_scale_c(float *C, int M, int N, int64_t ldc, float beta, hipStream_t s);
+// dst (drows x dcols, leading dimension ldd) = src (rows x cols, lds) with
+// zeros outside it.
+hipError_t launch_pack(const float *src, int64_t lds, int rows, int cols, float *dst, int64_t ldd, int drows,
+                       int dcols, hipStream_t s);
 
 }  // namespace sgemm

@@ -37,6 +37,8 @@ struct Workspace {
     int64_t ncounters = 0;
     float *partials = nullptr;
     int64_t partial_bytes = 0;
+    float *pack = nullptr;         // repacked operands (see run_packed)
+    int64_t pack_bytes = 0;
 };
 
 std::mutex g_mu;
@@ -135,6 +137,7 @@ struct Call {
     float alpha, beta;
     hipStream_t stream;
     int config, sched;
+    int repacked = 0;              // already laid out for the vector kernels by run_packed
 
     // Rows and columns of A and B as stored.
     int a_rows() const { return ta ? K : M; }
@@ -203,6 +206,85 @@ int workspace_for(int dev, hipStream_t s, const Plan &p, Workspace *out) {
     return SGEMM_OK;
 }
 
+// Repacking buffer of (dev, stream) holding at least `bytes`.  Takes g_mu.
+int pack_space_for(int dev, hipStream_t s, int64_t bytes, float **out) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace &w = g_workspaces[{dev, s}];
+    if (w.pack_bytes < bytes) {
+        hipError_t e = hipStreamSynchronize(s);   // the old buffer may still be in use
+        if (e != hipSuccess) return hip_fail(e);
+        if (w.pack) (void)hipFree(w.pack);
+        w.pack = nullptr;
+        w.pack_bytes = 0;
+        e = hipMalloc((void **)&w.pack, (size_t)bytes);
+        if (e != hipSuccess) return hip_fail(e);
+        w.pack_bytes = bytes;
+    }
+    *out = w.pack;
+    return SGEMM_OK;
+}
+
+int run(const Call &c);
+
+inline int up4(int x) { return (x + 3) & ~3; }
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+// Products of at least this many multiply-adds whose layout the vector
+// kernels cannot load are repacked rather than run on the general kernel.
+// Measured on MI355X (N odd, M = K = N - 1): the general kernel is faster at
+// 256^3 (17 vs 20 us, the copies' launches dominate), the repacked product
+// from 384^3 on (20 vs 25 us) and 3.3x faster at 2048^3; 2^25 ~ 322^3 lies
+// between.
+constexpr int64_t kRepackMinMacs = (int64_t)1 << 25;
+
+bool worth_repacking(const Call &c) {
+    const char *v = std::getenv("SGEMM_F32_REPACK_MIN_MACS");
+    const int64_t lim = v && *v ? std::atoll(v) : kRepackMinMacs;
+    return lim >= 0 && (int64_t)c.M * c.N * c.K >= lim && c.M >= 64 && c.N >= 64 && c.K >= 64;
+}
+
+// The same product on copies laid out for the vector kernels: every stored
+// row length (and N) padded to a multiple of 4 with zeros, 16-byte aligned
+// rows; the padded k terms are 0 * 0.  A, B are copied only when their own
+// layout does not already qualify; C is computed in a padded copy (holding
+// C's values when beta reads them) and its M x N part copied back.  All on
+// the caller's stream, in the library's per-stream repacking buffer.
+int run_packed(const Call &c, int dev) {
+    const int Mp = c.ta ? up4(c.M) : c.M, Np = up4(c.N), Kp = up4(c.K);
+    const int ar = c.ta ? Kp : Mp, ac = c.ta ? Mp : Kp;     // A as stored, padded
+    const int br = c.tb ? Np : Kp, bc = c.tb ? Kp : Np;
+    const bool pa = !(aligned16(c.A) && (c.lda & 3) == 0 && c.a_rows() == ar && c.a_cols() == ac);
+    const bool pb = !(aligned16(c.B) && (c.ldb & 3) == 0 && c.b_rows() == br && c.b_cols() == bc);
+    const bool pc = !(aligned16(c.C) && (c.ldc & 3) == 0 && Mp == c.M && Np == c.N);
+    auto round256 = [](int64_t b) { return (b + 255) / 256 * 256; };
+    const int64_t a_bytes = pa ? round256((int64_t)ar * ac * 4) : 0;
+    const int64_t b_bytes = pb ? round256((int64_t)br * bc * 4) : 0;
+    const int64_t c_bytes = pc ? round256((int64_t)Mp * Np * 4) : 0;
+    float *buf = nullptr;
+    int st = pack_space_for(dev, c.stream, a_bytes + b_bytes + c_bytes, &buf);
+    if (st != SGEMM_OK) return st;
+    float *Ap = buf, *Bp = (float *)((char *)buf + a_bytes), *Cp = (float *)((char *)buf + a_bytes + b_bytes);
+    hipError_t e = hipSuccess;
+    if (pa) e = launch_pack(c.A, c.lda, c.a_rows(), c.a_cols(), Ap, ac, ar, ac, c.stream);
+    if (e == hipSuccess && pb) e = launch_pack(c.B, c.ldb, c.b_rows(), c.b_cols(), Bp, bc, br, bc, c.stream);
+    if (e == hipSuccess && pc && c.scaled && c.beta != 0.0f)
+        e = launch_pack(c.C, c.ldc, c.M, c.N, Cp, Np, Mp, Np, c.stream);
+    if (e != hipSuccess) return hip_fail(e);
+
+    Call q = c;
+    q.M = Mp; q.N = Np; q.K = Kp;
+    if (pa) { q.A = Ap; q.lda = ac; }
+    if (pb) { q.B = Bp; q.ldb = bc; }
+    if (pc) { q.C = Cp; q.ldc = Np; }
+    q.repacked = 1;
+    if ((st = run(q)) != SGEMM_OK) return st;
+    if (pc) {
+        e = launch_pack(Cp, Np, c.M, c.N, c.C, c.ldc, c.M, c.N, c.stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return SGEMM_OK;
+}
+
 int run(const Call &c) {
     int st = check_args(c);
     if (st != SGEMM_OK) return st;
@@ -218,6 +300,9 @@ int run(const Call &c) {
         if ((st = check_device_range(c.A, extent_bytes(c.a_rows(), c.a_cols(), c.lda), dev)) != SGEMM_OK) return st;
         if ((st = check_device_range(c.B, extent_bytes(c.b_rows(), c.b_cols(), c.ldb), dev)) != SGEMM_OK) return st;
     }
+
+    if (!c.repacked && c.config == SGEMM_CFG_AUTO && c.reads_ab() && !vector_layout(c) && worth_repacking(c))
+        return run_packed(c, dev);
 
     DeviceInfo info;
     if ((st = device_info(dev, &info)) != SGEMM_OK) return st;
@@ -275,12 +360,12 @@ int run(const Call &c) {
 
 Call plain(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float *C, int ldc,
            hipStream_t stream, int config, int sched) {
-    return Call{M, N, K, 0, 0, A, B, C, lda, ldb, ldc, 0, 1.0f, 0.0f, stream, config, sched};
+    return Call{M, N, K, 0, 0, A, B, C, lda, ldb, ldc, 0, 1.0f, 0.0f, stream, config, sched, 0};
 }
 
 Call blas(int ta, int tb, int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
           float beta, float *C, int ldc, hipStream_t stream, int config, int sched) {
-    return Call{M, N, K, ta != 0, tb != 0, A, B, C, lda, ldb, ldc, 1, alpha, beta, stream, config, sched};
+    return Call{M, N, K, ta != 0, tb != 0, A, B, C, lda, ldb, ldc, 1, alpha, beta, stream, config, sched, 0};
 }
 
 }  // namespace
@@ -383,6 +468,7 @@ SGEMM_API int sgemm_f32_release(void) {
     for (auto &kv : sgemm::g_workspaces) {
         if (kv.second.counters && hipFree(kv.second.counters) != hipSuccess) st = SGEMM_ERR_HIP;
         if (kv.second.partials && hipFree(kv.second.partials) != hipSuccess) st = SGEMM_ERR_HIP;
+        if (kv.second.pack && hipFree(kv.second.pack) != hipSuccess) st = SGEMM_ERR_HIP;
     }
     sgemm::g_workspaces.clear();
     return st;

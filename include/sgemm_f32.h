@@ -22,7 +22,12 @@
  *   are multiples of 4, lda, ldb and ldc are multiples of 4 and A, B, C are
  *   16-byte aligned, the 16-byte vector kernels run (tile edges masked
  *   where the shape is not a multiple of the tile).  Any other layout runs
- *   on a general kernel with element-wise bounds checks.
+ *   on a general kernel with element-wise bounds checks, except that with
+ *   the automatic configuration, M, N, K >= 64 and M * N * K at least 2^25,
+ *   A and B (and C, when its own layout does not qualify) are first copied
+ *   on `stream` into zero-padded aligned buffers of the library and the
+ *   product runs on the vector kernels (results as unpadded; C's padding
+ *   is still untouched).
  *
  * Memory and ownership
  *   A, B, C are device pointers, caller-owned, allocated on the HIP device
@@ -46,7 +51,9 @@
  *   Split-K ("Stream-K") schedules keep partial tiles and per-tile arrival
  *   counters in a workspace owned by the library, one per (device, stream),
  *   grown on demand with hipMalloc and kept until sgemm_f32_release() or
- *   process exit.  Calls on different streams therefore never share one.
+ *   process exit.  Repacked calls (see above) keep their copies in a
+ *   buffer of the same (device, stream), held and freed the same way.
+ *   Calls on different streams therefore never share one.
  *   Calls that run concurrently on the SAME stream are impossible by stream
  *   order; calls from several host threads on one stream are serialised by
  *   the stream as well.
@@ -55,8 +62,8 @@
  *   A call only enqueues kernels (no memset, no copy), so it can be captured
  *   into a HIP graph, provided it allocates nothing during capture: make one
  *   eager call with the same stream and a shape at least as large first (the
- *   Stream-K workspace is then in place; shapes that run whole tiles need
- *   none).  Replays use the workspace the capturing stream had at capture
+ *   Stream-K workspace and the repacking buffer are then in place; aligned
+ *   shapes that run whole tiles need neither).  Replays use the workspace the capturing stream had at capture
  *   time: replays of graphs captured on one stream must not run
  *   concurrently, and a later call on that stream that needs a larger
  *   workspace (it replaces the buffers) or sgemm_f32_release() invalidates
@@ -70,7 +77,10 @@
  *   SGEMM_F32_XCD_REMAP     0 turns off the remapping of workgroup ids that
  *                           gives each XCD a contiguous run of tiles;
  *   SGEMM_F32_GROUP_M       tile rows per group of the tile order (default:
- *                           chosen by the planner).
+ *                           chosen by the planner);
+ *   SGEMM_F32_REPACK_MIN_MACS  products of at least this many multiply-adds
+ *                           whose layout the vector kernels cannot load are
+ *                           run on aligned copies (default 2^25; -1: never).
  */
 #ifndef SGEMM_F32_H
 #define SGEMM_F32_H

@@ -734,3 +734,104 @@ def test_python_binding_takes_transposed_views(dev, views):
         C = sg.gemm(Ad.t(), Bt.t(), trans_a=True)
     torch.cuda.synchronize()
     assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref)
+
+
+# Large products whose layout the vector kernels cannot load are run on
+# zero-padded aligned copies (automatic choice only): odd N, odd K, odd M
+# with A stored K x M, a float-offset pointer, odd leading dimensions, and
+# beta != 0 (C copied in and back).  Each above the size from which the
+# copies pay (2^25 multiply-adds).
+REPACK_CASES = {
+    # name: (ta, tb, M, N, K, pads (A, B, C), offsets (A, B, C), alpha, beta)
+    "odd_n": (0, 0, 1024, 1031, 2049 + 7, (0, 0, 0), (0, 0, 0), 1.0, 0.0),
+    "odd_k": (0, 0, 1200, 1280, 1401, (0, 0, 0), (0, 0, 0), 1.0, 0.0),
+    "ta_odd_m": (1, 0, 1201, 1024, 1792, (0, 0, 0), (0, 0, 0), 1.0, 0.0),
+    "tb_odd_k": (0, 1, 1024, 1152, 1827, (0, 0, 0), (0, 0, 0), -0.5, 0.0),
+    "tt_odd_all": (1, 1, 1237, 1113, 1601, (0, 0, 0), (0, 0, 0), 1.0, 0.0),
+    "a_offset": (0, 0, 1280, 1280, 1408, (0, 0, 0), (1, 0, 0), 1.0, 0.0),
+    "odd_ld_beta": (0, 0, 1280, 1283, 1344, (3, 1, 5), (0, 2, 1), 1.5, -2.0),
+}
+
+
+@pytest.mark.parametrize("case", list(REPACK_CASES))
+def test_repacked_large_products(dev, case):
+    import torch
+    ta, tb, M, N, K, pads, offs, alpha, beta = REPACK_CASES[case]
+    log(f"case repack {case}: ta={ta} tb={tb} shape=({M},{N},{K}) pads={pads} offs={offs}")
+    A, B = workloads.generate(M, N, K, "int4", 91)
+    As, Bs = stored(A, ta), stored(B, tb)
+    C0 = workloads.generate(M, 1, N, "int4", 92)[0]
+
+    def placed(X, pad, off):
+        rows, cols = X.shape
+        ld = cols + pad
+        buf = torch.full((rows * ld + off + 4,), float("nan"), dtype=torch.float32, device=dev)
+        view = torch.as_strided(buf, (rows, cols), (ld, 1), off)
+        view.copy_(to_dev(X, dev))
+        return buf, view, ld
+
+    _, Av, _ = placed(As, pads[0], offs[0])
+    _, Bv, _ = placed(Bs, pads[1], offs[1])
+    Cbuf, Cv, ldc = placed(C0, pads[2], offs[2])
+    for sched in (sg.SCHED_AUTO, sg.SCHED_STREAMK):
+        Cv.copy_(to_dev(C0, dev))
+        sg.gemm(Av, Bv, Cv, alpha, beta, ta, tb, sched=sched)
+        torch.cuda.synchronize()
+        C_ref, _ = oracle.gemm_blas(As, Bs, C0, alpha, beta, ta, tb)
+        assert np.array_equal(Cv.cpu().numpy().astype(np.float64), C_ref), sg.SCHED_NAMES[sched]
+        full = torch.as_strided(Cbuf, (M, ldc), (ldc, 1), offs[2]).cpu().numpy()
+        assert np.all(np.isnan(full[:, N:])), "ldc padding was written"
+
+
+@pytest.mark.parametrize("limit", ["0", "-1"], ids=["always_repack", "never_repack"])
+def test_repack_threshold_override(dev, limit, monkeypatch):
+    """SGEMM_F32_REPACK_MIN_MACS moves the size from which misaligned
+    products are repacked: 0 repacks a small odd-shaped product, -1 leaves
+    a large one on the general kernel; both give the oracle's result
+    (integer inputs: exact)."""
+    import torch
+    monkeypatch.setenv("SGEMM_F32_REPACK_MIN_MACS", limit)
+    M, N, K = (96, 101, 75) if limit == "0" else (700, 643, 901)
+    log(f"case repack override {limit}: shape=({M},{N},{K})")
+    A, B = workloads.generate(M, N, K, "int4", 93)
+    for ta, tb in LAYOUTS:
+        As, Bs = stored(A, ta), stored(B, tb)
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+        sg.gemm(to_dev(As, dev), to_dev(Bs, dev), C, 1.0, 0.0, ta, tb)
+        torch.cuda.synchronize()
+        C_ref, _ = oracle.gemm_blas(As, Bs, None, 1.0, 0.0, ta, tb)
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref), (ta, tb)
+
+
+def test_graph_capture_of_a_repacked_call(dev):
+    """A repacked call (odd N, beta != 0: A, B and C copied, C copied back)
+    captured after an eager call of the same shape replays correctly, with
+    new A and C between replays (integer inputs: exact)."""
+    import torch
+    M, N, K = 640, 517, 768
+    log(f"case graph capture repacked shape=({M},{N},{K})")
+    s = torch.cuda.Stream(device=dev)
+    A0, B = workloads.generate(M, N, K, "int4", 98)
+    Ad, Bd = to_dev(A0, dev), to_dev(B, dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    with torch.cuda.stream(s):
+        sg.gemm(Ad, Bd, C, 1.0, 1.0)                       # eager: repacking buffer ready
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        sg.gemm(Ad, Bd, C, 2.0, -1.0)
+    torch.cuda.synchronize()
+    for r in range(3):
+        A_r = workloads.generate(M, N, K, "int4", 210 + r)[0]
+        C_r = workloads.generate(M, 1, N, "int4", 220 + r)[0]
+        Ad.copy_(to_dev(A_r, dev))
+        E = to_dev(C_r, dev)
+        sg.gemm(Ad, Bd, E, 2.0, -1.0)                      # eager reference on the device
+        C.copy_(to_dev(C_r, dev))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        C_ref, _ = oracle.gemm_blas(A_r, B, C_r, 2.0, -1.0, 0, 0)
+        got = C.cpu().numpy()
+        assert np.array_equal(got.astype(np.float64), C_ref), f"replay {r}"
+        assert np.array_equal(got, E.cpu().numpy()), f"replay {r} vs eager"
