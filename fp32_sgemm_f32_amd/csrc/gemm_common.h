@@ -1,15 +1,10 @@
 // Device-side pieces shared by every kernel configuration: the kernel
 // argument block, the workgroup -> work mapping (data-parallel tiles first,
-// then the Stream-K share), and the deterministic partial-tile fixup.
+// then the Stream-K share), and the deterministic sum of split tiles.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-// How split workgroups publish partial tiles to the last arriver (see run_gemm).
-#ifndef SGEMM_FIXUP_MODE
-#define SGEMM_FIXUP_MODE 1
-#endif
 
 namespace sgemm {
 
@@ -39,8 +34,7 @@ struct KernelArgs {
     int xcd_remap;    // remap blockIdx so each XCD owns a contiguous run of work
     int group_m;      // tile order: groups of group_m tile rows
     int64_t sk_iters; // sk_tiles * ipt
-    int *counters;    // [sk_tiles] arrival counters, zero between calls
-    float *partials;  // [sk_grid][2][tile floats] partial tiles
+    float *partials;  // [sk_grid][2][tile rows][tile columns] partial tiles
 };
 
 // Value stored to C at p for a product value v: v itself for the plain
@@ -109,13 +103,18 @@ __device__ __forceinline__ float *partial_ptr(const KernelArgs &a, int w, int sl
 //   zero()                          accumulators := 0
 //   mainloop(a, lds, tm, tn, k0, k1) accumulate K chunks [k0, k1) of tile (tm, tn)
 //   store_c(a, tm, tn)              write the accumulators to C
-//   store_partial(p) / add_partial(p)  thread-private copy to/from a partial tile
+//   store_tile(p)                   write them to a dense row-major tile at p
+//
+// A split tile's contributors each leave their partial sum in the workspace
+// and nothing else: sk_fixup (a second kernel on the same stream, which the
+// kernel boundary orders after every partial is written) adds them and
+// writes C.  No workgroup waits for, or synchronises with, another.
 //
 // SPLIT = false is the whole-tile-only instance (sk_tiles == 0): it carries
 // none of the split bookkeeping, which keeps its register allocation to the
 // main loop's needs.
 template <class Core, bool SPLIT>
-__device__ __forceinline__ void run_gemm(const KernelArgs &a, float *lds, int *flag) {
+__device__ __forceinline__ void run_gemm(const KernelArgs &a, float *lds) {
     Core core;
     const int w = logical_wg(a);
 
@@ -135,68 +134,53 @@ __device__ __forceinline__ void run_gemm(const KernelArgs &a, float *lds, int *f
         const int tl = __builtin_amdgcn_readfirstlane(s / a.ipt);   // split-tile index
         const int k0 = s - tl * a.ipt;
         const int k1 = k0 + (e - s < a.ipt - k0 ? e - s : a.ipt - k0);
-        const int first = __builtin_amdgcn_readfirstlane(sk_owner(a, tl * a.ipt));
-        const int last = __builtin_amdgcn_readfirstlane(sk_owner(a, (tl + 1) * a.ipt - 1));
         int tm, tn;
         tile_coords(a, a.dp_tiles + tl, tm, tn);
         core.zero();
         core.mainloop(a, lds, tm, tn, k0, k1);
-
-        if (first == last) {
-            core.store_c(a, tm, tn);
-        } else {
-            // Every contributor leaves its partial; the last to arrive sums
-            // all partials in contributor order (a fixed order, so the result
-            // does not depend on arrival order) and writes C.  Nobody waits
-            // for anybody, and the counter is reset for the next call.
-            core.store_partial(partial_ptr<Core::TILE_FLOATS>(a, w, sk_slot(a, w, tl)));
-#if SGEMM_FIXUP_MODE == 0
-            __threadfence();
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                const int old = __hip_atomic_fetch_add(&a.counters[tl], 1, __ATOMIC_ACQ_REL,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-                *flag = (old == last - first) ? 1 : 0;
-            }
-            __syncthreads();
-#elif SGEMM_FIXUP_MODE == 1
-            // Each thread publishes its own partial (release at device scope),
-            // then one counter increment per workgroup.
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                const int old = __hip_atomic_fetch_add(&a.counters[tl], 1, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-                *flag = (old == last - first) ? 1 : 0;
-            }
-            __syncthreads();
-#else
-            // The workgroup barrier orders every thread's partial before thread
-            // 0's increment, which releases (and, for the last arriver,
-            // acquires) at device scope for the whole workgroup.
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                const int old = __hip_atomic_fetch_add(&a.counters[tl], 1, __ATOMIC_ACQ_REL,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-                *flag = (old == last - first) ? 1 : 0;
-            }
-            __syncthreads();
-#endif
-            const int is_last = __builtin_amdgcn_readfirstlane(*flag);
-            if (is_last) {
-#if SGEMM_FIXUP_MODE != 2
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#endif
-                core.zero();
-                for (int c = first; c <= last; ++c)
-                    core.add_partial(partial_ptr<Core::TILE_FLOATS>(a, c, sk_slot(a, c, tl)));
-                core.store_c(a, tm, tn);
-                if (threadIdx.x == 0)
-                    __hip_atomic_store(&a.counters[tl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            __syncthreads();   // *flag is reused by the next split tile
-        }
+        if (k0 == 0 && k1 == a.ipt)
+            core.store_c(a, tm, tn);   // the whole K range: not split after all
+        else
+            core.store_tile(partial_ptr<Core::TILE_FLOATS>(a, w, sk_slot(a, w, tl)));
         s += k1 - k0;
+    }
+}
+
+// The sum of the split tiles: one thread per 4 adjacent outputs of a split
+// tile (BM x BN, row-major in the partials).  Contributors are added in
+// Stream-K order, first to last, whatever order they finished in, so the
+// result is the same on every run.  Loads of up to 8 contributors are in
+// flight at once; the sum itself stays in contributor order.  Rows and
+// columns outside M x N are dropped; C is written with the epilogue.
+template <int BM, int BN>
+__device__ __forceinline__ void sk_fixup(const KernelArgs &a) {
+    constexpr int QUADS = BM * BN / 4;
+    const int64_t total = (int64_t)a.sk_tiles * QUADS;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int tl = (int)(q / QUADS);
+        const int e = 4 * (int)(q - (int64_t)tl * QUADS);
+        const int first = sk_owner(a, tl * a.ipt), last = sk_owner(a, (tl + 1) * a.ipt - 1);
+        if (first == last) continue;   // stored whole by its only owner
+        int tm, tn;
+        tile_coords(a, a.dp_tiles + tl, tm, tn);
+        const int row = tm * BM + e / BN, col = tn * BN + e % BN;
+        if (row >= a.M || col >= a.N) continue;
+        f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c0 = first; c0 <= last; c0 += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (c0 + u <= last)
+                    v[u] = *(const f32x4 *)(partial_ptr<BM * BN>(a, c0 + u, sk_slot(a, c0 + u, tl)) + e);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (c0 + u <= last) sum += v[u];
+        }
+        float *p = a.C + (int64_t)row * a.ldc + col;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (col + u < a.N) p[u] = epilogue(a, sum[u], p + u);
     }
 }
 

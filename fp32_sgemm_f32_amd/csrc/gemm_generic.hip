@@ -129,22 +129,21 @@ struct GenericCore {
         }
     }
 
-    __device__ __forceinline__ void store_partial(float *p) {
+    // The same mapping into a dense row-major BM x BN tile (a split tile's
+    // partial sum).
+    __device__ __forceinline__ void store_tile(float *p) {
+        const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+        const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
+        float *q = p + (wm * 32 + 4 * lh) * BN + wn * 32 + lr;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[r * NT + threadIdx.x] = acc[r];
-    }
-
-    __device__ __forceinline__ void add_partial(const float *p) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += p[r * NT + threadIdx.x];
+        for (int r = 0; r < 16; ++r) q[(8 * (r >> 2) + (r & 3)) * BN] = acc[r];
     }
 };
 
 template <bool SPLIT>
 __global__ __launch_bounds__(GenericCore::NT) void sgemm_generic_kernel(KernelArgs a) {
     __shared__ __attribute__((aligned(16))) float lds[GenericCore::LDS_FLOATS];
-    __shared__ int flag;
-    run_gemm<GenericCore, SPLIT>(a, lds, &flag);
+    run_gemm<GenericCore, SPLIT>(a, lds);
 }
 
 hipError_t launch_generic(int cfg, const KernelArgs &a, hipStream_t s) {

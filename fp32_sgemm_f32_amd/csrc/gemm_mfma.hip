@@ -332,40 +332,27 @@ struct MfmaCore {
                 }
     }
 
-    // Thread-private layout: value v of this thread at p[v * NT + tid].
-    __device__ __forceinline__ void store_partial(float *p) {
+    // The same mapping into a dense row-major BM x BN tile (a split tile's
+    // partial sum).
+    __device__ __forceinline__ void store_tile(float *p) {
         const int tid = threadIdx.x;
+        const int wave = tid >> 6, lane = tid & 63;
+        const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+        const int lr = lane & 31, lh = lane >> 5;
+        float *q = p + (wm * WTM + 4 * lh) * BN + wn * WTN + lr;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    p[((i * FN + j) * 16 + r) * NT + tid] = acc[i][j][r];
-    }
-
-    // One 32x32 block (16 values per lane) at a time: the empty asm keeps the
-    // compiler from hoisting every block's loads at once, which would need a
-    // second full accumulator set of registers.
-    __device__ __forceinline__ void add_partial(const float *p) {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    acc[i][j][r] += p[((i * FN + j) * 16 + r) * NT + tid];
-                asm volatile("" ::: "memory");
-            }
+                for (int r = 0; r < 16; ++r) q[(i * 32 + 8 * (r >> 2) + (r & 3)) * BN + j * 32] = acc[i][j][r];
     }
 };
 
 template <class Core, bool SPLIT>
 __global__ __launch_bounds__(Core::NT) void sgemm_mfma_kernel(KernelArgs a) {
     __shared__ __attribute__((aligned(16))) float lds[Core::LDS_FLOATS];
-    __shared__ int flag;
-    run_gemm<Core, SPLIT>(a, lds, &flag);
+    run_gemm<Core, SPLIT>(a, lds);
 }
 
 using Mfma256x256x16 = MfmaCore<256, 256, 16, 4, 2>;

@@ -661,29 +661,28 @@ struct MfmaDlCore {
             }
     }
 
-    // Thread-private layout: value v of thread t (of the first K group) at
-    // p[v * NT_MN + t].
-    __device__ __forceinline__ void store_partial(float *p) {
+    // The same mapping into a dense row-major BM x BN tile (a split tile's
+    // partial sum; whole tile, no masking, no epilogue).
+    __device__ __forceinline__ void store_tile(float *p) {
         const int tid = threadIdx.x;
         if (KSPLIT > 1 && tid >= NT_MN) return;
+        const int wave = tid >> 6, lane = tid & 63;
+        const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+        const int lr = lane & 31, lh = lane >> 5;
+        float *q = p + (wm * WTM + (AKC ? 4 : 4 * FM) * lh) * BN + wn * WTN + FN * lr;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) p[((i * FN + j) * 16 + r) * NT_MN + tid] = acc[i][j][r];
-    }
-
-    __device__ __forceinline__ void add_partial(const float *p) {
-        const int tid = threadIdx.x;
-        if (KSPLIT > 1 && tid >= NT_MN) return;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] += p[((i * FN + j) * 16 + r) * NT_MN + tid];
-                asm volatile("" ::: "memory");
+            for (int r = 0; r < 16; ++r) {
+                const int rho = 8 * (r >> 2) + (r & 3);
+                float *d = q + (AKC ? i * 32 + rho : FM * rho + i) * BN;
+                if constexpr (FN == 1) {
+                    *d = acc[i][0][r];
+                } else if constexpr (FN == 2) {
+                    *(f32x2 *)d = f32x2{acc[i][0][r], acc[i][1][r]};
+                } else {
+                    *(f32x4 *)d = f32x4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
+                }
             }
     }
 };
@@ -691,8 +690,7 @@ struct MfmaDlCore {
 template <class Core, bool SPLIT>
 __global__ __launch_bounds__(Core::NT) void sgemm_mfma_dl_kernel(KernelArgs a) {
     __shared__ __attribute__((aligned(1024))) float lds[Core::LDS_FLOATS];
-    __shared__ int flag;
-    run_gemm<Core, SPLIT>(a, lds, &flag);
+    run_gemm<Core, SPLIT>(a, lds);
     // No load may still write this workgroup's LDS once its waves are gone.
     wait_counts<0, 0>();
 }

@@ -116,28 +116,24 @@ struct Valu128x128x8 {
         }
     }
 
-    __device__ __forceinline__ void store_partial(float *p) {
+    // The same mapping into a dense row-major BM x BN tile (a split tile's
+    // partial sum).
+    __device__ __forceinline__ void store_tile(float *p) {
         const int tid = threadIdx.x;
+        const int tx = tid & 15, ty = tid >> 4;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p[(i * 8 + j) * NT + tid] = acc[i][j];
-    }
-
-    __device__ __forceinline__ void add_partial(const float *p) {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] += p[(i * 8 + j) * NT + tid];
+        for (int i = 0; i < 8; ++i) {
+            float *q = p + (i < 4 ? ty * 4 + i : 64 + ty * 4 + (i - 4)) * BN + tx * 4;
+            *(f32x4 *)q = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+            *(f32x4 *)(q + 64) = f32x4{acc[i][4], acc[i][5], acc[i][6], acc[i][7]};
+        }
     }
 };
 
 template <bool SPLIT>
 __global__ __launch_bounds__(Valu128x128x8::NT) void sgemm_valu_kernel(KernelArgs a) {
     __shared__ __attribute__((aligned(16))) float lds[Valu128x128x8::LDS_FLOATS];
-    __shared__ int flag;
-    run_gemm<Valu128x128x8, SPLIT>(a, lds, &flag);
+    run_gemm<Valu128x128x8, SPLIT>(a, lds);
 }
 
 hipError_t launch_valu(int cfg, const KernelArgs &a, hipStream_t s) {

@@ -18,6 +18,9 @@ hipError_t launch_generic(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t occupancy_generic(int cfg, int *wg_per_cu);
 hipError_t launch_valu(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t occupancy_valu(int cfg, int *wg_per_cu);
+// Sum of the split tiles of a Stream-K launch (tile bm x bn) into C; after
+// the GEMM kernel on the same stream.
+hipError_t launch_sk_fixup(const KernelArgs &a, int bm, int bn, hipStream_t s);
 hipError_t launch_scale_c(float *C, int M, int N, int64_t ldc, float beta, hipStream_t s);
 // dst (drows x dcols, leading dimension ldd) = src (rows x cols, lds) with
 // zeros outside it.

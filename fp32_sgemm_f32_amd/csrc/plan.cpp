@@ -45,8 +45,7 @@ static_assert(sizeof(kCfgs) / sizeof(kCfgs[0]) == SGEMM_NUM_CFGS, "config table 
 
 int64_t workspace_bytes(int grid, int sk_tiles, int bm, int bn) {
     if (sk_tiles <= 0) return 0;
-    int64_t counters = ((int64_t)sk_tiles * 4 + 255) / 256 * 256;
-    return counters + (int64_t)grid * 2 * bm * bn * 4;
+    return (int64_t)grid * 2 * bm * bn * 4;
 }
 
 static bool divides(const CfgInfo &c, int M, int N, int K) {
@@ -201,8 +200,6 @@ int make_plan(const PlanRequest &req, Plan *out) {
     if (run < 1) run = 1;
     p.group_m = pick_group_m(p.tiles_m > 0 ? p.tiles_m : 1, run);
     p.workspace_bytes = workspace_bytes(p.sk_grid, p.sk_tiles, p.bm, p.bn);
-    p.counters_offset = 0;
-    p.partials_offset = p.sk_tiles > 0 ? ((int64_t)p.sk_tiles * 4 + 255) / 256 * 256 : 0;
     *out = p;
     return SGEMM_OK;
 }

@@ -59,7 +59,6 @@ struct Plan {
     int edge;            // the shape is not a multiple of the tile: masked loads and stores
     int64_t sk_iters;
     int64_t workspace_bytes;
-    int64_t counters_offset, partials_offset;   // within the workspace
 };
 
 // Returns an SGEMM_* status; fills *out on success.
@@ -77,9 +76,9 @@ bool dl_offsets_fit(int cfg, bool edge, int64_t lda, int64_t ldb, bool trans_a =
 // for those).
 int staged_equivalent(int cfg);
 
-// Workspace layout for Stream-K: sk_tiles int counters (256-byte aligned
-// block), then sk_grid * 2 partial tiles of bm*bn floats (a split workgroup
-// leaves a partial for at most two tiles: the first and the last it touches).
+// Workspace of a Stream-K launch: sk_grid * 2 partial tiles of bm*bn floats
+// (a split workgroup leaves a partial for at most two tiles: the first and
+// the last it touches).
 int64_t workspace_bytes(int grid, int sk_tiles, int bm, int bn);
 
 }  // namespace sgemm

@@ -33,8 +33,6 @@ struct DeviceInfo {
 };
 
 struct Workspace {
-    int *counters = nullptr;
-    int64_t ncounters = 0;
     float *partials = nullptr;
     int64_t partial_bytes = 0;
     float *pack = nullptr;         // repacked operands (see run_packed)
@@ -174,33 +172,20 @@ bool vector_layout(const Call &c) {
            ((uintptr_t)c.C & 15) == 0;
 }
 
-// Stream-K workspace of (dev, stream), grown to hold `plan`.  Counters are
-// zeroed when allocated and left at zero by every call.  Caller holds g_mu.
+// Stream-K workspace of (dev, stream), grown to hold `plan`'s partial
+// tiles.  Caller holds g_mu.
 int workspace_for(int dev, hipStream_t s, const Plan &p, Workspace *out) {
     Workspace &w = g_workspaces[{dev, s}];
-    const int64_t need_part = (int64_t)p.sk_grid * 2 * p.bm * p.bn * 4;
-    if (w.ncounters < p.sk_tiles || w.partial_bytes < need_part) {
-        hipError_t e = hipStreamSynchronize(s);   // old buffers may still be in use
+    const int64_t need_part = p.workspace_bytes;
+    if (w.partial_bytes < need_part) {
+        hipError_t e = hipStreamSynchronize(s);   // the old buffer may still be in use
         if (e != hipSuccess) return hip_fail(e);
-        if (w.ncounters < p.sk_tiles) {
-            if (w.counters) (void)hipFree(w.counters);
-            w.counters = nullptr;
-            w.ncounters = 0;
-            int64_t n = p.sk_tiles < 4096 ? 4096 : p.sk_tiles;
-            e = hipMalloc((void **)&w.counters, (size_t)n * 4);
-            if (e != hipSuccess) return hip_fail(e);
-            e = hipMemsetAsync(w.counters, 0, (size_t)n * 4, s);
-            if (e != hipSuccess) return hip_fail(e);
-            w.ncounters = n;
-        }
-        if (w.partial_bytes < need_part) {
-            if (w.partials) (void)hipFree(w.partials);
-            w.partials = nullptr;
-            w.partial_bytes = 0;
-            e = hipMalloc((void **)&w.partials, (size_t)need_part);
-            if (e != hipSuccess) return hip_fail(e);
-            w.partial_bytes = need_part;
-        }
+        if (w.partials) (void)hipFree(w.partials);
+        w.partials = nullptr;
+        w.partial_bytes = 0;
+        e = hipMalloc((void **)&w.partials, (size_t)need_part);
+        if (e != hipSuccess) return hip_fail(e);
+        w.partial_bytes = need_part;
     }
     *out = w;
     return SGEMM_OK;
@@ -349,9 +334,9 @@ int run(const Call &c) {
         std::lock_guard<std::mutex> lock(g_mu);
         Workspace w;
         if ((st = workspace_for(dev, c.stream, p, &w)) != SGEMM_OK) return st;
-        a.counters = w.counters;
         a.partials = w.partials;
         e = launch_cfg(p.config, a, c.stream);
+        if (e == hipSuccess) e = launch_sk_fixup(a, p.bm, p.bn, c.stream);
     } else {
         e = launch_cfg(p.config, a, c.stream);
     }
@@ -466,7 +451,6 @@ SGEMM_API int sgemm_f32_release(void) {
     std::lock_guard<std::mutex> lock(sgemm::g_mu);
     int st = SGEMM_OK;
     for (auto &kv : sgemm::g_workspaces) {
-        if (kv.second.counters && hipFree(kv.second.counters) != hipSuccess) st = SGEMM_ERR_HIP;
         if (kv.second.partials && hipFree(kv.second.partials) != hipSuccess) st = SGEMM_ERR_HIP;
         if (kv.second.pack && hipFree(kv.second.pack) != hipSuccess) st = SGEMM_ERR_HIP;
     }

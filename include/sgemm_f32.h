@@ -48,12 +48,13 @@
  *   C is untouched.  Return values are the SGEMM_* status codes below.
  *
  * Workspace
- *   Split-K ("Stream-K") schedules keep partial tiles and per-tile arrival
- *   counters in a workspace owned by the library, one per (device, stream),
- *   grown on demand with hipMalloc and kept until sgemm_f32_release() or
- *   process exit.  Repacked calls (see above) keep their copies in a
- *   buffer of the same (device, stream), held and freed the same way.
- *   Calls on different streams therefore never share one.
+ *   Split-K ("Stream-K") schedules keep partial tiles in a workspace owned
+ *   by the library, one per (device, stream), grown on demand with
+ *   hipMalloc and kept until sgemm_f32_release() or process exit; a second
+ *   kernel, enqueued on the same stream right after the GEMM kernel, adds
+ *   them into C.  Repacked calls (see above) keep their copies in a buffer
+ *   of the same (device, stream), held and freed the same way.  Calls on
+ *   different streams therefore never share one.
  *   Calls that run concurrently on the SAME stream are impossible by stream
  *   order; calls from several host threads on one stream are serialised by
  *   the stream as well.

@@ -426,8 +426,8 @@ def test_non_default_stream(dev):
 
 def test_concurrent_streams_with_split_tiles(dev):
     """Stream-K calls on two streams with no host synchronisation between
-    them: each stream has its own workspace, so the partial tiles and
-    arrival counters of one never meet the other's (integer inputs: every
+    them: each stream has its own workspace, so the partial tiles of one
+    never meet the other's (integer inputs: every
     result exact, every repeat identical)."""
     import torch
     log("case two streams, Stream-K")

@@ -97,3 +97,14 @@ def test_mfma_loops_hold_no_vector_alu(dl_asm):
                 bad.append((name[:90], label.split(":")[0], valu[:4]))
     assert checked > 100
     assert not bad, "vector ALU in MFMA loop blocks: " + repr(bad[:6])
+
+
+def test_no_kernel_spills_to_scratch(dl_asm):
+    """Every direct-to-LDS kernel, split (Stream-K) instances included, keeps
+    its state in registers: a private segment would mean spills to scratch
+    memory."""
+    descriptors = re.findall(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", dl_asm, re.S)
+    assert len(descriptors) == 2 * (9 + 4 * 3 + 4 * 4)
+    for name, body in descriptors:
+        m = re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", body)
+        assert m and m.group(1) == "0", f"{name}: private segment {m and m.group(1)}"
