@@ -92,8 +92,11 @@ static int64_t tiles_of(int cfg, int M, int N) {
 //   * else 128x128x32 tiles when they fill whole waves (140 at 2048^3,
 //     143 at 2048x4096x2048);
 //   * else 64x64 tiles (146 at 1024x1024x16384, 106 at 1024^3, 141 at
-//     3072^3, where 128x128 tiles leave a part wave: 137), with a 64-deep
-//     K chunk where K allows.
+//     3072^3, where 128x128 tiles leave a part wave: 137), with 64-deep K
+//     chunks unless 32-deep ones need one chunk fewer in pairs, i.e. an odd
+//     number of 32-deep chunks (the last 64-deep chunk would then be at most
+//     half used: 1292^3 runs at 96 TFLOP/s with 32-deep chunks, 90 with
+//     64-deep ones).
 // Layouts the vector kernels cannot load go to the general kernel.
 static int auto_config(int M, int N, int K, int cus, bool aligned) {
     if (!aligned) return SGEMM_CFG_GENERIC_64x64x16;
@@ -102,8 +105,7 @@ static int auto_config(int M, int N, int K, int cus, bool aligned) {
     if (tiles_of(big, M, N) >= cus) return big;
     const int64_t mid_tiles = tiles_of(mid, M, N);
     if (mid_tiles >= cus && mid_tiles % cus == 0) return mid;
-    if (K % 64 == 0 || K % 32 != 0) return small;
-    return small32;
+    return ((K + 31) / 32) % 2 == 1 ? small32 : small;
 }
 
 int staged_equivalent(int cfg) {
@@ -161,6 +163,8 @@ int make_plan(const PlanRequest &req, Plan *out) {
     if (sched == SGEMM_SCHED_AUTO) {
         if (tiles >= cus && tiles % cus == 0) sched = SGEMM_SCHED_DP;
         else if (tiles < cus && p.ipt < 2 * kMinSkIters) sched = SGEMM_SCHED_DP;  // too short to split
+        else if (tiles > cus && tiles <= (int64_t)occ * cus && 100 * (int64_t)tiles >= 85 * (int64_t)occ * cus)
+            sched = SGEMM_SCHED_DP;   // one resident wave, nearly full: every tile runs at once
         else sched = SGEMM_SCHED_STREAMK;
     }
 
@@ -175,6 +179,21 @@ int make_plan(const PlanRequest &req, Plan *out) {
         // contiguous run of at least kMinSkIters (tile, K chunk) steps when
         // there are that many.
         int dp = req.sched == SGEMM_SCHED_STREAMK ? 0 : (tiles / cap) * cap;
+        if (dp == cap) {
+            // One full wave and a remainder: split everything instead when
+            // that ends sooner.  The remainder alone spreads over at most
+            // (its steps / kMinSkIters) workgroups, so with few K chunks per
+            // tile its split part can take longer than the whole product
+            // spread over the full grid (64x64 tiles at 1024x1028x2048: 94
+            // TFLOP/s split whole against 89).
+            const int64_t rest = (int64_t)(tiles - dp) * p.ipt;
+            int64_t g = rest / kMinSkIters;
+            if (g > cap) g = cap;
+            if (g < 1) g = 1;
+            const int64_t hybrid = p.ipt + (rest + g - 1) / g;
+            const int64_t whole = ((int64_t)tiles * p.ipt + cap - 1) / cap;
+            if (whole < hybrid) dp = 0;
+        }
         p.dp_tiles = dp;
         p.sk_tiles = tiles - dp;
         int64_t sk_iters = (int64_t)p.sk_tiles * p.ipt;

@@ -200,6 +200,19 @@ def test_auto_choices_on_256_cus():
     assert p["config"] == sg.CFG_DL_64x64x32
     p = sg.plan(256, 256, 256, num_cus=256, occupancy=occ)
     assert p["config"] == sg.CFG_DL_64x64x64
+    # 41 chunks of 32 (odd): 32-deep chunks; 441 tiles fill 86% of the 512
+    # resident slots, so every tile runs at once, data-parallel.
+    p = sg.plan(1292, 1292, 1292, num_cus=256, occupancy=occ)
+    assert (p["config"], p["sched"], p["grid"]) == (sg.CFG_DL_64x64x32, sg.SCHED_DP, 441)
+    # One full wave of 64x64 tiles and 16 more, 32 chunks each: the
+    # remainder alone would spread over only 64 workgroups, so every tile is
+    # split over the full grid instead.
+    p = sg.plan(1024, 1028, 2048, num_cus=256, occupancy=occ)
+    assert (p["config"], p["dp_tiles"], p["sk_tiles"], p["sk_grid"]) == (sg.CFG_DL_64x64x64, 0, 272, 256)
+    # With 256 chunks per tile the remainder spreads over the whole grid:
+    # one wave of whole tiles, then the 16 split.
+    p = sg.plan(4096, 4100, 4096, num_cus=256, occupancy=occ)
+    assert (p["config"], p["dp_tiles"], p["sk_tiles"], p["sk_grid"]) == (sg.CFG_DL_256x256x16, 256, 16, 256)
     # Ragged shapes: the edge-masking kernels of the same regimes, or the
     # general kernel when N or K is not a multiple of 4.
     p = sg.plan(4000, 4000, 4000, num_cus=256, occupancy=occ)
