@@ -20,6 +20,9 @@ struct KernelArgs {
     float *C;
     int lda, ldb, ldc;      // leading dimensions in elements (the API takes int)
     int M, N, K;      // the shape (the edge-masking kernels need it)
+    int cm, cn;       // rows and columns of C to store (M, N unless the
+                      // operands were padded beyond C: then C's own)
+    int c_scalar;     // C's layout rules out vector stores (edge kernels)
     int edge;         // the shape is not a multiple of the tile
     int trans_a;      // A stored K x M (op(A) = A^T); else M x K
     int trans_b;      // B stored N x K (op(B) = B^T); else K x N
@@ -165,7 +168,7 @@ __device__ __forceinline__ void sk_fixup(const KernelArgs &a) {
         int tm, tn;
         tile_coords(a, a.dp_tiles + tl, tm, tn);
         const int row = tm * BM + e / BN, col = tn * BN + e % BN;
-        if (row >= a.M || col >= a.N) continue;
+        if (row >= a.cm || col >= a.cn) continue;
         f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int c0 = first; c0 <= last; c0 += 8) {
             f32x4 v[8];
@@ -180,7 +183,7 @@ __device__ __forceinline__ void sk_fixup(const KernelArgs &a) {
         float *p = a.C + (int64_t)row * a.ldc + col;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            if (col + u < a.N) p[u] = epilogue(a, sum[u], p + u);
+            if (col + u < a.cn) p[u] = epilogue(a, sum[u], p + u);
     }
 }
 

@@ -117,12 +117,12 @@ struct GenericCore {
         const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
         const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
         const int col = tn * BN + wn * 32 + lr;
-        if (col >= a.N) return;
+        if (col >= a.cn) return;
         const int row0 = tm * BM + wm * 32 + 4 * lh;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = row0 + 8 * (r >> 2) + (r & 3);
-            if (row < a.M) {
+            if (row < a.cm) {
                 float *p = a.C + (int64_t)row * a.ldc + col;
                 *p = epilogue(a, acc[r], p);
             }

@@ -641,15 +641,32 @@ struct MfmaDlCore {
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
         const int lr = lane & 31, lh = lane >> 5;
         const int row0 = tm * BM + wm * WTM + (AKC ? 4 : 4 * FM) * lh, col0 = tn * BN + wn * WTN + FN * lr;
-        if (EDGE && col0 >= a.N) return;
+        if (EDGE && col0 >= a.cn) return;
         float *c = a.C + (int64_t)row0 * a.ldc + col0;
+        if (EDGE && a.c_scalar) {
+            // C with a leading dimension or base off the vector grid, or
+            // columns that end inside a lane's group: one float at a time.
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rho = 8 * (r >> 2) + (r & 3);
+                    const int dr = AKC ? i * 32 + rho : FM * rho + i;
+                    if (row0 + dr >= a.cm) continue;
+                    float *p = c + (int64_t)dr * a.ldc;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        if (col0 + j < a.cn) p[j] = epilogue(a, acc[i][j][r], p + j);
+                }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rho = 8 * (r >> 2) + (r & 3);
                 const int dr = AKC ? i * 32 + rho : FM * rho + i;
-                if (EDGE && row0 + dr >= a.M) continue;
+                if (EDGE && row0 + dr >= a.cm) continue;
                 float *p = c + (int64_t)dr * a.ldc;
                 if constexpr (FN == 1) {
                     *p = epilogue(a, acc[i][0][r], p);

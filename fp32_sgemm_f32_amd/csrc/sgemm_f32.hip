@@ -136,8 +136,12 @@ struct Call {
     hipStream_t stream;
     int config, sched;
     int repacked = 0;              // already laid out for the vector kernels by run_packed
+    int cm = 0, cn = 0;            // C's rows and columns when the operands were padded
+                                   // beyond them (run_packed); 0: M and N
 
-    // Rows and columns of A and B as stored.
+    // Rows and columns of C, and of A and B as stored.
+    int c_rows() const { return cm ? cm : M; }
+    int c_cols() const { return cn ? cn : N; }
     int a_rows() const { return ta ? K : M; }
     int a_cols() const { return ta ? M : K; }
     int b_rows() const { return tb ? N : K; }
@@ -153,10 +157,10 @@ int check_args(const Call &c) {
     const bool ab = c.reads_ab();
     // A and B (and their leading dimensions) are not read when the product
     // does not contribute.
-    if (c.ldc < c.N || (ab && (c.lda < c.a_cols() || c.ldb < c.b_cols()))) return SGEMM_ERR_LD;
+    if (c.ldc < c.c_cols() || (ab && (c.lda < c.a_cols() || c.ldb < c.b_cols()))) return SGEMM_ERR_LD;
     if (!c.C || (ab && (!c.A || !c.B))) return SGEMM_ERR_NULL;
     if (((uintptr_t)c.C & 3) || (ab && (((uintptr_t)c.A & 3) || ((uintptr_t)c.B & 3)))) return SGEMM_ERR_ALIGN;
-    const int64_t nc = extent_bytes(c.M, c.N, c.ldc);
+    const int64_t nc = extent_bytes(c.c_rows(), c.c_cols(), c.ldc);
     if (ab && (overlap(c.C, nc, c.A, extent_bytes(c.a_rows(), c.a_cols(), c.lda)) ||
                overlap(c.C, nc, c.B, extent_bytes(c.b_rows(), c.b_cols(), c.ldb))))
         return SGEMM_ERR_ALIAS;
@@ -165,12 +169,18 @@ int check_args(const Call &c) {
 
 // The layout the vector (16-byte) kernels need: the contiguous extent and
 // the leading dimension of every operand a multiple of 4, and 16-byte
-// aligned operands; anything else runs on the general kernel.
-bool vector_layout(const Call &c) {
+// aligned operands; anything else runs on the general kernel.  Loads (A, B
+// and N, the column count the tiles cover) and C stores separately.
+bool vector_ab(const Call &c) {
     return (c.a_cols() & 3) == 0 && (c.b_cols() & 3) == 0 && (c.N & 3) == 0 && (c.lda & 3) == 0 &&
-           (c.ldb & 3) == 0 && (c.ldc & 3) == 0 && ((uintptr_t)c.A & 15) == 0 && ((uintptr_t)c.B & 15) == 0 &&
-           ((uintptr_t)c.C & 15) == 0;
+           (c.ldb & 3) == 0 && ((uintptr_t)c.A & 15) == 0 && ((uintptr_t)c.B & 15) == 0;
 }
+
+bool vector_c(const Call &c) {
+    return (c.c_cols() & 3) == 0 && (c.ldc & 3) == 0 && ((uintptr_t)c.C & 15) == 0;
+}
+
+bool vector_layout(const Call &c) { return vector_ab(c) && vector_c(c); }
 
 // Stream-K workspace of (dev, stream), grown to hold `plan`'s partial
 // tiles.  Caller holds g_mu.
@@ -229,45 +239,39 @@ bool worth_repacking(const Call &c) {
 }
 
 // The same product on copies laid out for the vector kernels: every stored
-// row length (and N) padded to a multiple of 4 with zeros, 16-byte aligned
-// rows; the padded k terms are 0 * 0.  A, B are copied only when their own
-// layout does not already qualify; C is computed in a padded copy (holding
-// C's values when beta reads them) and its M x N part copied back.  All on
-// the caller's stream, in the library's per-stream repacking buffer.
+// row length of A and B (and N, and M when A is stored K x M) padded to a
+// multiple of 4 with zeros, 16-byte aligned rows; the padded k terms are
+// 0 * 0.  A, B are copied only when their own layout does not already
+// qualify.  C is written in place: the kernels store only its own rows and
+// columns (one float at a time when its layout rules out vector stores), so
+// it is neither copied in nor back.  All on the caller's stream, in the
+// library's per-stream repacking buffer.
 int run_packed(const Call &c, int dev) {
     const int Mp = c.ta ? up4(c.M) : c.M, Np = up4(c.N), Kp = up4(c.K);
     const int ar = c.ta ? Kp : Mp, ac = c.ta ? Mp : Kp;     // A as stored, padded
     const int br = c.tb ? Np : Kp, bc = c.tb ? Kp : Np;
     const bool pa = !(aligned16(c.A) && (c.lda & 3) == 0 && c.a_rows() == ar && c.a_cols() == ac);
     const bool pb = !(aligned16(c.B) && (c.ldb & 3) == 0 && c.b_rows() == br && c.b_cols() == bc);
-    const bool pc = !(aligned16(c.C) && (c.ldc & 3) == 0 && Mp == c.M && Np == c.N);
     auto round256 = [](int64_t b) { return (b + 255) / 256 * 256; };
     const int64_t a_bytes = pa ? round256((int64_t)ar * ac * 4) : 0;
     const int64_t b_bytes = pb ? round256((int64_t)br * bc * 4) : 0;
-    const int64_t c_bytes = pc ? round256((int64_t)Mp * Np * 4) : 0;
     float *buf = nullptr;
-    int st = pack_space_for(dev, c.stream, a_bytes + b_bytes + c_bytes, &buf);
-    if (st != SGEMM_OK) return st;
-    float *Ap = buf, *Bp = (float *)((char *)buf + a_bytes), *Cp = (float *)((char *)buf + a_bytes + b_bytes);
+    int st = SGEMM_OK;
+    if (a_bytes + b_bytes > 0 && (st = pack_space_for(dev, c.stream, a_bytes + b_bytes, &buf)) != SGEMM_OK)
+        return st;
+    float *Ap = buf, *Bp = (float *)((char *)buf + a_bytes);
     hipError_t e = hipSuccess;
     if (pa) e = launch_pack(c.A, c.lda, c.a_rows(), c.a_cols(), Ap, ac, ar, ac, c.stream);
     if (e == hipSuccess && pb) e = launch_pack(c.B, c.ldb, c.b_rows(), c.b_cols(), Bp, bc, br, bc, c.stream);
-    if (e == hipSuccess && pc && c.scaled && c.beta != 0.0f)
-        e = launch_pack(c.C, c.ldc, c.M, c.N, Cp, Np, Mp, Np, c.stream);
     if (e != hipSuccess) return hip_fail(e);
 
     Call q = c;
     q.M = Mp; q.N = Np; q.K = Kp;
     if (pa) { q.A = Ap; q.lda = ac; }
     if (pb) { q.B = Bp; q.ldb = bc; }
-    if (pc) { q.C = Cp; q.ldc = Np; }
+    if (Mp != c.M || Np != c.N || !vector_c(c)) { q.cm = c.M; q.cn = c.N; }
     q.repacked = 1;
-    if ((st = run(q)) != SGEMM_OK) return st;
-    if (pc) {
-        e = launch_pack(Cp, Np, c.M, c.N, c.C, c.ldc, c.M, c.N, c.stream);
-        if (e != hipSuccess) return hip_fail(e);
-    }
-    return SGEMM_OK;
+    return run(q);
 }
 
 int run(const Call &c) {
@@ -280,7 +284,7 @@ int run(const Call &c) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e);
-    if ((st = check_device_range(c.C, extent_bytes(c.M, c.N, c.ldc), dev)) != SGEMM_OK) return st;
+    if ((st = check_device_range(c.C, extent_bytes(c.c_rows(), c.c_cols(), c.ldc), dev)) != SGEMM_OK) return st;
     if (c.reads_ab()) {
         if ((st = check_device_range(c.A, extent_bytes(c.a_rows(), c.a_cols(), c.lda), dev)) != SGEMM_OK) return st;
         if ((st = check_device_range(c.B, extent_bytes(c.b_rows(), c.b_cols(), c.ldb), dev)) != SGEMM_OK) return st;
@@ -289,12 +293,17 @@ int run(const Call &c) {
     if (!c.repacked && c.config == SGEMM_CFG_AUTO && c.reads_ab() && !vector_layout(c) && worth_repacking(c))
         return run_packed(c, dev);
 
+    // C written in place beyond padded operands (run_packed): the edge
+    // variants store only C's own rows and columns.
+    const bool c_own = c.cm != 0 || c.cn != 0;
     DeviceInfo info;
     if ((st = device_info(dev, &info)) != SGEMM_OK) return st;
     PlanRequest req{c.M, c.N, c.K, c.config, c.sched, info.num_cus, info.occupancy,
-                    env_int("SGEMM_F32_SK_WG_PER_CU", 0), vector_layout(c) ? 1 : 0, c.ta, c.tb};
+                    env_int("SGEMM_F32_SK_WG_PER_CU", 0), vector_ab(c) && (c_own || vector_c(c)) ? 1 : 0,
+                    c.ta, c.tb};
     Plan p;
     if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
+    if (c_own) p.edge = 1;
     if (c.K > 0 && !dl_offsets_fit(p.config, p.edge != 0, c.lda, c.ldb, c.ta != 0, c.tb != 0)) {
         // Leading dimensions too large for the 32-bit source offsets of the
         // direct-to-LDS kernels: an automatic choice falls back to the
@@ -316,6 +325,8 @@ int run(const Call &c) {
     a.A = c.A; a.B = c.B; a.C = c.C;
     a.lda = c.lda; a.ldb = c.ldb; a.ldc = c.ldc;
     a.M = c.M; a.N = c.N; a.K = c.K;
+    a.cm = c.c_rows(); a.cn = c.c_cols();
+    a.c_scalar = c_own && !vector_c(c) ? 1 : 0;
     a.edge = p.edge;
     a.trans_a = c.ta; a.trans_b = c.tb;
     a.scaled = c.scaled && !(c.alpha == 1.0f && c.beta == 0.0f);

@@ -24,10 +24,11 @@
  *   where the shape is not a multiple of the tile).  Any other layout runs
  *   on a general kernel with element-wise bounds checks, except that with
  *   the automatic configuration, M, N, K >= 64 and M * N * K at least 2^25,
- *   A and B (and C, when its own layout does not qualify) are first copied
- *   on `stream` into zero-padded aligned buffers of the library and the
- *   product runs on the vector kernels (results as unpadded; C's padding
- *   is still untouched).
+ *   A and B are first copied on `stream` into zero-padded aligned buffers
+ *   of the library (each only when its own layout does not qualify) and the
+ *   product runs on the vector kernels, which then write C in place (one
+ *   float at a time when C's layout does not qualify; results as unpadded,
+ *   C's padding untouched).
  *
  * Memory and ownership
  *   A, B, C are device pointers, caller-owned, allocated on the HIP device

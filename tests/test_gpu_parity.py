@@ -737,9 +737,9 @@ def test_python_binding_takes_transposed_views(dev, views):
 
 
 # Large products whose layout the vector kernels cannot load are run on
-# zero-padded aligned copies (automatic choice only): odd N, odd K, odd M
-# with A stored K x M, a float-offset pointer, odd leading dimensions, and
-# beta != 0 (C copied in and back).  Each above the size from which the
+# zero-padded aligned copies of A and B (automatic choice only), C written
+# in place: odd N, odd K, odd M with A stored K x M, a float-offset pointer,
+# odd leading dimensions, beta != 0, and C alone off the vector grid.  Each above the size from which the
 # copies pay (2^25 multiply-adds).
 REPACK_CASES = {
     # name: (ta, tb, M, N, K, pads (A, B, C), offsets (A, B, C), alpha, beta)
@@ -750,6 +750,9 @@ REPACK_CASES = {
     "tt_odd_all": (1, 1, 1237, 1113, 1601, (0, 0, 0), (0, 0, 0), 1.0, 0.0),
     "a_offset": (0, 0, 1280, 1280, 1408, (0, 0, 0), (1, 0, 0), 1.0, 0.0),
     "odd_ld_beta": (0, 0, 1280, 1283, 1344, (3, 1, 5), (0, 2, 1), 1.5, -2.0),
+    # Only C off the vector grid: nothing copied, C stored one float at a time.
+    "c_offset_beta": (0, 0, 1024, 1024, 1024, (0, 0, 0), (0, 0, 1), 1.0, 1.0),
+    "tt_c_odd_ld": (1, 1, 1024, 1024, 1024, (0, 0, 3), (0, 0, 0), -1.0, 0.5),
 }
 
 
