@@ -22,9 +22,17 @@ hipError_t occupancy_valu(int cfg, int *wg_per_cu);
 // the GEMM kernel on the same stream.
 hipError_t launch_sk_fixup(const KernelArgs &a, int bm, int bn, hipStream_t s);
 hipError_t launch_scale_c(float *C, int M, int N, int64_t ldc, float beta, hipStream_t s);
-// dst (drows x dcols, leading dimension ldd) = src (rows x cols, lds) with
-// zeros outside it.
-hipError_t launch_pack(const float *src, int64_t lds, int rows, int cols, float *dst, int64_t ldd, int drows,
-                       int dcols, hipStream_t s);
+// One copy of a repacking launch: dst (drows x dcols, leading dimension
+// ldd) = src (rows x cols, leading dimension lds) with zeros outside it.
+struct PackJob {
+    const float *src;
+    int64_t lds;
+    int rows, cols;
+    float *dst;
+    int64_t ldd;
+    int drows, dcols;
+};
+// Up to two copies in one launch (jobs with no rows or columns skipped).
+hipError_t launch_pack(const PackJob *jobs, int njobs, hipStream_t s);
 
 }  // namespace sgemm

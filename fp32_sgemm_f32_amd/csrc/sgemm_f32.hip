@@ -260,9 +260,11 @@ int run_packed(const Call &c, int dev) {
     if (a_bytes + b_bytes > 0 && (st = pack_space_for(dev, c.stream, a_bytes + b_bytes, &buf)) != SGEMM_OK)
         return st;
     float *Ap = buf, *Bp = (float *)((char *)buf + a_bytes);
-    hipError_t e = hipSuccess;
-    if (pa) e = launch_pack(c.A, c.lda, c.a_rows(), c.a_cols(), Ap, ac, ar, ac, c.stream);
-    if (e == hipSuccess && pb) e = launch_pack(c.B, c.ldb, c.b_rows(), c.b_cols(), Bp, bc, br, bc, c.stream);
+    PackJob jobs[2];
+    int njobs = 0;
+    if (pa) jobs[njobs++] = PackJob{c.A, c.lda, c.a_rows(), c.a_cols(), Ap, ac, ar, ac};
+    if (pb) jobs[njobs++] = PackJob{c.B, c.ldb, c.b_rows(), c.b_cols(), Bp, bc, br, bc};
+    const hipError_t e = launch_pack(jobs, njobs, c.stream);
     if (e != hipSuccess) return hip_fail(e);
 
     Call q = c;
