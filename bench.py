@@ -44,7 +44,7 @@ PAGES_4096_TFLOPS = 49.8
 # kernel sources they were taken on (digest below); otherwise reported null.
 TRAFFIC = {
     "kernel": "dl_256x256x16", "workload": "sgemm_4096",
-    "source_digest": "c90813722fa96a12",
+    "source_digest": "c901998312e62bc7",
     "bytes": 469864950,
 }
 KERNEL_SOURCES = ("fp32_sgemm_f32_amd/csrc/gemm_mfma_dl.hip", "fp32_sgemm_f32_amd/csrc/gemm_common.h")
