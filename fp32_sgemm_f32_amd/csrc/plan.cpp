@@ -84,6 +84,13 @@ static int64_t tiles_of(int cfg, int M, int N) {
     return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
+// The tiles of `cfg` cover M x N with at least 90% of their area inside it
+// (a side much narrower than the tile wastes the rest of every tile).
+static bool covers_well(int cfg, int M, int N) {
+    const int64_t area = tiles_of(cfg, M, N) * kCfgs[cfg].bm * kCfgs[cfg].bn;
+    return 10 * (int64_t)M * N >= 9 * area;
+}
+
 // Automatic choice, from timings of the configurations on MI355X (256 CUs;
 // all direct-to-LDS, every storage order):
 //   * 256x256x16 tiles (8 waves) when every CU gets at least one (149
@@ -91,21 +98,29 @@ static int64_t tiles_of(int cfg, int M, int N) {
 //     same tile measured 0-5% slower);
 //   * else 128x128x32 tiles when they fill whole waves (140 at 2048^3,
 //     143 at 2048x4096x2048);
+//     either only when the tiles lie at least 90% inside C (65536x128x2048
+//     on 256x256 tiles, half of each outside: 74, on 128x128 tiles: 139);
 //   * else 64x64 tiles (146 at 1024x1024x16384, 106 at 1024^3, 141 at
 //     3072^3, where 128x128 tiles leave a part wave: 137), with 64-deep K
 //     chunks unless 32-deep ones need one chunk fewer in pairs, i.e. an odd
 //     number of 32-deep chunks (the last 64-deep chunk would then be at most
 //     half used: 1292^3 runs at 96 TFLOP/s with 32-deep chunks, 90 with
-//     64-deep ones).
+//     64-deep ones), or C is narrow (at most 8 tiles across one side) with
+//     at least two waves of tiles: the 32-deep kernel fits two workgroups
+//     per CU and keeps twice the loads in flight, which such shapes, with
+//     little reuse of the long operand, need (131072x64x1024: 114 against
+//     105; 8192x384x4096: 144 against 140).
 // Layouts the vector kernels cannot load go to the general kernel.
 static int auto_config(int M, int N, int K, int cus, bool aligned) {
     if (!aligned) return SGEMM_CFG_GENERIC_64x64x16;
     const int big = SGEMM_CFG_DL_256x256x16, mid = SGEMM_CFG_DL_128x128x32, small = SGEMM_CFG_DL_64x64x64,
               small32 = SGEMM_CFG_DL_64x64x32;
-    if (tiles_of(big, M, N) >= cus) return big;
+    if (tiles_of(big, M, N) >= cus && covers_well(big, M, N)) return big;
     const int64_t mid_tiles = tiles_of(mid, M, N);
-    if (mid_tiles >= cus && mid_tiles % cus == 0) return mid;
-    return ((K + 31) / 32) % 2 == 1 ? small32 : small;
+    if (mid_tiles >= cus && mid_tiles % cus == 0 && covers_well(mid, M, N)) return mid;
+    const int small_m = (M + 63) / 64, small_n = (N + 63) / 64;
+    const bool narrow = (small_m <= 8 || small_n <= 8) && tiles_of(small, M, N) >= 2 * (int64_t)cus;
+    return ((K + 31) / 32) % 2 == 1 || narrow ? small32 : small;
 }
 
 int staged_equivalent(int cfg) {
@@ -218,6 +233,12 @@ int make_plan(const PlanRequest &req, Plan *out) {
     int run = p.xcd_remap ? p.grid / 8 : p.grid;
     if (run < 1) run = 1;
     p.group_m = pick_group_m(p.tiles_m > 0 ? p.tiles_m : 1, run);
+    // A narrow C: few tile columns and a B that fits one XCD's L2 (4 MiB)
+    // go row by row, so the tiles that share an A panel run side by side
+    // and A streams through once (49152x192x4096: 139 TFLOP/s against 134
+    // with 16-row groups); few tile rows and a small A, column by column.
+    if (p.tiles_n <= 8 && (int64_t)K * N * 4 <= ((int64_t)4 << 20)) p.group_m = 1;
+    else if (p.tiles_m <= 8 && (int64_t)M * K * 4 <= ((int64_t)4 << 20)) p.group_m = p.tiles_m > 0 ? p.tiles_m : 1;
     p.workspace_bytes = workspace_bytes(p.sk_grid, p.sk_tiles, p.bm, p.bn);
     *out = p;
     return SGEMM_OK;

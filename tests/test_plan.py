@@ -213,6 +213,24 @@ def test_auto_choices_on_256_cus():
     # one wave of whole tiles, then the 16 split.
     p = sg.plan(4096, 4100, 4096, num_cus=256, occupancy=occ)
     assert (p["config"], p["dp_tiles"], p["sk_tiles"], p["sk_grid"]) == (sg.CFG_DL_256x256x16, 256, 16, 256)
+    # A side much narrower than the tile: tiles at most half inside C are
+    # passed over for ones that fit (256 columns of 128: 128x128 tiles).
+    p = sg.plan(65536, 128, 2048, num_cus=256, occupancy=occ)
+    assert (p["config"], p["sched"], p["tiles_m"], p["tiles_n"]) == (sg.CFG_DL_128x128x32, sg.SCHED_DP, 512, 1)
+    p = sg.plan(128, 65536, 2048, num_cus=256, occupancy=occ)
+    assert p["config"] == sg.CFG_DL_128x128x32
+    p = sg.plan(65536, 320, 2048, num_cus=256, occupancy=occ)   # 83% inside 128-wide tiles
+    assert p["config"] in (sg.CFG_DL_64x64x64, sg.CFG_DL_64x64x32)
+    # Narrow C with a small B: row by row (tiles sharing an A panel side by
+    # side); few tile rows with a small A: column by column.
+    assert p["group_m"] == 1
+    p = sg.plan(49152, 192, 4096, num_cus=256, occupancy=occ)
+    assert (p["config"], p["tiles_n"], p["group_m"]) == (sg.CFG_DL_64x64x32, 3, 1)
+    # Narrow but few tiles (64): the 64-deep chunks.
+    assert sg.plan(512, 512, 8192, num_cus=256, occupancy=occ)["config"] == sg.CFG_DL_64x64x64
+    p = sg.plan(192, 49152, 4096, num_cus=256, occupancy=occ)
+    assert (p["tiles_m"], p["group_m"]) == (3, 3)
+    check_plan(p, 192, 49152, 4096)
     # Ragged shapes: the edge-masking kernels of the same regimes, or the
     # general kernel when N or K is not a multiple of 4.
     p = sg.plan(4000, 4000, 4000, num_cus=256, occupancy=occ)
