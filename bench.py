@@ -86,6 +86,11 @@ def parse():
     ap.add_argument("--warm-seconds", type=float, default=0.5,
                     help="keep making untimed warm-up calls until this long has passed (clock ramp)")
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--shape", default=None, metavar="MxNxK",
+                    help="instead of a named workload: this shape, dense row-major operands "
+                         "(lda = K, ldb = ldc = N), U[-1,1] seed 0 unless --dist / --seed")
+    ap.add_argument("--dist", default="uniform", choices=workloads.DISTRIBUTIONS)
+    ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--config", type=int, default=0)
     ap.add_argument("--sched", type=int, default=0)
     ap.add_argument("--all", action="store_true", help="also time every workload (details only)")
@@ -285,7 +290,11 @@ def main():
                           "median_ms": round(t * 1e3, 4), "steps": args.steps}), flush=True)
         return
 
-    w = workloads.WORKLOADS[args.workload]
+    if args.shape:
+        M, N, K = (int(x) for x in args.shape.lower().split("x"))
+        w = workloads.Workload(f"sgemm_{M}x{N}x{K}", M, N, K, args.dist, args.seed)
+    else:
+        w = workloads.WORKLOADS[args.workload]
     head = bench_workload(sg, w, args, dev, stream, cold=not args.no_cold, with_torch=args.torch)
     log(json.dumps(head))
     detail = {"headline": head, "device": props.name, "cus": props.multi_processor_count}
@@ -302,7 +311,7 @@ def main():
             # The FP64 oracle on each workload (a bounded row sample, whole
             # product where it fits the budget) beside the GPU's median.
             for r in [head] + rest:
-                ww = workloads.WORKLOADS[r["workload"]]
+                ww = w if r is head else workloads.WORKLOADS[r["workload"]]
                 cpu_r = cpu_baseline(ww, min(args.cpu_seconds, 6.0))
                 r["cpu_oracle"] = cpu_r
                 r["gpu_over_oracle"] = r["tflops_median"] / cpu_r["value"]
@@ -338,7 +347,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist, "seed": w.seed,
                    "kernel": cfg_name, "sched": sg.SCHED_NAMES[head["plan"]["sched"]],
-                   "grid": head["plan"]["grid"], "parallelism": "single-gpu"},
+                   "grid": head["plan"]["grid"], "parallelism": "single-gpu",
+                   **({"repacked": True} if head["plan"]["repacked"] else {})},
         "frac_of_fp32_peak": round(head["tflops"] / PEAK_FP32_TFLOPS, 4),
         "median_event_tflops": round(head["tflops_median"], 3),
         "cold_median_event_tflops": (round(head["cold_tflops_median"], 3) if "cold_tflops_median" in head

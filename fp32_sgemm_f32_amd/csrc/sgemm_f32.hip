@@ -423,13 +423,23 @@ static int plan_for(int ta, int tb, int M, int N, int K, int config, int sched, 
     if (!out) return SGEMM_ERR_NULL;
     if ((ta != 0 && ta != 1) || (tb != 0 && tb != 1)) return SGEMM_ERR_CONFIG;
     // Dense operands on 16-byte boundaries: the vector layout holds when
-    // the stored row lengths of A and B, and N, are multiples of 4.
+    // the stored row lengths of A and B, and N, are multiples of 4.  Else
+    // the call itself may repack (see run_packed), and the plan is that of
+    // the padded product.
     const int a_cols = ta ? M : K, b_cols = tb ? K : N;
-    sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu,
-                           (a_cols % 4 == 0 && b_cols % 4 == 0 && N % 4 == 0) ? 1 : 0, ta, tb};
+    const bool aligned = a_cols % 4 == 0 && b_cols % 4 == 0 && N % 4 == 0;
+    sgemm::Call c = sgemm::plain(M, N, K, nullptr, a_cols, nullptr, b_cols, nullptr, N, nullptr, config, sched);
+    c.ta = ta;
+    c.tb = tb;
+    const bool repack = !aligned && config == SGEMM_CFG_AUTO && K > 0 && M > 0 && N > 0 && sgemm::worth_repacking(c);
+    const int Mp = repack && ta ? sgemm::up4(M) : M, Np = repack ? sgemm::up4(N) : N,
+              Kp = repack ? sgemm::up4(K) : K;
+    sgemm::PlanRequest req{Mp, Np, Kp, config, sched, num_cus, occupancy, sk_wg_per_cu, aligned || repack ? 1 : 0,
+                           ta, tb};
     sgemm::Plan p;
     int st = sgemm::make_plan(req, &p);
     if (st != SGEMM_OK) return st;
+    out->repacked = repack ? 1 : 0;
     out->config = p.config;
     out->sched = p.sched;
     out->tile_m = p.bm;

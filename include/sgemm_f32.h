@@ -233,7 +233,9 @@ int sgemm_f32_last_hip_error(void);
  * configuration c that fit on one compute unit (NULL: the library's
  * built-in figures); sk_wg_per_cu is the number of split workgroups per CU
  * (0: the library's default, one), capped by the occupancy.  The plan
- * assumes dense operands (lda = K, ldb = ldc = N) on 16-byte boundaries.
+ * assumes dense operands (lda = K, ldb = ldc = N) on 16-byte boundaries;
+ * where such a call would run on repacked copies (see "Fast and general
+ * layouts"), it is the plan of the padded product and `repacked` is 1.
  * Returns an SGEMM_* status code; *out is filled on success.
  */
 typedef struct sgemm_f32_plan_t {
@@ -251,6 +253,8 @@ typedef struct sgemm_f32_plan_t {
     int group_m;         /* tile order: groups of group_m tile rows, column-major inside */
     long long sk_iters;  /* sk_tiles * iters_per_tile */
     long long workspace_bytes;
+    int repacked;        /* 1: A and B are first copied to padded buffers; the
+                            fields above describe the padded product */
 } sgemm_f32_plan_t;
 
 int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,

@@ -239,10 +239,18 @@ def test_auto_choices_on_256_cus():
     assert p["config"] == sg.CFG_DL_128x128x32
     p = sg.plan(1000, 1000, 1000, num_cus=256, occupancy=occ)
     assert p["config"] == sg.CFG_DL_64x64x64
-    p = sg.plan(1000, 1001, 1000, num_cus=256, occupancy=occ)
-    assert p["config"] == sg.CFG_GENERIC_64x64x16
+    p = sg.plan(100, 101, 100, num_cus=256, occupancy=occ)
+    assert (p["config"], p["repacked"]) == (sg.CFG_GENERIC_64x64x16, 0)
     p = sg.plan(7, 13, 5, num_cus=256, occupancy=occ)
     assert p["config"] == sg.CFG_GENERIC_64x64x16
+    # At least 2^25 multiply-adds (M, N, K >= 64): the call runs on padded
+    # copies, and the plan is the padded product's.
+    p = sg.plan(1000, 1001, 1000, num_cus=256, occupancy=occ)
+    assert (p["config"], p["repacked"], p["tiles_n"]) == (sg.CFG_DL_64x64x64, 1, 16)
+    p = sg.plan(4096, 4097, 4096, num_cus=256, occupancy=occ)
+    assert (p["config"], p["repacked"], p["tiles_n"]) == (sg.CFG_DL_256x256x16, 1, 17)
+    p = sg.plan(1000, 1001, 1000, sg.CFG_GENERIC_64x64x16, num_cus=256, occupancy=occ)   # forced: as asked
+    assert (p["config"], p["repacked"]) == (sg.CFG_GENERIC_64x64x16, 0)
 
 
 # Configurations that also run A stored K x M and / or B stored N x K.
@@ -266,10 +274,17 @@ def test_auto_choices_for_transposed_storage(layout):
     assert cfg(1024, 1024, 16384) == sg.CFG_DL_64x64x64
     assert cfg(1024, 1024, 96) == sg.CFG_DL_64x64x32
     # A stored K x M has rows of M floats; B stored N x K rows of K floats.
-    assert cfg(1022, 1024, 1024) == (sg.CFG_GENERIC_64x64x16 if ta else sg.CFG_DL_64x64x64)
-    assert cfg(1024, 1024, 1022) == (sg.CFG_DL_64x64x64 if (ta and not tb) else
-                                     sg.CFG_GENERIC_64x64x16)
-    assert cfg(1024, 1022, 1024) == sg.CFG_GENERIC_64x64x16          # C rows
+    # Below 2^25 multiply-adds such a layout runs on the general kernel:
+    assert cfg(254, 256, 256) == (sg.CFG_GENERIC_64x64x16 if ta else sg.CFG_DL_64x64x64)
+    assert cfg(256, 256, 254) == (sg.CFG_DL_64x64x64 if (ta and not tb) else
+                                  sg.CFG_GENERIC_64x64x16)
+    assert cfg(256, 254, 256) == sg.CFG_GENERIC_64x64x16          # C rows
+    # at or above it, on padded copies (the plan of the padded product).
+    for shape, misaligned in (((1022, 1024, 1024), ta), ((1024, 1024, 1022), not (ta and not tb)),
+                              ((1024, 1022, 1024), True)):
+        p = sg.plan(*shape, num_cus=256, occupancy=occ, trans_a=ta, trans_b=tb)
+        assert p["repacked"] == (1 if misaligned else 0), shape
+        assert p["config"] == sg.CFG_DL_64x64x64
     p = sg.plan(4096, 4096, 4096, num_cus=256, occupancy=occ, trans_a=ta, trans_b=tb)
     assert p["tiles_m"] == 16 and p["sched"] == sg.SCHED_DP
 
