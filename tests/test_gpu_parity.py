@@ -838,3 +838,36 @@ def test_graph_capture_of_a_repacked_call(dev):
         got = C.cpu().numpy()
         assert np.array_equal(got.astype(np.float64), C_ref), f"replay {r}"
         assert np.array_equal(got, E.cpu().numpy()), f"replay {r} vs eager"
+
+
+# Shapes that take each tile-order and configuration route of the automatic
+# choice for narrow or ragged C: (shape, storage orders, expected
+# configuration, expected tile-row group).  Integer inputs: exact results.
+ROUTE_CASES = {
+    "col_order_3_rows_split": ((192, 8192, 512), (0, 0), "dl_64x64x64", 3),
+    "col_order_3_rows_tt": ((192, 8192, 512), (1, 1), "dl_64x64x64", 3),
+    "col_order_5_rows_32deep": ((320, 8192, 384), (0, 0), "dl_64x64x32", 5),
+    "row_order_narrow_32deep": ((8192, 320, 512), (0, 0), "dl_64x64x32", 1),
+    "row_order_dp_32deep": ((16384, 128, 256), (0, 1), "dl_64x64x32", 1),
+    "coverage_picks_128": ((65536, 128, 32), (0, 0), "dl_128x128x32", 1),
+    "one_wave_split_whole": ((1024, 1028, 512), (1, 0), "dl_64x64x64", None),
+}
+
+
+@pytest.mark.parametrize("case", list(ROUTE_CASES))
+def test_planner_routes_for_narrow_and_ragged_c(dev, case):
+    import torch
+    (M, N, K), (ta, tb), cfg_name, group = ROUTE_CASES[case]
+    p = sg.plan(M, N, K, num_cus=torch.cuda.get_device_properties(dev).multi_processor_count,
+                trans_a=ta, trans_b=tb)
+    assert sg.CFG_NAMES[p["config"]] == cfg_name
+    if group is not None:
+        assert p["group_m"] == group
+    log(f"case route {case}: shape=({M},{N},{K}) ta={ta} tb={tb} plan={p}")
+    A, B = workloads.generate(M, N, K, "int4", 99)
+    As, Bs = stored(A, ta), stored(B, tb)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    sg.gemm(to_dev(As, dev), to_dev(Bs, dev), C, 1.0, 0.0, ta, tb)
+    torch.cuda.synchronize()
+    C_ref, _ = oracle.gemm_blas(As, Bs, None, 1.0, 0.0, ta, tb)
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref)
