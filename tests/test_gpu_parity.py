@@ -871,3 +871,40 @@ def test_planner_routes_for_narrow_and_ragged_c(dev, case):
     torch.cuda.synchronize()
     C_ref, _ = oracle.gemm_blas(As, Bs, None, 1.0, 0.0, ta, tb)
     assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref)
+
+
+# C with more elements than a 32-bit index reaches (65536 x 32800 = 2.15e9
+# floats, 8.6 GB): every route that writes C, checked on whole rows at the
+# far end, whole columns and random points (integer inputs: exact).
+BIG_C_CASES = {
+    # name: (M, N, K, config, beta)
+    "dl_edge": (65536, 32800, 32, sg.CFG_AUTO, 0.0),
+    "repacked_odd_n": (65536, 32801, 32, sg.CFG_AUTO, 0.0),
+    "general_kernel": (65536, 32800, 32, sg.CFG_GENERIC_64x64x16, 0.0),
+    "k_zero_scale": (65536, 32800, 0, sg.CFG_AUTO, 2.0),
+}
+
+
+@pytest.mark.parametrize("case", list(BIG_C_CASES))
+def test_c_beyond_32bit_element_offsets(dev, case):
+    import torch
+    M, N, K, config, beta = BIG_C_CASES[case]
+    log(f"case big C {case}: shape=({M},{N},{K}) config={sg.CFG_NAMES[config]} beta={beta}")
+    assert M * N > 2 ** 31
+    A, B = workloads.generate(M, N, K, "int4", 94)
+    C = torch.full((M, N), 1.5, dtype=torch.float32, device=dev)
+    sg.gemm(to_dev(A, dev), to_dev(B, dev), C, 1.0, beta, config=config)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(95)
+    full_rows = np.array([0, M - 2, M - 1])
+    full_cols = np.array([int(rng.integers(0, N)), N - 1])
+    r = np.concatenate([np.repeat(full_rows, N), np.tile(np.arange(M), 2), rng.integers(M // 2, M, 20000)])
+    c = np.concatenate([np.tile(np.arange(N), 3), np.repeat(full_cols, M), rng.integers(0, N, 20000)])
+    got = C[torch.from_numpy(r).to(dev), torch.from_numpy(c).to(dev)].cpu().numpy().astype(np.float64)
+    if K == 0:
+        expected = np.full(r.shape, 1.5 * beta)
+    else:
+        expected, _ = oracle.gemm_points(A, B, r, c)
+    assert np.array_equal(got, expected)
+    del C
+    torch.cuda.empty_cache()
