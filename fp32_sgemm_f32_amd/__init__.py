@@ -47,7 +47,8 @@ CFG_DL_64x64x64 = 19
 CFG_DL_128x256x16 = 20
 CFG_DL_256x128x16 = 21
 CFG_GENERIC_64x64x16 = 22
-NUM_CFGS = 23
+CFG_SKINNY_16x256 = 23
+NUM_CFGS = 24
 CFG_NAMES = {
     CFG_AUTO: "auto",
     CFG_MFMA_256x256x16: "mfma_256x256x16",
@@ -72,6 +73,7 @@ CFG_NAMES = {
     CFG_DL_128x256x16: "dl_128x256x16",
     CFG_DL_256x128x16: "dl_256x128x16",
     CFG_GENERIC_64x64x16: "generic_64x64x16",
+    CFG_SKINNY_16x256: "skinny_16x256",
 }
 # (tile_m, tile_n, tile_k) of each configuration.
 CFG_TILES = {

@@ -17,6 +17,9 @@ hipError_t occupancy_mfma_dl(int cfg, int *wg_per_cu);
 hipError_t launch_generic(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t occupancy_generic(int cfg, int *wg_per_cu);
 hipError_t launch_valu(int cfg, const KernelArgs &a, hipStream_t s);
+// The skinny kernel (M <= 16) and, for a K-split plan, the sum of its splits.
+hipError_t launch_skinny(int cfg, const KernelArgs &a, hipStream_t s);
+hipError_t occupancy_skinny(int cfg, int *wg_per_cu);
 hipError_t occupancy_valu(int cfg, int *wg_per_cu);
 // Sum of the split tiles of a Stream-K launch (tile bm x bn) into C; after
 // the GEMM kernel on the same stream.

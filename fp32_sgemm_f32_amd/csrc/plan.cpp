@@ -38,6 +38,7 @@ const CfgInfo kCfgs[] = {
     {SGEMM_CFG_DL_128x256x16, 128, 256, 16, 256, kKindMfmaDl, 2, false, false, "dl_128x256x16"},
     {SGEMM_CFG_DL_256x128x16, 256, 128, 16, 256, kKindMfmaDl, 2, false, false, "dl_256x128x16"},
     {SGEMM_CFG_GENERIC_64x64x16, 64, 64, 16, 256, kKindGeneric, 2, true, true, "generic_64x64x16"},
+    {SGEMM_CFG_SKINNY_16x256, 16, 256, kSkinnyBlock, 512, kKindSkinny, 1, true, true, "skinny_16x256"},
 };
 const int kNumCfgs = SGEMM_NUM_CFGS;
 
@@ -55,6 +56,10 @@ static bool divides(const CfgInfo &c, int M, int N, int K) {
 // Whether configuration c can run the shape: the generic kernel runs
 // anything; the others need the aligned fast-path layout, and a tile that
 // divides the shape unless they mask ragged edges.
+// The skinny kernel: at most 16 rows, B stored K x N with the vector layout
+// (A and C are read and written one float at a time, in any layout).
+static bool skinny_fits(const PlanRequest &r) { return r.M <= 16 && !r.trans_b && r.b_vector; }
+
 static bool fits(const CfgInfo &c, int M, int N, int K, bool aligned, bool transposed) {
     if (c.kind == kKindGeneric) return true;
     if (!aligned || (transposed && !c.layouts)) return false;
@@ -110,8 +115,16 @@ static bool covers_well(int cfg, int M, int N) {
 //     per CU and keeps twice the loads in flight, which such shapes, with
 //     little reuse of the long operand, need (131072x64x1024: 114 against
 //     105; 8192x384x4096: 144 against 140).
+//   * at most 8 rows, B stored K x N with the vector layout, N and K at
+//     least 256: the skinny kernel, which streams B without computing the
+//     empty rows of a 64-row tile (1 x 16384 x 16384: 5.9 TB/s of B against
+//     4.4 for the tiled kernel and 5.8 for hipBLASLt; 8 x 8192 x 28672: 5.5
+//     against 4.3 and 4.9).  Its 16-row form runs when asked for but is
+//     slower than the tiled kernels (16 x 16384 x 16384: 3.7 TB/s).
 // Layouts the vector kernels cannot load go to the general kernel.
-static int auto_config(int M, int N, int K, int cus, bool aligned) {
+static int auto_config(const PlanRequest &r, int cus, bool aligned) {
+    const int M = r.M, N = r.N, K = r.K;
+    if (skinny_fits(r) && M <= 8 && N >= 256 && K >= 256) return SGEMM_CFG_SKINNY_16x256;
     if (!aligned) return SGEMM_CFG_GENERIC_64x64x16;
     const int big = SGEMM_CFG_DL_256x256x16, mid = SGEMM_CFG_DL_128x128x32, small = SGEMM_CFG_DL_64x64x64,
               small32 = SGEMM_CFG_DL_64x64x32;
@@ -146,6 +159,48 @@ bool dl_offsets_fit(int cfg, bool edge, int64_t lda, int64_t ldb, bool trans_a, 
     return rows_a * lda * 4 < lim && rows_b * ldb * 4 < lim;
 }
 
+// The skinny kernel's plan, in the terms of the tiled ones: a "tile" is a
+// strip of 256 columns (one tile row, 16 rows high), its "K chunks" are the
+// KS splits of K, and every workgroup owns exactly one (strip, split) step,
+// so KS > 1 is a Stream-K plan whose every tile is split.  KS gives the
+// grid about one workgroup per CU (8 waves: two per SIMD), with at least
+// 256 k per split; the data-parallel schedule forces KS = 1.
+static int plan_skinny(const PlanRequest &req, int cus, Plan *out) {
+    if (!skinny_fits(req)) return SGEMM_ERR_CONFIG;
+    const CfgInfo &c = kCfgs[SGEMM_CFG_SKINNY_16x256];
+    Plan p{};
+    p.config = SGEMM_CFG_SKINNY_16x256;
+    p.bm = c.bm; p.bn = c.bn; p.threads = c.threads;
+    p.tiles_m = (req.M + c.bm - 1) / c.bm;
+    p.tiles_n = (req.N + c.bn - 1) / c.bn;
+    p.edge = 1;
+    const int strips = p.tiles_n;
+    int ks = 1;
+    if (req.sched != SGEMM_SCHED_DP && strips > 0 && req.K > 0) {
+        ks = (cus + strips - 1) / strips;
+        const int by_k = req.K / 256 > 1 ? req.K / 256 : 1;
+        if (ks > by_k) ks = by_k;
+        if (req.sched == SGEMM_SCHED_STREAMK && ks < 2 && req.K >= 2) ks = 2;
+    }
+    p.bk = req.K > 0 ? (req.K + ks - 1) / ks : 1;   // k per split
+    p.ipt = req.K > 0 ? (req.K + p.bk - 1) / p.bk : 0;
+    const int tiles = p.tiles_m * p.tiles_n;
+    if (tiles == 0 || p.ipt == 0 || (p.ipt == 1 && req.sched != SGEMM_SCHED_STREAMK)) {
+        p.dp_tiles = tiles; p.sk_tiles = 0; p.sk_grid = 0; p.grid = tiles;
+        p.sched = SGEMM_SCHED_DP;
+    } else {
+        p.dp_tiles = 0; p.sk_tiles = tiles;
+        p.sk_iters = (int64_t)tiles * p.ipt;
+        p.sk_grid = (int)p.sk_iters; p.grid = p.sk_grid;
+        p.sched = SGEMM_SCHED_STREAMK;
+        p.workspace_bytes = (int64_t)p.ipt * 16 * strips * c.bn * 4;   // [KS][16][strips * 256]
+    }
+    p.xcd_remap = 0;
+    p.group_m = 1;
+    *out = p;
+    return SGEMM_OK;
+}
+
 int make_plan(const PlanRequest &req, Plan *out) {
     const int M = req.M, N = req.N, K = req.K;
     if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SHAPE;
@@ -155,8 +210,9 @@ int make_plan(const PlanRequest &req, Plan *out) {
 
     int cfg = req.config;
     const bool aligned = req.aligned != 0, transposed = req.trans_a || req.trans_b;
-    if (cfg == SGEMM_CFG_AUTO) cfg = auto_config(M, N, K, cus, aligned);
+    if (cfg == SGEMM_CFG_AUTO) cfg = auto_config(req, cus, aligned);
     const CfgInfo &c = kCfgs[cfg];
+    if (c.kind == kKindSkinny) return plan_skinny(req, cus, out);
     if (!fits(c, M, N, K, aligned, transposed)) return SGEMM_ERR_CONFIG;
 
     Plan p{};

@@ -13,7 +13,11 @@ enum CfgKind {
     kKindMfma = 1,      // matrix cores, tiles staged through registers
     kKindMfmaDl = 2,    // matrix cores, tiles loaded straight into LDS
     kKindGeneric = 3,   // matrix cores, element-wise bounds-checked loads (any shape/alignment)
+    kKindSkinny = 4,    // scalar VALU FMAs over the M <= 16 rows only, B streamed
 };
+
+// K values of A staged in LDS at a time by the skinny kernel.
+constexpr int kSkinnyBlock = 512;
 
 struct CfgInfo {
     int id;
@@ -48,6 +52,8 @@ struct PlanRequest {
                          // extents of A, B, C multiples of 4
     int trans_a = 0;     // A stored K x M
     int trans_b = 0;     // B stored N x K
+    int b_vector = 0;    // B alone has the vector layout: 16-byte aligned, ldb and the
+                         // stored row length multiples of 4, and N too
 };
 
 struct Plan {

@@ -48,6 +48,7 @@ hipError_t launch_cfg(int cfg, const KernelArgs &a, hipStream_t s) {
     case kKindMfma: return launch_mfma(cfg, a, s);
     case kKindMfmaDl: return launch_mfma_dl(cfg, a, s);
     case kKindGeneric: return launch_generic(cfg, a, s);
+    case kKindSkinny: return launch_skinny(cfg, a, s);
     default: return launch_valu(cfg, a, s);
     }
 }
@@ -57,6 +58,7 @@ hipError_t occupancy_of(int cfg, int *n) {
     case kKindMfma: return occupancy_mfma(cfg, n);
     case kKindMfmaDl: return occupancy_mfma_dl(cfg, n);
     case kKindGeneric: return occupancy_generic(cfg, n);
+    case kKindSkinny: return occupancy_skinny(cfg, n);
     default: return occupancy_valu(cfg, n);
     }
 }
@@ -182,6 +184,11 @@ bool vector_c(const Call &c) {
 
 bool vector_layout(const Call &c) { return vector_ab(c) && vector_c(c); }
 
+// B alone in the vector layout (what the skinny kernel needs).
+bool vector_b(const Call &c) {
+    return (c.b_cols() & 3) == 0 && (c.N & 3) == 0 && (c.ldb & 3) == 0 && ((uintptr_t)c.B & 15) == 0;
+}
+
 // Stream-K workspace of (dev, stream), grown to hold `plan`'s partial
 // tiles.  Caller holds g_mu.
 int workspace_for(int dev, hipStream_t s, const Plan &p, Workspace *out) {
@@ -292,9 +299,6 @@ int run(const Call &c) {
         if ((st = check_device_range(c.B, extent_bytes(c.b_rows(), c.b_cols(), c.ldb), dev)) != SGEMM_OK) return st;
     }
 
-    if (!c.repacked && c.config == SGEMM_CFG_AUTO && c.reads_ab() && !vector_layout(c) && worth_repacking(c))
-        return run_packed(c, dev);
-
     // C written in place beyond padded operands (run_packed): the edge
     // variants store only C's own rows and columns.
     const bool c_own = c.cm != 0 || c.cn != 0;
@@ -302,9 +306,15 @@ int run(const Call &c) {
     if ((st = device_info(dev, &info)) != SGEMM_OK) return st;
     PlanRequest req{c.M, c.N, c.K, c.config, c.sched, info.num_cus, info.occupancy,
                     env_int("SGEMM_F32_SK_WG_PER_CU", 0), vector_ab(c) && (c_own || vector_c(c)) ? 1 : 0,
-                    c.ta, c.tb};
+                    c.ta, c.tb, vector_b(c) ? 1 : 0};
     Plan p;
     if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
+    // An automatic choice other than the skinny kernel (which reads A and
+    // writes C in any layout) on a layout the vector kernels cannot load:
+    // large products run on repacked copies.
+    if (!c.repacked && c.config == SGEMM_CFG_AUTO && c.reads_ab() && kCfgs[p.config].kind != kKindSkinny &&
+        !vector_layout(c) && worth_repacking(c))
+        return run_packed(c, dev);
     if (c_own) p.edge = 1;
     if (c.K > 0 && !dl_offsets_fit(p.config, p.edge != 0, c.lda, c.ldb, c.ta != 0, c.tb != 0)) {
         // Leading dimensions too large for the 32-bit source offsets of the
@@ -348,8 +358,8 @@ int run(const Call &c) {
         Workspace w;
         if ((st = workspace_for(dev, c.stream, p, &w)) != SGEMM_OK) return st;
         a.partials = w.partials;
-        e = launch_cfg(p.config, a, c.stream);
-        if (e == hipSuccess) e = launch_sk_fixup(a, p.bm, p.bn, c.stream);
+        e = launch_cfg(p.config, a, c.stream);   // the skinny kernel adds its own splits
+        if (e == hipSuccess && kCfgs[p.config].kind != kKindSkinny) e = launch_sk_fixup(a, p.bm, p.bn, c.stream);
     } else {
         e = launch_cfg(p.config, a, c.stream);
     }
@@ -428,17 +438,24 @@ static int plan_for(int ta, int tb, int M, int N, int K, int config, int sched, 
     // the padded product.
     const int a_cols = ta ? M : K, b_cols = tb ? K : N;
     const bool aligned = a_cols % 4 == 0 && b_cols % 4 == 0 && N % 4 == 0;
+    const bool b_vector = b_cols % 4 == 0 && N % 4 == 0;
     sgemm::Call c = sgemm::plain(M, N, K, nullptr, a_cols, nullptr, b_cols, nullptr, N, nullptr, config, sched);
     c.ta = ta;
     c.tb = tb;
-    const bool repack = !aligned && config == SGEMM_CFG_AUTO && K > 0 && M > 0 && N > 0 && sgemm::worth_repacking(c);
-    const int Mp = repack && ta ? sgemm::up4(M) : M, Np = repack ? sgemm::up4(N) : N,
-              Kp = repack ? sgemm::up4(K) : K;
-    sgemm::PlanRequest req{Mp, Np, Kp, config, sched, num_cus, occupancy, sk_wg_per_cu, aligned || repack ? 1 : 0,
-                           ta, tb};
+    sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu, aligned ? 1 : 0, ta, tb,
+                           b_vector ? 1 : 0};
     sgemm::Plan p;
     int st = sgemm::make_plan(req, &p);
     if (st != SGEMM_OK) return st;
+    const bool repack = !aligned && config == SGEMM_CFG_AUTO && K > 0 && M > 0 && N > 0 &&
+                        sgemm::kCfgs[p.config].kind != sgemm::kKindSkinny && sgemm::worth_repacking(c);
+    if (repack) {
+        req.M = ta ? sgemm::up4(M) : M;
+        req.N = sgemm::up4(N);
+        req.K = sgemm::up4(K);
+        req.aligned = 1;
+        if ((st = sgemm::make_plan(req, &p)) != SGEMM_OK) return st;
+    }
     out->repacked = repack ? 1 : 0;
     out->config = p.config;
     out->sched = p.sched;

@@ -1,0 +1,208 @@
+// Products with at most 16 rows (M <= 16), B stored K x N with 16-byte rows:
+// HBM-bound on B.  A tile of the matrix-core kernels computes 64 or more
+// rows, so for such an M most of its work is empty rows, and streaming B
+// stops at what those MFMAs allow (~4.4 TB/s).  This kernel does only the
+// M rows' multiply-adds on the vector ALU and spends its registers on loads
+// in flight instead: the design the pages use for their FMA kernels (a
+// register-tiled outer product fed from shared memory: "2D Block Tiling:
+// Scaling Matrix Multiplication on NVIDIA H100", section 3; 16-byte loads:
+// "Vectorized Memory Access: Pushing CUDA SGEMM to 29 TFLOPS on H100",
+// section 3), with A as the small operand held in LDS and B streamed.
+//
+// Work: workgroup w of the grid owns column strip w / KS (256 columns) and
+// K split w % KS (ceil(K / KS) consecutive k).  Its 8 waves split that range
+// again, each lane holding 4 adjacent columns for all MR rows (MR = 4, 8 or
+// 16 >= M): per k one 16-byte B load and 4 * MR multiply-adds, 16 loads in
+// flight per lane.  Two waves per SIMD: the 16-row kernel's LDS (96 KiB)
+// admits one workgroup per CU anyway, so each wave may use 256 registers.  A's values, the same for every lane, are staged in LDS
+// (k-major, MR floats per k) a block of 512 k at a time and read as
+// broadcasts.  The 8 waves' sums are added through LDS in a fixed tree
+// order; with KS > 1 each workgroup writes its strip's partial sum, and a
+// second kernel adds the KS partials in split order and writes C.  Every
+// sum is taken in a fixed order, so results repeat bit for bit.
+#include "gemm_common.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace sgemm {
+
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCols = 256;            // columns per strip: 64 lanes x 4
+constexpr int kBlock = kSkinnyBlock;  // k per A staging block
+
+// A(m, k) of the product (A stored M x K, or K x M when trans_a).
+__device__ __forceinline__ float a_at(const KernelArgs &a, int m, int k) {
+    return a.trans_a ? a.A[(int64_t)k * a.lda + m] : a.A[(int64_t)m * a.lda + k];
+}
+
+// acc[m][j] += A(m, k) * B(k, n0 + j) for one k: A's MR values (a broadcast
+// LDS read) times the lane's 4 B values, m and then j ascending.
+template <int MR>
+__device__ __forceinline__ void fma_k(float (&acc)[MR][4], const float *ap, const f32x4 &b) {
+#pragma unroll
+    for (int q = 0; q < MR / 4; ++q) {
+        const f32x4 av = *(const f32x4 *)(ap + 4 * q);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[4 * q + r][j] += av[r] * b[j];
+    }
+}
+
+template <int MR>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sgemm_skinny_kernel(KernelArgs a) {
+    constexpr int kUnroll = 16;   // B loads in flight per lane
+    // A block (k-major, MR floats per k), then the waves' sums.
+    __shared__ __attribute__((aligned(16))) float as[kBlock * MR];
+    __shared__ __attribute__((aligned(16))) float red[(kWaves / 2) * MR * kCols];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int ks_count = a.ipt;
+    const int strip = blockIdx.x / ks_count, ks = blockIdx.x - strip * ks_count;
+    const int k_per = (a.K + ks_count - 1) / ks_count;
+    const int k_begin = ks * k_per;
+    const int k_end = k_begin + k_per < a.K ? k_begin + k_per : a.K;
+    const int n0 = strip * kCols + 4 * lane;
+    const bool col_ok = n0 < a.N;   // N is a multiple of 4: a lane's 4 columns are all in or all out
+    const float *bcol = a.B + n0;
+
+    float acc[MR][4];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m][j] = 0.0f;
+
+    for (int blk = k_begin; blk < k_end; blk += kBlock) {
+        const int blen = k_end - blk < kBlock ? k_end - blk : kBlock;
+        __syncthreads();   // the previous block's reads are done
+        // Stage A(0..MR-1, blk..blk+blen-1), zeros in rows >= M; threads
+        // along A's contiguous dimension.
+        for (int i = tid; i < blen * MR; i += kThreads) {
+            int m, kl;
+            if (a.trans_a) { kl = i / MR; m = i - kl * MR; }
+            else { m = i / blen; kl = i - m * blen; }
+            as[kl * MR + m] = m < a.M ? a_at(a, m, blk + kl) : 0.0f;
+        }
+        __syncthreads();
+        // This wave's share of the block: whole groups of kUnroll k (all
+        // loads first), then the remaining k one at a time.
+        const int w0 = blk + (blen * wave) / kWaves, w1 = blk + (blen * (wave + 1)) / kWaves;
+        int k = w0;
+        for (; k + kUnroll <= w1; k += kUnroll) {
+            f32x4 b[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                b[u] = col_ok ? *(const f32x4 *)(bcol + (int64_t)(k + u) * a.ldb) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) fma_k(acc, as + (k + u - blk) * MR, b[u]);
+        }
+        for (; k < w1; ++k) {
+            const f32x4 b = col_ok ? *(const f32x4 *)(bcol + (int64_t)k * a.ldb) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            fma_k(acc, as + (k - blk) * MR, b);
+        }
+    }
+
+    // Sum the 8 waves in a fixed tree: (w + 4), then (w + 2), then (w + 1).
+#pragma unroll
+    for (int half = kWaves / 2; half >= 1; half >>= 1) {
+        __syncthreads();
+        if (wave >= half && wave < 2 * half) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                *(f32x4 *)(red + ((wave - half) * MR + m) * kCols + 4 * lane) =
+                    f32x4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+        }
+        __syncthreads();
+        if (wave < half) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const f32x4 v = *(const f32x4 *)(red + (wave * MR + m) * kCols + 4 * lane);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[m][j] += v[j];
+            }
+        }
+    }
+    if (wave != 0 || !col_ok) return;
+
+    if (ks_count == 1) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            if (m >= a.M) break;
+            float *c = a.C + (int64_t)m * a.ldc + n0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[j] = epilogue(a, acc[m][j], c + j);
+        }
+    } else {
+        // Partial sums, dense: split ks, row m, column n at
+        // partials[(ks * 16 + m) * Np + n], Np = strips * 256.
+        const int64_t np = (int64_t)a.tiles_n * kCols;
+        float *p = a.partials + (int64_t)ks * 16 * np + n0;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            if (m >= a.M) break;
+            *(f32x4 *)(p + m * np) = f32x4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+        }
+    }
+}
+
+// C(m, n..n+3) = the KS partial sums added in split order, then the
+// epilogue: one thread per 4 outputs, up to 8 splits' loads in flight.
+__global__ __launch_bounds__(256) void sgemm_skinny_sum_kernel(KernelArgs a) {
+    const int quads = a.N / 4;
+    const int64_t total = (int64_t)a.M * quads;
+    const int64_t np = (int64_t)a.tiles_n * kCols;
+    const int ks_count = a.ipt;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int m = (int)(t / quads), n = 4 * (int)(t - (int64_t)m * quads);
+        const float *p = a.partials + (int64_t)m * np + n;
+        f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s0 = 0; s0 < ks_count; s0 += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < ks_count) v[u] = *(const f32x4 *)(p + (int64_t)(s0 + u) * 16 * np);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < ks_count) sum += v[u];
+        }
+        float *c = a.C + (int64_t)m * a.ldc + n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] = epilogue(a, sum[j], c + j);
+    }
+}
+
+template <int MR>
+hipError_t launch_rows(const KernelArgs &a, hipStream_t s) {
+    KernelArgs args = a;
+    void *params[] = {&args};
+    hipError_t e = hipLaunchKernel((const void *)sgemm_skinny_kernel<MR>, dim3(a.grid), dim3(kThreads), params, 0, s);
+    if (e != hipSuccess || a.ipt <= 1) return e;
+    const int64_t threads = (int64_t)a.M * (a.N / 4);
+    int64_t blocks = (threads + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    return hipLaunchKernel((const void *)sgemm_skinny_sum_kernel, dim3((unsigned)blocks), dim3(256), params, 0, s);
+}
+
+}  // namespace
+
+hipError_t launch_skinny(int cfg, const KernelArgs &a, hipStream_t s) {
+    if (cfg != SGEMM_CFG_SKINNY_16x256 || a.M < 1 || a.M > 16 || a.N % 4 || a.trans_b ||
+        (a.ipt > 1 && !a.partials))
+        return hipErrorInvalidValue;
+    if (a.M <= 4) return launch_rows<4>(a, s);
+    if (a.M <= 8) return launch_rows<8>(a, s);
+    return launch_rows<16>(a, s);
+}
+
+hipError_t occupancy_skinny(int cfg, int *wg_per_cu) {
+    if (cfg != SGEMM_CFG_SKINNY_16x256) return hipErrorInvalidValue;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(wg_per_cu, (const void *)sgemm_skinny_kernel<16>, kThreads,
+                                                        0);
+}
+
+}  // namespace sgemm

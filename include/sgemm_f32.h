@@ -143,7 +143,12 @@ extern "C" {
 /* Element-wise bounds-checked loads: any shape, leading dimension and
  * (4-byte) alignment. */
 #define SGEMM_CFG_GENERIC_64x64x16  22 /* 256 threads, 4 waves of 32x32 */
-#define SGEMM_NUM_CFGS              23 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
+/* At most 16 rows (M <= 16), B stored K x N with 16-byte aligned rows, ldb
+ * and N multiples of 4 (A and C in any layout): vector-ALU multiply-adds
+ * over the M rows only, B streamed once, K split over the grid.  The
+ * automatic choice takes it for such products with M <= 8, N, K >= 256. */
+#define SGEMM_CFG_SKINNY_16x256     23 /* 512 threads, 8 waves over 256 columns */
+#define SGEMM_NUM_CFGS              24 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
 /* The configurations not named above as running other shapes or storage
  * orders need A stored M x K, B stored K x N, the vector layout and a shape
  * their tile divides. */

@@ -55,6 +55,8 @@ def fits(config, M, N, K, vector=None):
     vector layout holds when N and K are multiples of 4)."""
     if config in (sg.CFG_AUTO, sg.CFG_GENERIC_64x64x16):
         return True
+    if config == sg.CFG_SKINNY_16x256:   # dense B rows of N floats on 16-byte boundaries
+        return M <= 16 and N % 4 == 0
     if vector is None:
         vector = N % 4 == 0 and K % 4 == 0
     if not vector:
@@ -101,8 +103,9 @@ def test_parity_random(dev, config, sched, shape):
 @pytest.mark.parametrize("config", CONFIGS, ids=lambda c: sg.CFG_NAMES[c])
 def test_integer_inputs_bit_exact(dev, config, sched):
     """Entries in {-4..4} with K <= 1024: every partial sum is an integer below
-    2^24, exact in FP32 in any order, so every variant must match exactly."""
-    M, N, K = 512, 768, 1024
+    2^24, exact in FP32 in any order, so every variant must match exactly
+    (16 rows for the skinny kernel, which runs at most that many)."""
+    M, N, K = (16 if config == sg.CFG_SKINNY_16x256 else 512), 768, 1024
     log(f"case int4 config={sg.CFG_NAMES[config]} sched={sg.SCHED_NAMES[sched]}")
     A, B = workloads.generate(M, N, K, "int4", 77)
     C = gpu_matmul(A, B, dev, config, sched)
@@ -112,7 +115,7 @@ def test_integer_inputs_bit_exact(dev, config, sched):
 
 @pytest.mark.parametrize("config", CONFIGS, ids=lambda c: sg.CFG_NAMES[c])
 def test_identity_b_gives_a(dev, config):
-    M, K = 512, 256
+    M, K = (16 if config == sg.CFG_SKINNY_16x256 else 512), 256
     log(f"case identity config={sg.CFG_NAMES[config]}")
     A, _ = workloads.generate(M, K, K, "normal", 5)
     C = gpu_matmul(A, np.eye(K, dtype=np.float32), dev, config, sg.SCHED_STREAMK)
@@ -313,13 +316,14 @@ def test_storage_orders_integer_inputs_bit_exact(dev, config, layout):
 
 
 @pytest.mark.parametrize("config", [sg.CFG_MFMA_256x256x16, sg.CFG_MFMA_128x128x32, sg.CFG_VALU_128x128x8,
-                                    sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_GENERIC_64x64x16],
+                                    sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_GENERIC_64x64x16,
+                                    sg.CFG_SKINNY_16x256],
                          ids=lambda c: sg.CFG_NAMES[c])
 def test_blas_scaling_on_every_kernel_family(dev, config):
     """alpha / beta in the epilogue of each kernel family, whole tiles and
     Stream-K (the scaling is applied once, after the partial sums)."""
     import torch
-    M, N, K = 512, 512, 768
+    M, N, K = (13 if config == sg.CFG_SKINNY_16x256 else 512), 512, 768
     log(f"case blas scaling config={sg.CFG_NAMES[config]}")
     A, B = workloads.generate(M, N, K, "int4", 61)
     C0 = workloads.generate(M, 1, N, "int4", 62)[0]
@@ -908,3 +912,66 @@ def test_c_beyond_32bit_element_offsets(dev, case):
     assert np.array_equal(got, expected)
     del C
     torch.cuda.empty_cache()
+
+
+# Products with at most 16 rows: the skinny kernel (vector-ALU FMAs over the
+# M rows, B streamed, K split over the grid and the splits added in order).
+# (M, N, K, trans_a, A pad / offset, C pad / offset, alpha, beta, schedule)
+SKINNY_CASES = {
+    "gemv": (1, 4096, 4096, 0, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_AUTO),
+    "m3_ragged": (3, 1028, 777, 0, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_AUTO),
+    "m8_split": (8, 4096, 4096, 0, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_AUTO),
+    "m16_dp": (16, 4096, 300, 0, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_DP),
+    "m16_long_k": (16, 260, 65536, 0, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_AUTO),
+    "m5_ta_beta": (5, 2048, 1500, 1, (0, 0), (0, 0), -1.5, 0.5, sg.SCHED_AUTO),
+    "m16_odd_lda_ldc": (16, 1024, 1024, 0, (3, 1), (5, 2), 2.0, -1.0, sg.SCHED_STREAMK),
+    "m1_ta_offset": (1, 512, 8192, 1, (0, 1), (1, 1), 1.0, 0.0, sg.SCHED_AUTO),
+}
+
+
+@pytest.mark.parametrize("case", list(SKINNY_CASES))
+def test_skinny_rows(dev, case):
+    import torch
+    M, N, K, ta, (apad, aoff), (cpad, coff), alpha, beta, sched = SKINNY_CASES[case]
+    config = sg.CFG_AUTO if M <= 8 else sg.CFG_SKINNY_16x256   # the automatic choice up to 8 rows
+    p = sg.plan(M, N, K, config, sched, num_cus=torch.cuda.get_device_properties(dev).multi_processor_count,
+                trans_a=ta)
+    assert p["config"] == sg.CFG_SKINNY_16x256
+    log(f"case skinny {case}: shape=({M},{N},{K}) ta={ta} A pad/off={apad}/{aoff} C pad/off={cpad}/{coff} "
+        f"alpha={alpha} beta={beta} plan={p}")
+    A, B = workloads.generate(M, N, K, "int4", 101)
+    As = stored(A, ta)
+    C0 = workloads.generate(M, 1, N, "int4", 102)[0]
+
+    def placed(X, pad, off):
+        rows, cols = X.shape
+        ld = cols + pad
+        buf = torch.full((rows * ld + off + 4,), float("nan"), dtype=torch.float32, device=dev)
+        view = torch.as_strided(buf, (rows, cols), (ld, 1), off)
+        view.copy_(to_dev(X, dev))
+        return buf, view, ld
+
+    _, Av, _ = placed(As, apad, aoff)
+    Cbuf, Cv, ldc = placed(C0, cpad, coff)
+    Bd = to_dev(B, dev)
+    for rep in range(2):   # the same bits every time
+        Cv.copy_(to_dev(C0, dev))
+        sg.gemm(Av, Bd, Cv, alpha, beta, ta, 0, config=config, sched=sched)
+        torch.cuda.synchronize()
+        C_ref, _ = oracle.gemm_blas(As, B, C0, alpha, beta, ta, 0)
+        assert np.array_equal(Cv.cpu().numpy().astype(np.float64), C_ref), f"repeat {rep}"
+    full = torch.as_strided(Cbuf, (M, ldc), (ldc, 1), coff).cpu().numpy()
+    assert np.all(np.isnan(full[:, N:])), "ldc padding was written"
+
+
+def test_skinny_rows_full_size_sampled(dev):
+    """16 x 8192 x 16384 (B: 512 MiB) on the skinny kernel, every output
+    against the oracle (integer inputs: |partial sums| <= 16 K = 2^18, exact
+    in FP32)."""
+    import torch
+    M, N, K = 16, 8192, 16384
+    log(f"case skinny full size ({M},{N},{K})")
+    A, B = workloads.generate(M, N, K, "int4", 103)
+    C = gpu_matmul(A, B, dev, sg.CFG_SKINNY_16x256)
+    C_ref, _ = oracle.gemm(A, B)
+    assert np.array_equal(C.astype(np.float64), C_ref)
