@@ -48,7 +48,8 @@ CFG_DL_128x256x16 = 20
 CFG_DL_256x128x16 = 21
 CFG_GENERIC_64x64x16 = 22
 CFG_SKINNY_16x256 = 23
-NUM_CFGS = 24
+CFG_ROWDOT_N8 = 24
+NUM_CFGS = 25
 CFG_NAMES = {
     CFG_AUTO: "auto",
     CFG_MFMA_256x256x16: "mfma_256x256x16",
@@ -74,6 +75,7 @@ CFG_NAMES = {
     CFG_DL_256x128x16: "dl_256x128x16",
     CFG_GENERIC_64x64x16: "generic_64x64x16",
     CFG_SKINNY_16x256: "skinny_16x256",
+    CFG_ROWDOT_N8: "rowdot_n8",
 }
 # (tile_m, tile_n, tile_k) of each configuration.
 CFG_TILES = {

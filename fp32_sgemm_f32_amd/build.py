@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsgemm_f32.so")
 
-SOURCES = ["sgemm_f32.hip", "plan.cpp", "gemm_mfma.hip", "gemm_mfma_dl.hip", "gemm_generic.hip", "gemm_valu.hip", "pack.hip", "sk_fixup.hip", "skinny.hip"]
+SOURCES = ["sgemm_f32.hip", "plan.cpp", "gemm_mfma.hip", "gemm_mfma_dl.hip", "gemm_generic.hip", "gemm_valu.hip", "pack.hip", "sk_fixup.hip", "skinny.hip", "rowdot.hip"]
 ARCH = "gfx950"
 
 COMMON = [

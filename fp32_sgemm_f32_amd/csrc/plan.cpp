@@ -39,6 +39,7 @@ const CfgInfo kCfgs[] = {
     {SGEMM_CFG_DL_256x128x16, 256, 128, 16, 256, kKindMfmaDl, 2, false, false, "dl_256x128x16"},
     {SGEMM_CFG_GENERIC_64x64x16, 64, 64, 16, 256, kKindGeneric, 2, true, true, "generic_64x64x16"},
     {SGEMM_CFG_SKINNY_16x256, 16, 256, kSkinnyBlock, 512, kKindSkinny, 1, true, true, "skinny_16x256"},
+    {SGEMM_CFG_ROWDOT_N8, 4, 8, 0, 256, kKindRowdot, 2, true, true, "rowdot_n8"},
 };
 const int kNumCfgs = SGEMM_NUM_CFGS;
 
@@ -59,6 +60,10 @@ static bool divides(const CfgInfo &c, int M, int N, int K) {
 // The skinny kernel: at most 16 rows, B stored K x N with the vector layout
 // (A and C are read and written one float at a time, in any layout).
 static bool skinny_fits(const PlanRequest &r) { return r.M <= 16 && !r.trans_b && r.b_vector; }
+
+// The row-dot kernel: at most 8 columns, A stored M x K with 16-byte rows
+// (B and C are read and written one float at a time, in any layout).
+static bool rowdot_fits(const PlanRequest &r) { return r.N >= 1 && r.N <= 8 && !r.trans_a && r.a_rows16; }
 
 static bool fits(const CfgInfo &c, int M, int N, int K, bool aligned, bool transposed) {
     if (c.kind == kKindGeneric) return true;
@@ -115,6 +120,13 @@ static bool covers_well(int cfg, int M, int N) {
 //     per CU and keeps twice the loads in flight, which such shapes, with
 //     little reuse of the long operand, need (131072x64x1024: 114 against
 //     105; 8192x384x4096: 144 against 140).
+//   * at most 2 columns (or 8 once A has 2^26 elements), A stored M x K
+//     with 16-byte rows, M and K at least 256: the row-dot kernel (per-row
+//     dot products streaming A; y = A x).  16384 x 1 x 16384: 209 us against
+//     1190 on the general kernel and 216 for hipBLASLt; 16384 x 8 x 16384:
+//     231 against 264 on the tiled kernel.  At 4096 x 8 x 4096 the tiled
+//     kernel is faster (26 against 41 us): staging B per workgroup costs as
+//     much as the little A each one streams;
 //   * at most 8 rows, B stored K x N with the vector layout, N and K at
 //     least 256: the skinny kernel, which streams B without computing the
 //     empty rows of a 64-row tile (1 x 16384 x 16384: 5.9 TB/s of B against
@@ -125,6 +137,9 @@ static bool covers_well(int cfg, int M, int N) {
 static int auto_config(const PlanRequest &r, int cus, bool aligned) {
     const int M = r.M, N = r.N, K = r.K;
     if (skinny_fits(r) && M <= 8 && N >= 256 && K >= 256) return SGEMM_CFG_SKINNY_16x256;
+    if (rowdot_fits(r) && M >= 256 && K >= 256 && (N <= 2 || (int64_t)M * K >= ((int64_t)1 << 26)) &&
+        (r.sched != SGEMM_SCHED_DP || K <= kRowdotFloats / rowdot_cols(N)))
+        return SGEMM_CFG_ROWDOT_N8;
     if (!aligned) return SGEMM_CFG_GENERIC_64x64x16;
     const int big = SGEMM_CFG_DL_256x256x16, mid = SGEMM_CFG_DL_128x128x32, small = SGEMM_CFG_DL_64x64x64,
               small32 = SGEMM_CFG_DL_64x64x32;
@@ -201,6 +216,57 @@ static int plan_skinny(const PlanRequest &req, int cus, Plan *out) {
     return SGEMM_OK;
 }
 
+// The row-dot kernel's plan, in the same terms: a "tile" is a block of
+// rows (all 8 columns), its "K chunks" are the KS splits of K, every
+// workgroup owns one (block, split) step.  KS is at least what fits B's
+// split in LDS; blocks and splits give about two workgroups per CU; a
+// data-parallel schedule needs B's whole K range to fit.
+static int plan_rowdot(const PlanRequest &req, int cus, int occ, Plan *out) {
+    if (!rowdot_fits(req)) return SGEMM_ERR_CONFIG;
+    const CfgInfo &c = kCfgs[SGEMM_CFG_ROWDOT_N8];
+    const int M = req.M, K = req.K;
+    const int kb = kRowdotFloats / rowdot_cols(req.N);   // k of one split at most
+    int ks = K > 0 ? (K + kb - 1) / kb : 1;
+    if (req.sched == SGEMM_SCHED_DP && ks > 1) return SGEMM_ERR_CONFIG;
+    const int64_t target = (int64_t)cus * occ;
+    const int64_t rb_max = M > 0 ? (M + 3) / 4 : 0;   // blocks of at least 4 rows
+    int64_t rb = target / ks > 1 ? target / ks : 1;
+    if (rb > rb_max) rb = rb_max;
+    if (req.sched != SGEMM_SCHED_DP && rb > 0 && rb * ks < target) {
+        // Few rows: split K further (at least 256 k per split).
+        int64_t more = (target + rb - 1) / rb;
+        const int64_t by_k = K / 256 > 1 ? K / 256 : 1;
+        if (more > by_k) more = by_k;
+        if (more > ks) ks = (int)more;
+    }
+    if (req.sched == SGEMM_SCHED_STREAMK && ks < 2 && K >= 8) ks = 2;
+    Plan p{};
+    p.config = SGEMM_CFG_ROWDOT_N8;
+    p.threads = c.threads;
+    p.bn = c.bn;
+    p.bm = rb > 0 ? (int)((M + rb - 1) / rb) : c.bm;
+    p.tiles_m = M > 0 ? (M + p.bm - 1) / p.bm : 0;
+    p.tiles_n = req.N > 0 ? 1 : 0;
+    p.bk = K > 0 ? rowdot_k_per(K, ks) : 1;
+    p.ipt = K > 0 ? (K + p.bk - 1) / p.bk : 0;
+    p.edge = 1;
+    const int tiles = p.tiles_m * p.tiles_n;
+    if (tiles == 0 || p.ipt == 0 || (p.ipt == 1 && req.sched != SGEMM_SCHED_STREAMK)) {
+        p.dp_tiles = tiles; p.sk_tiles = 0; p.sk_grid = 0; p.grid = tiles;
+        p.sched = SGEMM_SCHED_DP;
+    } else {
+        p.dp_tiles = 0; p.sk_tiles = tiles;
+        p.sk_iters = (int64_t)tiles * p.ipt;
+        p.sk_grid = (int)p.sk_iters; p.grid = p.sk_grid;
+        p.sched = SGEMM_SCHED_STREAMK;
+        p.workspace_bytes = (int64_t)p.sk_grid * p.bm * c.bn * 4;   // [KS][rows][8], rows padded to blocks
+    }
+    p.xcd_remap = 0;
+    p.group_m = 1;
+    *out = p;
+    return SGEMM_OK;
+}
+
 int make_plan(const PlanRequest &req, Plan *out) {
     const int M = req.M, N = req.N, K = req.K;
     if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SHAPE;
@@ -213,6 +279,7 @@ int make_plan(const PlanRequest &req, Plan *out) {
     if (cfg == SGEMM_CFG_AUTO) cfg = auto_config(req, cus, aligned);
     const CfgInfo &c = kCfgs[cfg];
     if (c.kind == kKindSkinny) return plan_skinny(req, cus, out);
+    if (c.kind == kKindRowdot) return plan_rowdot(req, cus, occ_of(req, cfg), out);
     if (!fits(c, M, N, K, aligned, transposed)) return SGEMM_ERR_CONFIG;
 
     Plan p{};

@@ -14,10 +14,19 @@ enum CfgKind {
     kKindMfmaDl = 2,    // matrix cores, tiles loaded straight into LDS
     kKindGeneric = 3,   // matrix cores, element-wise bounds-checked loads (any shape/alignment)
     kKindSkinny = 4,    // scalar VALU FMAs over the M <= 16 rows only, B streamed
+    kKindRowdot = 5,    // per-row dot products for N <= 8 columns, A streamed
 };
 
 // K values of A staged in LDS at a time by the skinny kernel.
 constexpr int kSkinnyBlock = 512;
+
+// The row-dot kernel (N <= 8): floats of B held in LDS per workgroup
+// (64 KiB), for its columns rounded up to 1, 2, 4 or 8, and the k of one K
+// split (rounded up to a multiple of 4, so splits start on 16-byte
+// boundaries of A's rows).
+constexpr int kRowdotFloats = 16384;
+inline int rowdot_cols(int N) { return N <= 2 ? (N < 1 ? 1 : N) : N <= 4 ? 4 : 8; }
+inline int rowdot_k_per(int K, int splits) { return ((K + splits - 1) / splits + 3) & ~3; }
 
 struct CfgInfo {
     int id;
@@ -54,6 +63,7 @@ struct PlanRequest {
     int trans_b = 0;     // B stored N x K
     int b_vector = 0;    // B alone has the vector layout: 16-byte aligned, ldb and the
                          // stored row length multiples of 4, and N too
+    int a_rows16 = 0;    // A stored M x K with rows on 16-byte boundaries (aligned, lda % 4 == 0)
 };
 
 struct Plan {

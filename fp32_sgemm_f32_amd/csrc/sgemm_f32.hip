@@ -49,6 +49,7 @@ hipError_t launch_cfg(int cfg, const KernelArgs &a, hipStream_t s) {
     case kKindMfmaDl: return launch_mfma_dl(cfg, a, s);
     case kKindGeneric: return launch_generic(cfg, a, s);
     case kKindSkinny: return launch_skinny(cfg, a, s);
+    case kKindRowdot: return launch_rowdot(cfg, a, s);
     default: return launch_valu(cfg, a, s);
     }
 }
@@ -59,6 +60,7 @@ hipError_t occupancy_of(int cfg, int *n) {
     case kKindMfmaDl: return occupancy_mfma_dl(cfg, n);
     case kKindGeneric: return occupancy_generic(cfg, n);
     case kKindSkinny: return occupancy_skinny(cfg, n);
+    case kKindRowdot: return occupancy_rowdot(cfg, n);
     default: return occupancy_valu(cfg, n);
     }
 }
@@ -189,6 +191,13 @@ bool vector_b(const Call &c) {
     return (c.b_cols() & 3) == 0 && (c.N & 3) == 0 && (c.ldb & 3) == 0 && ((uintptr_t)c.B & 15) == 0;
 }
 
+// A stored M x K with rows on 16-byte boundaries (what the row-dot kernel needs).
+bool rows16_a(const Call &c) { return !c.ta && (c.lda & 3) == 0 && ((uintptr_t)c.A & 15) == 0; }
+
+// Kernels that read A or B and write C one float at a time where needed, so
+// that no layout calls for repacking them.
+bool any_layout(int cfg) { return kCfgs[cfg].kind == kKindSkinny || kCfgs[cfg].kind == kKindRowdot; }
+
 // Stream-K workspace of (dev, stream), grown to hold `plan`'s partial
 // tiles.  Caller holds g_mu.
 int workspace_for(int dev, hipStream_t s, const Plan &p, Workspace *out) {
@@ -306,14 +315,14 @@ int run(const Call &c) {
     if ((st = device_info(dev, &info)) != SGEMM_OK) return st;
     PlanRequest req{c.M, c.N, c.K, c.config, c.sched, info.num_cus, info.occupancy,
                     env_int("SGEMM_F32_SK_WG_PER_CU", 0), vector_ab(c) && (c_own || vector_c(c)) ? 1 : 0,
-                    c.ta, c.tb, vector_b(c) ? 1 : 0};
+                    c.ta, c.tb, vector_b(c) ? 1 : 0, rows16_a(c) ? 1 : 0};
     Plan p;
     if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
-    // An automatic choice other than the skinny kernel (which reads A and
-    // writes C in any layout) on a layout the vector kernels cannot load:
+    // An automatic choice other than the kernels that take any layout of
+    // their small operands, on a layout the vector kernels cannot load:
     // large products run on repacked copies.
-    if (!c.repacked && c.config == SGEMM_CFG_AUTO && c.reads_ab() && kCfgs[p.config].kind != kKindSkinny &&
-        !vector_layout(c) && worth_repacking(c))
+    if (!c.repacked && c.config == SGEMM_CFG_AUTO && c.reads_ab() && !any_layout(p.config) && !vector_layout(c) &&
+        worth_repacking(c))
         return run_packed(c, dev);
     if (c_own) p.edge = 1;
     if (c.K > 0 && !dl_offsets_fit(p.config, p.edge != 0, c.lda, c.ldb, c.ta != 0, c.tb != 0)) {
@@ -358,8 +367,8 @@ int run(const Call &c) {
         Workspace w;
         if ((st = workspace_for(dev, c.stream, p, &w)) != SGEMM_OK) return st;
         a.partials = w.partials;
-        e = launch_cfg(p.config, a, c.stream);   // the skinny kernel adds its own splits
-        if (e == hipSuccess && kCfgs[p.config].kind != kKindSkinny) e = launch_sk_fixup(a, p.bm, p.bn, c.stream);
+        e = launch_cfg(p.config, a, c.stream);   // the skinny and row-dot kernels add their own splits
+        if (e == hipSuccess && !any_layout(p.config)) e = launch_sk_fixup(a, p.bm, p.bn, c.stream);
     } else {
         e = launch_cfg(p.config, a, c.stream);
     }
@@ -439,16 +448,17 @@ static int plan_for(int ta, int tb, int M, int N, int K, int config, int sched, 
     const int a_cols = ta ? M : K, b_cols = tb ? K : N;
     const bool aligned = a_cols % 4 == 0 && b_cols % 4 == 0 && N % 4 == 0;
     const bool b_vector = b_cols % 4 == 0 && N % 4 == 0;
+    const bool a_rows16 = !ta && K % 4 == 0;
     sgemm::Call c = sgemm::plain(M, N, K, nullptr, a_cols, nullptr, b_cols, nullptr, N, nullptr, config, sched);
     c.ta = ta;
     c.tb = tb;
     sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu, aligned ? 1 : 0, ta, tb,
-                           b_vector ? 1 : 0};
+                           b_vector ? 1 : 0, a_rows16 ? 1 : 0};
     sgemm::Plan p;
     int st = sgemm::make_plan(req, &p);
     if (st != SGEMM_OK) return st;
     const bool repack = !aligned && config == SGEMM_CFG_AUTO && K > 0 && M > 0 && N > 0 &&
-                        sgemm::kCfgs[p.config].kind != sgemm::kKindSkinny && sgemm::worth_repacking(c);
+                        !sgemm::any_layout(p.config) && sgemm::worth_repacking(c);
     if (repack) {
         req.M = ta ? sgemm::up4(M) : M;
         req.N = sgemm::up4(N);

@@ -148,7 +148,13 @@ extern "C" {
  * over the M rows only, B streamed once, K split over the grid.  The
  * automatic choice takes it for such products with M <= 8, N, K >= 256. */
 #define SGEMM_CFG_SKINNY_16x256     23 /* 512 threads, 8 waves over 256 columns */
-#define SGEMM_NUM_CFGS              24 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
+/* At most 8 columns (N <= 8, y = A x among them), A stored M x K with rows
+ * on 16-byte boundaries (aligned, lda a multiple of 4; B and C in any
+ * layout): per-row dot products, A streamed once, B held in LDS.  The
+ * automatic choice takes it for such products with M, K >= 256 and N <= 2,
+ * or N <= 8 once M * K >= 2^26. */
+#define SGEMM_CFG_ROWDOT_N8         24 /* 256 threads, 4 waves over rows of A */
+#define SGEMM_NUM_CFGS              25 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
 /* The configurations not named above as running other shapes or storage
  * orders need A stored M x K, B stored K x N, the vector layout and a shape
  * their tile divides. */

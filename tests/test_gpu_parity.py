@@ -57,6 +57,8 @@ def fits(config, M, N, K, vector=None):
         return True
     if config == sg.CFG_SKINNY_16x256:   # dense B rows of N floats on 16-byte boundaries
         return M <= 16 and N % 4 == 0
+    if config == sg.CFG_ROWDOT_N8:       # dense A rows of K floats on 16-byte boundaries
+        return N <= 8 and K % 4 == 0
     if vector is None:
         vector = N % 4 == 0 and K % 4 == 0
     if not vector:
@@ -105,7 +107,7 @@ def test_integer_inputs_bit_exact(dev, config, sched):
     """Entries in {-4..4} with K <= 1024: every partial sum is an integer below
     2^24, exact in FP32 in any order, so every variant must match exactly
     (16 rows for the skinny kernel, which runs at most that many)."""
-    M, N, K = (16 if config == sg.CFG_SKINNY_16x256 else 512), 768, 1024
+    M, N, K = (16 if config == sg.CFG_SKINNY_16x256 else 512), (8 if config == sg.CFG_ROWDOT_N8 else 768), 1024
     log(f"case int4 config={sg.CFG_NAMES[config]} sched={sg.SCHED_NAMES[sched]}")
     A, B = workloads.generate(M, N, K, "int4", 77)
     C = gpu_matmul(A, B, dev, config, sched)
@@ -115,7 +117,7 @@ def test_integer_inputs_bit_exact(dev, config, sched):
 
 @pytest.mark.parametrize("config", CONFIGS, ids=lambda c: sg.CFG_NAMES[c])
 def test_identity_b_gives_a(dev, config):
-    M, K = (16 if config == sg.CFG_SKINNY_16x256 else 512), 256
+    M, K = (16 if config == sg.CFG_SKINNY_16x256 else 512), (8 if config == sg.CFG_ROWDOT_N8 else 256)
     log(f"case identity config={sg.CFG_NAMES[config]}")
     A, _ = workloads.generate(M, K, K, "normal", 5)
     C = gpu_matmul(A, np.eye(K, dtype=np.float32), dev, config, sg.SCHED_STREAMK)
@@ -317,13 +319,13 @@ def test_storage_orders_integer_inputs_bit_exact(dev, config, layout):
 
 @pytest.mark.parametrize("config", [sg.CFG_MFMA_256x256x16, sg.CFG_MFMA_128x128x32, sg.CFG_VALU_128x128x8,
                                     sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_GENERIC_64x64x16,
-                                    sg.CFG_SKINNY_16x256],
+                                    sg.CFG_SKINNY_16x256, sg.CFG_ROWDOT_N8],
                          ids=lambda c: sg.CFG_NAMES[c])
 def test_blas_scaling_on_every_kernel_family(dev, config):
     """alpha / beta in the epilogue of each kernel family, whole tiles and
     Stream-K (the scaling is applied once, after the partial sums)."""
     import torch
-    M, N, K = (13 if config == sg.CFG_SKINNY_16x256 else 512), 512, 768
+    M, N, K = (13 if config == sg.CFG_SKINNY_16x256 else 512), (5 if config == sg.CFG_ROWDOT_N8 else 512), 768
     log(f"case blas scaling config={sg.CFG_NAMES[config]}")
     A, B = workloads.generate(M, N, K, "int4", 61)
     C0 = workloads.generate(M, 1, N, "int4", 62)[0]
@@ -973,5 +975,70 @@ def test_skinny_rows_full_size_sampled(dev):
     log(f"case skinny full size ({M},{N},{K})")
     A, B = workloads.generate(M, N, K, "int4", 103)
     C = gpu_matmul(A, B, dev, sg.CFG_SKINNY_16x256)
+    C_ref, _ = oracle.gemm(A, B)
+    assert np.array_equal(C.astype(np.float64), C_ref)
+
+
+# Products with at most 8 columns: the row-dot kernel (per-row dot products
+# streaming A, B held in LDS, K split over the grid and the splits added in
+# order).  (M, N, K, trans_b, A pad, B pad / offset, C pad / offset, alpha,
+# beta, schedule); A's padding keeps its rows on 16-byte boundaries.
+ROWDOT_CASES = {
+    "gemv": (16384, 1, 4096, 0, 0, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_AUTO),
+    "n2_k_tail": (3000, 2, 1021, 0, 3, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_AUTO),
+    "n3_tb_beta": (1000, 3, 5000, 1, 0, (0, 0), (0, 0), -0.5, 2.0, sg.SCHED_AUTO),
+    "n5_split_many": (256, 5, 65536, 0, 0, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_AUTO),
+    "n8_dp": (4099, 8, 2044, 0, 0, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_DP),
+    "n8_streamk_odd_ld": (2500, 8, 3000, 1, 4, (3, 1), (5, 2), 2.0, -1.0, sg.SCHED_STREAMK),
+    "n1_b_offset": (777, 1, 9999, 0, 1, (0, 1), (1, 1), 1.0, 0.0, sg.SCHED_AUTO),
+}
+
+
+@pytest.mark.parametrize("case", list(ROWDOT_CASES))
+def test_rowdot_columns(dev, case):
+    import torch
+    M, N, K, tb, apad, (bpad, boff), (cpad, coff), alpha, beta, sched = ROWDOT_CASES[case]
+    assert (K + apad) % 4 == 0
+    # The plan query assumes dense operands: shown for the cases that are.
+    p = sg.plan(M, N, K, sg.CFG_ROWDOT_N8, sched, trans_b=tb) if apad == 0 else "padded A"
+    log(f"case rowdot {case}: shape=({M},{N},{K}) tb={tb} A pad={apad} B pad/off={bpad}/{boff} "
+        f"C pad/off={cpad}/{coff} alpha={alpha} beta={beta} plan={p}")
+    A, B = workloads.generate(M, N, K, "int4", 104)
+    Bs = stored(B, tb)
+    C0 = workloads.generate(M, 1, N, "int4", 105)[0]
+
+    def placed(X, pad, off):
+        rows, cols = X.shape
+        ld = cols + pad
+        buf = torch.full((rows * ld + off + 4,), float("nan"), dtype=torch.float32, device=dev)
+        view = torch.as_strided(buf, (rows, cols), (ld, 1), off)
+        view.copy_(to_dev(X, dev))
+        return buf, view, ld
+
+    _, Av, _ = placed(A, apad, 0)
+    _, Bv, _ = placed(Bs, bpad, boff)
+    Cbuf, Cv, ldc = placed(C0, cpad, coff)
+    for rep in range(2):   # the same bits every time
+        Cv.copy_(to_dev(C0, dev))
+        sg.gemm(Av, Bv, Cv, alpha, beta, 0, tb, config=sg.CFG_ROWDOT_N8, sched=sched)
+        torch.cuda.synchronize()
+        C_ref, _ = oracle.gemm_blas(A, Bs, C0, alpha, beta, 0, tb)
+        assert np.array_equal(Cv.cpu().numpy().astype(np.float64), C_ref), f"repeat {rep}"
+    full = torch.as_strided(Cbuf, (M, ldc), (ldc, 1), coff).cpu().numpy()
+    assert np.all(np.isnan(full[:, N:])), "ldc padding was written"
+
+
+@pytest.mark.parametrize("shape", [(16384, 1, 16384), (32768, 2, 4096), (65536, 4, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_rowdot_is_the_automatic_choice(dev, shape):
+    """Where the automatic choice runs the row-dot kernel, it matches the
+    oracle exactly (integer inputs, K <= 16384)."""
+    import torch
+    M, N, K = shape
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    assert sg.plan(M, N, K, num_cus=cus)["config"] == sg.CFG_ROWDOT_N8
+    log(f"case rowdot auto {shape}")
+    A, B = workloads.generate(M, N, K, "int4", 106)
+    C = gpu_matmul(A, B, dev)
     C_ref, _ = oracle.gemm(A, B)
     assert np.array_equal(C.astype(np.float64), C_ref)

@@ -13,7 +13,7 @@ import pytest
 
 import fp32_sgemm_f32_amd as sg
 
-OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1, 2, 1, 1, 1, 2, 1, 1, 2, 2, 2, 1]
+OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1, 2, 1, 1, 1, 2, 1, 1, 2, 2, 2, 1, 2]
 EDGE_CFGS = {sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32, sg.CFG_DL_256x256x16,
              sg.CFG_GENERIC_64x64x16}
 
@@ -104,7 +104,7 @@ def check_plan(p, M, N, K):
         assert sorted(ws) == list(range(min(ws), max(ws) + 1))
     # Two partial slots per split workgroup; one for the skinny kernel, whose
     # workgroups each own a single (strip, split) step.
-    slots = 1 if p["config"] == sg.CFG_SKINNY_16x256 else 2
+    slots = 1 if p["config"] in (sg.CFG_SKINNY_16x256, sg.CFG_ROWDOT_N8) else 2
     need = p["sk_grid"] * slots * p["tile_m"] * p["tile_n"] * 4 if p["sk_tiles"] else 0
     assert p["workspace_bytes"] >= need
     return per_tile
@@ -113,7 +113,8 @@ def check_plan(p, M, N, K):
 SHAPES = [(128, 128, 32), (256, 256, 256), (512, 384, 96), (1024, 1024, 1024), (1024, 1024, 16384),
           (2048, 2048, 2048), (4096, 4096, 4096), (1280, 768, 640), (3072, 2048, 352),
           (1, 1, 1), (7, 13, 5), (100, 196, 36), (1000, 1000, 1000), (4095, 4096, 4092), (300, 17, 9000),
-          (16, 4096, 4096), (1, 256, 1), (5, 1028, 300), (16, 256, 65536)]
+          (16, 4096, 4096), (1, 256, 1), (5, 1028, 300), (16, 256, 65536),
+          (4096, 1, 4096), (300, 8, 20000), (7, 3, 12), (100000, 5, 64)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -131,6 +132,10 @@ def test_every_step_covered_once(shape, config, sched, cus):
         assert e.status == sg.ERR_CONFIG and config != sg.CFG_AUTO
         if config == sg.CFG_SKINNY_16x256:   # at most 16 rows, B rows of N floats, N a multiple of 4
             assert M > 16 or N % 4
+            return
+        if config == sg.CFG_ROWDOT_N8:       # at most 8 columns, A rows of K floats, K a multiple of 4;
+            cols = 1 if N <= 1 else 2 if N == 2 else 4 if N <= 4 else 8      # whole K in LDS for DP
+            assert N > 8 or K % 4 or (sched == sg.SCHED_DP and K > 16384 // cols)
             return
         bm, bn, bk = sg.CFG_TILES[config]
         divides = M % bm == 0 and N % bn == 0 and K % bk == 0
