@@ -32,6 +32,7 @@ import numpy as np  # noqa: E402
 import workloads  # noqa: E402
 
 PEAK_FP32_TFLOPS = 157.3          # MI355X dense FP32 (vector with packed FMA, or matrix)
+PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
 PEAK_HBM_GBS = 8000.0
 # The pages' own kernel at 4096^3 on an H100 (context, other hardware): "Beyond
 # Kernel 7", section "The confirmed result", k13f 2761.2 us = 49.8 TFLOP/s.
@@ -324,11 +325,19 @@ def main():
             and TRAFFIC["source_digest"] == kernel_source_digest()):
         traffic = TRAFFIC["bytes"]
     # The vector-ALU kernel is bounded by the FP32 vector rate (157.3 TFLOP/s
-    # too), the others by the FP32 matrix-core rate.
-    bound = "alu" if head["plan"]["config"] == sg.CFG_VALU_128x128x8 else "mfma"
-    roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic,
-                "traffic_unit": "bytes per launch"}
+    # too), the skinny and row-dot kernels (at most 16 rows / 8 columns) by
+    # HBM: their algorithmic bytes are A, B and C once, 4 (MK + KN + MN);
+    # the others by the FP32 matrix-core rate.
+    cfg = head["plan"]["config"]
+    if cfg in (sg.CFG_SKINNY_16x256, sg.CFG_ROWDOT_N8):
+        gbps = 4 * (w.M * w.K + w.K * w.N + w.M * w.N) / (head["region_event_ms_per_call"] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "traffic_unit": "bytes per launch"}
+    else:
+        bound = "alu" if cfg == sg.CFG_VALU_128x128x8 else "mfma"
+        roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic,
+                    "traffic_unit": "bytes per launch"}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
