@@ -39,7 +39,7 @@ const CfgInfo kCfgs[] = {
     {SGEMM_CFG_DL_256x128x16, 256, 128, 16, 256, kKindMfmaDl, 2, false, false, "dl_256x128x16"},
     {SGEMM_CFG_GENERIC_64x64x16, 64, 64, 16, 256, kKindGeneric, 2, true, true, "generic_64x64x16"},
     {SGEMM_CFG_SKINNY_16x256, 16, 256, kSkinnyBlock, 512, kKindSkinny, 1, true, true, "skinny_16x256"},
-    {SGEMM_CFG_ROWDOT_N8, 4, 8, 0, 256, kKindRowdot, 2, true, true, "rowdot_n8"},
+    {SGEMM_CFG_ROWDOT_N8, 8, 8, 0, 512, kKindRowdot, 2, true, true, "rowdot_n8"},
 };
 const int kNumCfgs = SGEMM_NUM_CFGS;
 
@@ -229,7 +229,7 @@ static int plan_rowdot(const PlanRequest &req, int cus, int occ, Plan *out) {
     int ks = K > 0 ? (K + kb - 1) / kb : 1;
     if (req.sched == SGEMM_SCHED_DP && ks > 1) return SGEMM_ERR_CONFIG;
     const int64_t target = (int64_t)cus * occ;
-    const int64_t rb_max = M > 0 ? (M + 3) / 4 : 0;   // blocks of at least 4 rows
+    const int64_t rb_max = M > 0 ? (M + 7) / 8 : 0;   // blocks of at least a row per wave
     int64_t rb = target / ks > 1 ? target / ks : 1;
     if (rb > rb_max) rb = rb_max;
     if (req.sched != SGEMM_SCHED_DP && rb > 0 && rb * ks < target) {

@@ -153,7 +153,7 @@ extern "C" {
  * layout): per-row dot products, A streamed once, B held in LDS.  The
  * automatic choice takes it for such products with M, K >= 256 and N <= 2,
  * or N <= 8 once M * K >= 2^26. */
-#define SGEMM_CFG_ROWDOT_N8         24 /* 256 threads, 4 waves over rows of A */
+#define SGEMM_CFG_ROWDOT_N8         24 /* 512 threads, 8 waves over rows of A */
 #define SGEMM_NUM_CFGS              25 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
 /* The configurations not named above as running other shapes or storage
  * orders need A stored M x K, B stored K x N, the vector layout and a shape
