@@ -1042,3 +1042,38 @@ def test_rowdot_is_the_automatic_choice(dev, shape):
     C = gpu_matmul(A, B, dev)
     C_ref, _ = oracle.gemm(A, B)
     assert np.array_equal(C.astype(np.float64), C_ref)
+
+
+@pytest.mark.parametrize("shape", [(4, 4096, 4096), (8192, 8, 8192)], ids=["skinny", "rowdot"])
+def test_graph_capture_of_thin_products(dev, shape):
+    """The skinny and row-dot kernels with K split (partials in the stream's
+    workspace, a second kernel adding them) captured after an eager call of
+    the same shape: every replay, with new A and eager work in between,
+    matches the oracle and the eager result exactly (integer inputs)."""
+    import torch
+    M, N, K = shape
+    p = sg.plan(M, N, K, num_cus=torch.cuda.get_device_properties(dev).multi_processor_count)
+    assert p["config"] in (sg.CFG_SKINNY_16x256, sg.CFG_ROWDOT_N8) and p["sk_tiles"] > 0
+    log(f"case graph capture thin {shape} plan={p}")
+    s = torch.cuda.Stream(device=dev)
+    A0, B = workloads.generate(M, N, K, "int4", 107)
+    Ad, Bd = to_dev(A0, dev), to_dev(B, dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    with torch.cuda.stream(s):
+        sg.gemm(Ad, Bd, C)                                  # eager: workspace ready
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        sg.gemm(Ad, Bd, C)
+    torch.cuda.synchronize()
+    for r in range(3):
+        A_r = workloads.generate(M, N, K, "int4", 230 + r)[0]
+        Ad.copy_(to_dev(A_r, dev))
+        E = sg.matmul(Ad, Bd)                               # eager reference on the device
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        C_ref, _ = oracle.gemm(A_r, B)
+        got = C.cpu().numpy()
+        assert np.array_equal(got.astype(np.float64), C_ref), f"replay {r}"
+        assert np.array_equal(got, E.cpu().numpy()), f"replay {r} vs eager"
