@@ -28,7 +28,11 @@
  *   of the library (each only when its own layout does not qualify) and the
  *   product runs on the vector kernels, which then write C in place (one
  *   float at a time when C's layout does not qualify; results as unpadded,
- *   C's padding untouched).
+ *   C's padding untouched).  Thin products have kernels of their own, for
+ *   which only the streamed operand needs 16-byte rows: at most 8 rows
+ *   with B stored K x N (SGEMM_CFG_SKINNY_16x256), at most 2 columns, or 8
+ *   for large A, with A stored M x K (SGEMM_CFG_ROWDOT_N8); the other
+ *   operand and C may have any layout.
  *
  * Memory and ownership
  *   A, B, C are device pointers, caller-owned, allocated on the HIP device
