@@ -131,8 +131,9 @@ static bool covers_well(int cfg, int M, int N) {
 //     least 256: the skinny kernel, which streams B without computing the
 //     empty rows of a 64-row tile (1 x 16384 x 16384: 5.9 TB/s of B against
 //     4.4 for the tiled kernel and 5.8 for hipBLASLt; 8 x 8192 x 28672: 5.5
-//     against 4.3 and 4.9).  Its 16-row form runs when asked for but is
-//     slower than the tiled kernels (16 x 16384 x 16384: 3.7 TB/s).
+//     against 4.3 and 4.9).  For 9-16 rows (two groups of 8 rows per
+//     workgroup) it only ties the tiled kernel (16 x 16384 x 16384: 4.2
+//     against 4.3 TB/s; 12 rows 4.4 against 4.3) and runs when asked for.
 // Layouts the vector kernels cannot load go to the general kernel.
 static int auto_config(const PlanRequest &r, int cus, bool aligned) {
     const int M = r.M, N = r.N, K = r.K;

@@ -11,9 +11,10 @@
 //
 // Work: workgroup w of the grid owns column strip w / KS (256 columns) and
 // K split w % KS (ceil(K / KS) consecutive k).  Its 8 waves split that range
-// again, each lane holding 4 adjacent columns for all MR rows (MR = 4, 8 or
-// 16 >= M): per k one 16-byte B load and 4 * MR multiply-adds, 16 loads in
-// flight per lane.  Two waves per SIMD: the 16-row kernel's LDS (96 KiB)
+// again, each lane holding 4 adjacent columns for MRW rows (4 or 8): per k
+// one 16-byte B load and 4 * MRW multiply-adds, 16 loads in flight per lane.
+// For 9-16 rows the workgroup's two halves each take 8 of the rows over the
+// same columns and K range, four waves splitting it.  Two waves per SIMD: the 16-row kernel's LDS (96 KiB)
 // admits one workgroup per CU anyway, so each wave may use 256 registers.  A's values, the same for every lane, are staged in LDS
 // (k-major, MR floats per k) a block of 512 k at a time and read as
 // broadcasts.  The 8 waves' sums are added through LDS in a fixed tree
@@ -52,15 +53,22 @@ __device__ __forceinline__ void fma_k(float (&acc)[MR][4], const float *ap, cons
     }
 }
 
-template <int MR>
+// MRW rows per wave, H row groups per workgroup (MR = MRW * H rows in all):
+// with H = 2 the two halves of the workgroup take rows 0-7 and 8-15 of the
+// same columns and K range, each wave keeping the 32 accumulators of the
+// 8-row form (the second read of each B line comes from L2).
+template <int MRW, int H>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sgemm_skinny_kernel(KernelArgs a) {
     constexpr int kUnroll = 16;   // B loads in flight per lane
+    constexpr int MR = MRW * H;   // rows staged
+    constexpr int WH = kWaves / H;   // waves per row group
     // A block (k-major, MR floats per k), then the waves' sums.
     __shared__ __attribute__((aligned(16))) float as[kBlock * MR];
-    __shared__ __attribute__((aligned(16))) float red[(kWaves / 2) * MR * kCols];
+    __shared__ __attribute__((aligned(16))) float red[H * (WH / 2) * MRW * kCols];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int grp = wave / WH, sub = wave - grp * WH;   // row group, wave within it
     const int ks_count = a.ipt;
     const int strip = blockIdx.x / ks_count, ks = blockIdx.x - strip * ks_count;
     const int k_per = (a.K + ks_count - 1) / ks_count;
@@ -70,9 +78,9 @@ void sgemm_skinny_kernel(KernelArgs a) {
     const bool col_ok = n0 < a.N;   // N is a multiple of 4: a lane's 4 columns are all in or all out
     const float *bcol = a.B + n0;
 
-    float acc[MR][4];
+    float acc[MRW][4];
 #pragma unroll
-    for (int m = 0; m < MR; ++m)
+    for (int m = 0; m < MRW; ++m)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[m][j] = 0.0f;
 
@@ -90,7 +98,8 @@ void sgemm_skinny_kernel(KernelArgs a) {
         __syncthreads();
         // This wave's share of the block: whole groups of kUnroll k (all
         // loads first), then the remaining k one at a time.
-        const int w0 = blk + (blen * wave) / kWaves, w1 = blk + (blen * (wave + 1)) / kWaves;
+        const int w0 = blk + (blen * sub) / WH, w1 = blk + (blen * (sub + 1)) / WH;
+        const float *ag = as + grp * MRW;   // this group's rows of each k
         int k = w0;
         for (; k + kUnroll <= w1; k += kUnroll) {
             f32x4 b[kUnroll];
@@ -98,41 +107,43 @@ void sgemm_skinny_kernel(KernelArgs a) {
             for (int u = 0; u < kUnroll; ++u)
                 b[u] = col_ok ? *(const f32x4 *)(bcol + (int64_t)(k + u) * a.ldb) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) fma_k(acc, as + (k + u - blk) * MR, b[u]);
+            for (int u = 0; u < kUnroll; ++u) fma_k(acc, ag + (k + u - blk) * MR, b[u]);
         }
         for (; k < w1; ++k) {
             const f32x4 b = col_ok ? *(const f32x4 *)(bcol + (int64_t)k * a.ldb) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            fma_k(acc, as + (k - blk) * MR, b);
+            fma_k(acc, ag + (k - blk) * MR, b);
         }
     }
 
-    // Sum the 8 waves in a fixed tree: (w + 4), then (w + 2), then (w + 1).
+    // Sum each group's waves in a fixed tree: (w + WH/2), ..., then (w + 1).
+    float *const rg = red + grp * (WH / 2) * MRW * kCols;
 #pragma unroll
-    for (int half = kWaves / 2; half >= 1; half >>= 1) {
+    for (int half = WH / 2; half >= 1; half >>= 1) {
         __syncthreads();
-        if (wave >= half && wave < 2 * half) {
+        if (sub >= half && sub < 2 * half) {
 #pragma unroll
-            for (int m = 0; m < MR; ++m)
-                *(f32x4 *)(red + ((wave - half) * MR + m) * kCols + 4 * lane) =
+            for (int m = 0; m < MRW; ++m)
+                *(f32x4 *)(rg + ((sub - half) * MRW + m) * kCols + 4 * lane) =
                     f32x4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
         }
         __syncthreads();
-        if (wave < half) {
+        if (sub < half) {
 #pragma unroll
-            for (int m = 0; m < MR; ++m) {
-                const f32x4 v = *(const f32x4 *)(red + (wave * MR + m) * kCols + 4 * lane);
+            for (int m = 0; m < MRW; ++m) {
+                const f32x4 v = *(const f32x4 *)(rg + (sub * MRW + m) * kCols + 4 * lane);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[m][j] += v[j];
             }
         }
     }
-    if (wave != 0 || !col_ok) return;
+    if (sub != 0 || !col_ok) return;
+    const int row0 = grp * MRW;   // this group's first row
 
     if (ks_count == 1) {
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            if (m >= a.M) break;
-            float *c = a.C + (int64_t)m * a.ldc + n0;
+        for (int m = 0; m < MRW; ++m) {
+            if (row0 + m >= a.M) break;
+            float *c = a.C + (int64_t)(row0 + m) * a.ldc + n0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) c[j] = epilogue(a, acc[m][j], c + j);
         }
@@ -140,10 +151,10 @@ void sgemm_skinny_kernel(KernelArgs a) {
         // Partial sums, dense: split ks, row m, column n at
         // partials[(ks * 16 + m) * Np + n], Np = strips * 256.
         const int64_t np = (int64_t)a.tiles_n * kCols;
-        float *p = a.partials + (int64_t)ks * 16 * np + n0;
+        float *p = a.partials + ((int64_t)ks * 16 + row0) * np + n0;
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            if (m >= a.M) break;
+        for (int m = 0; m < MRW; ++m) {
+            if (row0 + m >= a.M) break;
             *(f32x4 *)(p + m * np) = f32x4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
         }
     }
@@ -176,11 +187,12 @@ __global__ __launch_bounds__(256) void sgemm_skinny_sum_kernel(KernelArgs a) {
     }
 }
 
-template <int MR>
+template <int MRW, int H>
 hipError_t launch_rows(const KernelArgs &a, hipStream_t s) {
     KernelArgs args = a;
     void *params[] = {&args};
-    hipError_t e = hipLaunchKernel((const void *)sgemm_skinny_kernel<MR>, dim3(a.grid), dim3(kThreads), params, 0, s);
+    hipError_t e =
+        hipLaunchKernel((const void *)sgemm_skinny_kernel<MRW, H>, dim3(a.grid), dim3(kThreads), params, 0, s);
     if (e != hipSuccess || a.ipt <= 1) return e;
     const int64_t threads = (int64_t)a.M * (a.N / 4);
     int64_t blocks = (threads + 255) / 256;
@@ -194,14 +206,14 @@ hipError_t launch_skinny(int cfg, const KernelArgs &a, hipStream_t s) {
     if (cfg != SGEMM_CFG_SKINNY_16x256 || a.M < 1 || a.M > 16 || a.N % 4 || a.trans_b ||
         (a.ipt > 1 && !a.partials))
         return hipErrorInvalidValue;
-    if (a.M <= 4) return launch_rows<4>(a, s);
-    if (a.M <= 8) return launch_rows<8>(a, s);
-    return launch_rows<16>(a, s);
+    if (a.M <= 4) return launch_rows<4, 1>(a, s);
+    if (a.M <= 8) return launch_rows<8, 1>(a, s);
+    return launch_rows<8, 2>(a, s);
 }
 
 hipError_t occupancy_skinny(int cfg, int *wg_per_cu) {
     if (cfg != SGEMM_CFG_SKINNY_16x256) return hipErrorInvalidValue;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(wg_per_cu, (const void *)sgemm_skinny_kernel<16>, kThreads,
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(wg_per_cu, (const void *)sgemm_skinny_kernel<8, 2>, kThreads,
                                                         0);
 }
 
