@@ -57,13 +57,13 @@ static bool divides(const CfgInfo &c, int M, int N, int K) {
 // Whether configuration c can run the shape: the generic kernel runs
 // anything; the others need the aligned fast-path layout, and a tile that
 // divides the shape unless they mask ragged edges.
-// The skinny kernel: at most 16 rows, B stored K x N with the vector layout
-// (A and C are read and written one float at a time, in any layout).
-static bool skinny_fits(const PlanRequest &r) { return r.M <= 16 && !r.trans_b && r.b_vector; }
+// The skinny kernel: at most 16 rows, B stored K x N (A and C read and
+// written one float at a time; B too where it is off the 16-byte grid).
+static bool skinny_fits(const PlanRequest &r) { return r.M <= 16 && !r.trans_b; }
 
-// The row-dot kernel: at most 8 columns, A stored M x K with 16-byte rows
-// (B and C are read and written one float at a time, in any layout).
-static bool rowdot_fits(const PlanRequest &r) { return r.N >= 1 && r.N <= 8 && !r.trans_a && r.a_rows16; }
+// The row-dot kernel: at most 8 columns, A stored M x K (B and C read and
+// written one float at a time; A too where it is off the 16-byte grid).
+static bool rowdot_fits(const PlanRequest &r) { return r.N >= 1 && r.N <= 8 && !r.trans_a; }
 
 static bool fits(const CfgInfo &c, int M, int N, int K, bool aligned, bool transposed) {
     if (c.kind == kKindGeneric) return true;
@@ -120,15 +120,16 @@ static bool covers_well(int cfg, int M, int N) {
 //     per CU and keeps twice the loads in flight, which such shapes, with
 //     little reuse of the long operand, need (131072x64x1024: 114 against
 //     105; 8192x384x4096: 144 against 140).
-//   * at most 2 columns (or 8 once A has 2^26 elements), A stored M x K
-//     with 16-byte rows, M and K at least 256: the row-dot kernel (per-row
+//   * at most 2 columns (or 8 once A has 2^26 elements, or when the tiled
+//     kernels cannot load the layout), A stored M x K, M and K at least 256:
+//     the row-dot kernel (per-row
 //     dot products streaming A; y = A x).  16384 x 1 x 16384: 209 us against
 //     1190 on the general kernel and 216 for hipBLASLt; 16384 x 8 x 16384:
 //     231 against 264 on the tiled kernel.  At 4096 x 8 x 4096 the tiled
 //     kernel is faster (26 against 41 us): staging B per workgroup costs as
 //     much as the little A each one streams;
-//   * at most 8 rows, B stored K x N with the vector layout, N and K at
-//     least 256: the skinny kernel, which streams B without computing the
+//   * at most 8 rows, B stored K x N, N and K at least 256: the skinny
+//     kernel, which streams B without computing the
 //     empty rows of a 64-row tile (1 x 16384 x 16384: 5.9 TB/s of B against
 //     4.4 for the tiled kernel and 5.8 for hipBLASLt; 8 x 8192 x 28672: 5.5
 //     against 4.3 and 4.9).  For 9-16 rows (two groups of 8 rows per
@@ -138,7 +139,7 @@ static bool covers_well(int cfg, int M, int N) {
 static int auto_config(const PlanRequest &r, int cus, bool aligned) {
     const int M = r.M, N = r.N, K = r.K;
     if (skinny_fits(r) && M <= 8 && N >= 256 && K >= 256) return SGEMM_CFG_SKINNY_16x256;
-    if (rowdot_fits(r) && M >= 256 && K >= 256 && (N <= 2 || (int64_t)M * K >= ((int64_t)1 << 26)) &&
+    if (rowdot_fits(r) && M >= 256 && K >= 256 && (N <= 2 || !aligned || (int64_t)M * K >= ((int64_t)1 << 26)) &&
         (r.sched != SGEMM_SCHED_DP || K <= kRowdotFloats / rowdot_cols(N)))
         return SGEMM_CFG_ROWDOT_N8;
     if (!aligned) return SGEMM_CFG_GENERIC_64x64x16;

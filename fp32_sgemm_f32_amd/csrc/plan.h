@@ -61,9 +61,6 @@ struct PlanRequest {
                          // extents of A, B, C multiples of 4
     int trans_a = 0;     // A stored K x M
     int trans_b = 0;     // B stored N x K
-    int b_vector = 0;    // B alone has the vector layout: 16-byte aligned, ldb and the
-                         // stored row length multiples of 4, and N too
-    int a_rows16 = 0;    // A stored M x K with rows on 16-byte boundaries (aligned, lda % 4 == 0)
 };
 
 struct Plan {

@@ -1,9 +1,10 @@
-// Products with at most 8 columns (N <= 8), A stored M x K with 16-byte rows:
-// HBM-bound on A (y = A x is the case N = 1).  Each output is the dot
-// product of a row of A with a column of B, so the lanes of a wave stream a
-// row of A along K (one 16-byte load per lane, 1 KiB per wave per load: the
-// coalesced access of "Vectorized Memory Access: Pushing CUDA SGEMM to 29
-// TFLOPS on H100", section 3) and each keeps partial dot products for the
+// Products with at most 8 columns (N <= 8), A stored M x K: HBM-bound on A
+// (y = A x is the case N = 1).  Each output is the dot product of a row of
+// A with a column of B, so the lanes of a wave stream a row of A along K
+// (one 16-byte load per lane, 1 KiB per wave per load: the coalesced access
+// of "Vectorized Memory Access: Pushing CUDA SGEMM to 29 TFLOPS on H100",
+// section 3; four 4-byte loads covering the same 1 KiB when A's rows are
+// off the 16-byte grid) and each keeps partial dot products for the
 // few columns; a butterfly over the 64 lanes, always the same one, finishes
 // them.
 //
@@ -42,16 +43,20 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// 16 bytes of A's row at column k when all four lie before k_end, else the
-// ones that do and zeros.
+// A's row at columns k..k+3: one 16-byte load when the rows lie on 16-byte
+// boundaries (VEC) and all four come before k_end, else one float at a
+// time (zeros at and after k_end).
+template <bool VEC>
 __device__ __forceinline__ f32x4 a_quad(const float *row, int k, int k_end) {
-    if (k + 4 <= k_end) return *(const f32x4 *)(row + k);
+    if (VEC && k + 4 <= k_end) return *(const f32x4 *)(row + k);
     f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int t = 0; k + t < k_end; ++t) v[t] = row[k + t];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        if (k + t < k_end) v[t] = row[k + t];
     return v;
 }
 
-template <int R, int NR>
+template <int R, int NR, bool VEC>
 __global__ __launch_bounds__(kThreads) void sgemm_rowdot_kernel(KernelArgs a) {
     constexpr int KB = kRowdotFloats / NR;   // k of B per column staged
     constexpr int U = R == 1 ? 8 : 4;        // A quads in flight per lane and row
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void sgemm_rowdot_kernel(KernelArgs a) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const int kl = q0 + 256 * u;
-                    av[u][r] = (ok[r] && kl < klen) ? a_quad(row[r], k_begin + kl, k_end)
+                    av[u][r] = (ok[r] && kl < klen) ? a_quad<VEC>(row[r], k_begin + kl, k_end)
                                                     : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 }
 #pragma unroll
@@ -162,7 +167,10 @@ template <int R, int NR>
 hipError_t launch_shape(const KernelArgs &a, hipStream_t s) {
     KernelArgs args = a;
     void *params[] = {&args};
-    hipError_t e = hipLaunchKernel((const void *)sgemm_rowdot_kernel<R, NR>, dim3(a.grid), dim3(kThreads), params, 0, s);
+    // 16-byte loads of A when its rows start on 16-byte boundaries.
+    const bool vec = ((uintptr_t)a.A & 15) == 0 && (a.lda & 3) == 0;
+    const void *f = vec ? (const void *)sgemm_rowdot_kernel<R, NR, true> : (const void *)sgemm_rowdot_kernel<R, NR, false>;
+    hipError_t e = hipLaunchKernel(f, dim3(a.grid), dim3(kThreads), params, 0, s);
     if (e != hipSuccess || a.ipt <= 1) return e;
     const int64_t threads = (int64_t)a.M * a.N;
     int64_t blocks = (threads + 255) / 256;
@@ -191,7 +199,7 @@ hipError_t launch_rowdot(int cfg, const KernelArgs &a, hipStream_t s) {
 
 hipError_t occupancy_rowdot(int cfg, int *wg_per_cu) {
     if (cfg != SGEMM_CFG_ROWDOT_N8) return hipErrorInvalidValue;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(wg_per_cu, (const void *)sgemm_rowdot_kernel<1, 8>,
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(wg_per_cu, (const void *)sgemm_rowdot_kernel<1, 8, true>,
                                                         kThreads, 0);
 }
 

@@ -186,14 +186,6 @@ bool vector_c(const Call &c) {
 
 bool vector_layout(const Call &c) { return vector_ab(c) && vector_c(c); }
 
-// B alone in the vector layout (what the skinny kernel needs).
-bool vector_b(const Call &c) {
-    return (c.b_cols() & 3) == 0 && (c.N & 3) == 0 && (c.ldb & 3) == 0 && ((uintptr_t)c.B & 15) == 0;
-}
-
-// A stored M x K with rows on 16-byte boundaries (what the row-dot kernel needs).
-bool rows16_a(const Call &c) { return !c.ta && (c.lda & 3) == 0 && ((uintptr_t)c.A & 15) == 0; }
-
 // Kernels that read A or B and write C one float at a time where needed, so
 // that no layout calls for repacking them.
 bool any_layout(int cfg) { return kCfgs[cfg].kind == kKindSkinny || kCfgs[cfg].kind == kKindRowdot; }
@@ -315,7 +307,7 @@ int run(const Call &c) {
     if ((st = device_info(dev, &info)) != SGEMM_OK) return st;
     PlanRequest req{c.M, c.N, c.K, c.config, c.sched, info.num_cus, info.occupancy,
                     env_int("SGEMM_F32_SK_WG_PER_CU", 0), vector_ab(c) && (c_own || vector_c(c)) ? 1 : 0,
-                    c.ta, c.tb, vector_b(c) ? 1 : 0, rows16_a(c) ? 1 : 0};
+                    c.ta, c.tb};
     Plan p;
     if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
     // An automatic choice other than the kernels that take any layout of
@@ -447,13 +439,11 @@ static int plan_for(int ta, int tb, int M, int N, int K, int config, int sched, 
     // the padded product.
     const int a_cols = ta ? M : K, b_cols = tb ? K : N;
     const bool aligned = a_cols % 4 == 0 && b_cols % 4 == 0 && N % 4 == 0;
-    const bool b_vector = b_cols % 4 == 0 && N % 4 == 0;
-    const bool a_rows16 = !ta && K % 4 == 0;
+
     sgemm::Call c = sgemm::plain(M, N, K, nullptr, a_cols, nullptr, b_cols, nullptr, N, nullptr, config, sched);
     c.ta = ta;
     c.tb = tb;
-    sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu, aligned ? 1 : 0, ta, tb,
-                           b_vector ? 1 : 0, a_rows16 ? 1 : 0};
+    sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu, aligned ? 1 : 0, ta, tb};
     sgemm::Plan p;
     int st = sgemm::make_plan(req, &p);
     if (st != SGEMM_OK) return st;

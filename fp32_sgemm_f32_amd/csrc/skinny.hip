@@ -1,5 +1,4 @@
-// Products with at most 16 rows (M <= 16), B stored K x N with 16-byte rows:
-// HBM-bound on B.  A tile of the matrix-core kernels computes 64 or more
+// Products with at most 16 rows (M <= 16), B stored K x N: HBM-bound on B.  A tile of the matrix-core kernels computes 64 or more
 // rows, so for such an M most of its work is empty rows, and streaming B
 // stops at what those MFMAs allow (~4.4 TB/s).  This kernel does only the
 // M rows' multiply-adds on the vector ALU and spends its registers on loads
@@ -12,7 +11,9 @@
 // Work: workgroup w of the grid owns column strip w / KS (256 columns) and
 // K split w % KS (ceil(K / KS) consecutive k).  Its 8 waves split that range
 // again, each lane holding 4 adjacent columns for MRW rows (4 or 8): per k
-// one 16-byte B load and 4 * MRW multiply-adds, 16 loads in flight per lane.
+// one 16-byte B load (when B is off the 16-byte grid: four 4-byte loads, the
+// lane's columns 64 apart so that each load of a wave is contiguous) and
+// 4 * MRW multiply-adds, 16 loads in flight per lane.
 // For 9-16 rows the workgroup's two halves each take 8 of the rows over the
 // same columns and K range, four waves splitting it.  Two waves per SIMD: the 16-row kernel's LDS (96 KiB)
 // admits one workgroup per CU anyway, so each wave may use 256 registers.  A's values, the same for every lane, are staged in LDS
@@ -39,7 +40,7 @@ __device__ __forceinline__ float a_at(const KernelArgs &a, int m, int k) {
     return a.trans_a ? a.A[(int64_t)k * a.lda + m] : a.A[(int64_t)m * a.lda + k];
 }
 
-// acc[m][j] += A(m, k) * B(k, n0 + j) for one k: A's MR values (a broadcast
+// acc[m][j] += A(m, k) * B(k, the lane's column j) for one k: A's MR values (a broadcast
 // LDS read) times the lane's 4 B values, m and then j ascending.
 template <int MR>
 __device__ __forceinline__ void fma_k(float (&acc)[MR][4], const float *ap, const f32x4 &b) {
@@ -57,7 +58,30 @@ __device__ __forceinline__ void fma_k(float (&acc)[MR][4], const float *ap, cons
 // with H = 2 the two halves of the workgroup take rows 0-7 and 8-15 of the
 // same columns and K range, each wave keeping the 32 accumulators of the
 // 8-row form (the second read of each B line comes from L2).
-template <int MRW, int H>
+// The lane's 4 columns of its strip: adjacent (n0 .. n0 + 3, one 16-byte
+// load) when B's rows and N are on the 16-byte grid (VEC); else 64 apart
+// (base + 64 j + lane), so that each of the 4 one-float loads of a wave
+// reads 64 consecutive floats.
+template <bool VEC>
+__device__ __forceinline__ int lane_col(int strip, int lane, int j) {
+    return VEC ? strip * kCols + 4 * lane + j : strip * kCols + 64 * j + lane;
+}
+
+// B's row k at the lane's 4 columns, zeros at and after N.
+template <bool VEC>
+__device__ __forceinline__ f32x4 b_quad(const KernelArgs &a, int k, int strip, int lane) {
+    const float *p = a.B + (int64_t)k * a.ldb;
+    if (VEC) return *(const f32x4 *)(p + lane_col<true>(strip, lane, 0));
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = lane_col<false>(strip, lane, j);
+        if (n < a.N) v[j] = p[n];
+    }
+    return v;
+}
+
+template <int MRW, int H, bool VEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sgemm_skinny_kernel(KernelArgs a) {
     constexpr int kUnroll = 16;   // B loads in flight per lane
@@ -74,9 +98,7 @@ void sgemm_skinny_kernel(KernelArgs a) {
     const int k_per = (a.K + ks_count - 1) / ks_count;
     const int k_begin = ks * k_per;
     const int k_end = k_begin + k_per < a.K ? k_begin + k_per : a.K;
-    const int n0 = strip * kCols + 4 * lane;
-    const bool col_ok = n0 < a.N;   // N is a multiple of 4: a lane's 4 columns are all in or all out
-    const float *bcol = a.B + n0;
+    const bool col_ok = lane_col<VEC>(strip, lane, 0) < a.N;   // the lane's first (lowest) column
 
     float acc[MRW][4];
 #pragma unroll
@@ -105,12 +127,12 @@ void sgemm_skinny_kernel(KernelArgs a) {
             f32x4 b[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
-                b[u] = col_ok ? *(const f32x4 *)(bcol + (int64_t)(k + u) * a.ldb) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                b[u] = col_ok ? b_quad<VEC>(a, k + u, strip, lane) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) fma_k(acc, ag + (k + u - blk) * MR, b[u]);
         }
         for (; k < w1; ++k) {
-            const f32x4 b = col_ok ? *(const f32x4 *)(bcol + (int64_t)k * a.ldb) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const f32x4 b = col_ok ? b_quad<VEC>(a, k, strip, lane) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             fma_k(acc, ag + (k - blk) * MR, b);
         }
     }
@@ -143,27 +165,37 @@ void sgemm_skinny_kernel(KernelArgs a) {
 #pragma unroll
         for (int m = 0; m < MRW; ++m) {
             if (row0 + m >= a.M) break;
-            float *c = a.C + (int64_t)(row0 + m) * a.ldc + n0;
+            float *c = a.C + (int64_t)(row0 + m) * a.ldc;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) c[j] = epilogue(a, acc[m][j], c + j);
+            for (int j = 0; j < 4; ++j) {
+                const int n = lane_col<VEC>(strip, lane, j);
+                if (VEC || n < a.N) c[n] = epilogue(a, acc[m][j], c + n);
+            }
         }
     } else {
         // Partial sums, dense: split ks, row m, column n at
         // partials[(ks * 16 + m) * Np + n], Np = strips * 256.
         const int64_t np = (int64_t)a.tiles_n * kCols;
-        float *p = a.partials + ((int64_t)ks * 16 + row0) * np + n0;
+        float *p = a.partials + ((int64_t)ks * 16 + row0) * np;
 #pragma unroll
         for (int m = 0; m < MRW; ++m) {
             if (row0 + m >= a.M) break;
-            *(f32x4 *)(p + m * np) = f32x4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+            if (VEC) {
+                *(f32x4 *)(p + m * np + lane_col<true>(strip, lane, 0)) =
+                    f32x4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p[m * np + lane_col<false>(strip, lane, j)] = acc[m][j];
+            }
         }
     }
 }
 
 // C(m, n..n+3) = the KS partial sums added in split order, then the
-// epilogue: one thread per 4 outputs, up to 8 splits' loads in flight.
+// epilogue: one thread per 4 outputs (the last quad of a row may end at N),
+// up to 8 splits' loads in flight.
 __global__ __launch_bounds__(256) void sgemm_skinny_sum_kernel(KernelArgs a) {
-    const int quads = a.N / 4;
+    const int quads = (a.N + 3) / 4;
     const int64_t total = (int64_t)a.M * quads;
     const int64_t np = (int64_t)a.tiles_n * kCols;
     const int ks_count = a.ipt;
@@ -183,7 +215,8 @@ __global__ __launch_bounds__(256) void sgemm_skinny_sum_kernel(KernelArgs a) {
         }
         float *c = a.C + (int64_t)m * a.ldc + n;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) c[j] = epilogue(a, sum[j], c + j);
+        for (int j = 0; j < 4; ++j)
+            if (n + j < a.N) c[j] = epilogue(a, sum[j], c + j);
     }
 }
 
@@ -191,10 +224,13 @@ template <int MRW, int H>
 hipError_t launch_rows(const KernelArgs &a, hipStream_t s) {
     KernelArgs args = a;
     void *params[] = {&args};
-    hipError_t e =
-        hipLaunchKernel((const void *)sgemm_skinny_kernel<MRW, H>, dim3(a.grid), dim3(kThreads), params, 0, s);
+    // 16-byte loads of B when its rows and N are on the 16-byte grid.
+    const bool vec = ((uintptr_t)a.B & 15) == 0 && (a.ldb & 3) == 0 && (a.N & 3) == 0;
+    const void *f = vec ? (const void *)sgemm_skinny_kernel<MRW, H, true>
+                        : (const void *)sgemm_skinny_kernel<MRW, H, false>;
+    hipError_t e = hipLaunchKernel(f, dim3(a.grid), dim3(kThreads), params, 0, s);
     if (e != hipSuccess || a.ipt <= 1) return e;
-    const int64_t threads = (int64_t)a.M * (a.N / 4);
+    const int64_t threads = (int64_t)a.M * ((a.N + 3) / 4);
     int64_t blocks = (threads + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     return hipLaunchKernel((const void *)sgemm_skinny_sum_kernel, dim3((unsigned)blocks), dim3(256), params, 0, s);
@@ -203,7 +239,7 @@ hipError_t launch_rows(const KernelArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_skinny(int cfg, const KernelArgs &a, hipStream_t s) {
-    if (cfg != SGEMM_CFG_SKINNY_16x256 || a.M < 1 || a.M > 16 || a.N % 4 || a.trans_b ||
+    if (cfg != SGEMM_CFG_SKINNY_16x256 || a.M < 1 || a.M > 16 || a.trans_b ||
         (a.ipt > 1 && !a.partials))
         return hipErrorInvalidValue;
     if (a.M <= 4) return launch_rows<4, 1>(a, s);
@@ -213,7 +249,7 @@ hipError_t launch_skinny(int cfg, const KernelArgs &a, hipStream_t s) {
 
 hipError_t occupancy_skinny(int cfg, int *wg_per_cu) {
     if (cfg != SGEMM_CFG_SKINNY_16x256) return hipErrorInvalidValue;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(wg_per_cu, (const void *)sgemm_skinny_kernel<8, 2>, kThreads,
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(wg_per_cu, (const void *)sgemm_skinny_kernel<8, 2, true>, kThreads,
                                                         0);
 }
 

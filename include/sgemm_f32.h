@@ -28,11 +28,11 @@
  *   of the library (each only when its own layout does not qualify) and the
  *   product runs on the vector kernels, which then write C in place (one
  *   float at a time when C's layout does not qualify; results as unpadded,
- *   C's padding untouched).  Thin products have kernels of their own, for
- *   which only the streamed operand needs 16-byte rows: at most 8 rows
- *   with B stored K x N (SGEMM_CFG_SKINNY_16x256), at most 2 columns, or 8
- *   for large A, with A stored M x K (SGEMM_CFG_ROWDOT_N8); the other
- *   operand and C may have any layout.
+ *   C's padding untouched).  Thin products have kernels of their own that
+ *   take any layout: at most 8 rows with B stored K x N
+ *   (SGEMM_CFG_SKINNY_16x256), at most 2 columns, or 8 for large A or a
+ *   layout the tiled kernels cannot load, with A stored M x K
+ *   (SGEMM_CFG_ROWDOT_N8).
  *
  * Memory and ownership
  *   A, B, C are device pointers, caller-owned, allocated on the HIP device
@@ -147,16 +147,16 @@ extern "C" {
 /* Element-wise bounds-checked loads: any shape, leading dimension and
  * (4-byte) alignment. */
 #define SGEMM_CFG_GENERIC_64x64x16  22 /* 256 threads, 4 waves of 32x32 */
-/* At most 16 rows (M <= 16), B stored K x N with 16-byte aligned rows, ldb
- * and N multiples of 4 (A and C in any layout): vector-ALU multiply-adds
+/* At most 16 rows (M <= 16), B stored K x N (any layout; 16-byte loads
+ * where B's rows and N are on the 16-byte grid): vector-ALU multiply-adds
  * over the M rows only, B streamed once, K split over the grid.  The
  * automatic choice takes it for such products with M <= 8, N, K >= 256. */
 #define SGEMM_CFG_SKINNY_16x256     23 /* 512 threads, 8 waves over 256 columns */
-/* At most 8 columns (N <= 8, y = A x among them), A stored M x K with rows
- * on 16-byte boundaries (aligned, lda a multiple of 4; B and C in any
- * layout): per-row dot products, A streamed once, B held in LDS.  The
- * automatic choice takes it for such products with M, K >= 256 and N <= 2,
- * or N <= 8 once M * K >= 2^26. */
+/* At most 8 columns (N <= 8, y = A x among them), A stored M x K (any
+ * layout; 16-byte loads where A's rows are on the 16-byte grid): per-row
+ * dot products, A streamed once, B held in LDS.  The automatic choice takes
+ * it for such products with M, K >= 256 and N <= 2, or N <= 8 once
+ * M * K >= 2^26 or when the layout rules out the tiled kernels. */
 #define SGEMM_CFG_ROWDOT_N8         24 /* 512 threads, 8 waves over rows of A */
 #define SGEMM_NUM_CFGS              25 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
 /* The configurations not named above as running other shapes or storage

@@ -130,12 +130,12 @@ def test_every_step_covered_once(shape, config, sched, cus):
         # refused: a tile that does not divide it on a kernel without edge
         # masking, or the vector kernels when N or K is not a multiple of 4.
         assert e.status == sg.ERR_CONFIG and config != sg.CFG_AUTO
-        if config == sg.CFG_SKINNY_16x256:   # at most 16 rows, B rows of N floats, N a multiple of 4
-            assert M > 16 or N % 4
+        if config == sg.CFG_SKINNY_16x256:   # at most 16 rows
+            assert M > 16
             return
-        if config == sg.CFG_ROWDOT_N8:       # at most 8 columns, A rows of K floats, K a multiple of 4;
-            cols = 1 if N <= 1 else 2 if N == 2 else 4 if N <= 4 else 8      # whole K in LDS for DP
-            assert N > 8 or K % 4 or (sched == sg.SCHED_DP and K > 16384 // cols)
+        if config == sg.CFG_ROWDOT_N8:       # at most 8 columns; B's whole K range in LDS for DP
+            cols = 1 if N <= 1 else 2 if N == 2 else 4 if N <= 4 else 8
+            assert N > 8 or (sched == sg.SCHED_DP and K > 16384 // cols)
             return
         bm, bn, bk = sg.CFG_TILES[config]
         divides = M % bm == 0 and N % bn == 0 and K % bk == 0
