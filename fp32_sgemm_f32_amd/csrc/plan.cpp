@@ -179,9 +179,12 @@ bool dl_offsets_fit(int cfg, bool edge, int64_t lda, int64_t ldb, bool trans_a, 
 // The skinny kernel's plan, in the terms of the tiled ones: a "tile" is a
 // strip of 256 columns (one tile row, 16 rows high), its "K chunks" are the
 // KS splits of K, and every workgroup owns exactly one (strip, split) step,
-// so KS > 1 is a Stream-K plan whose every tile is split.  KS gives the
-// grid about one workgroup per CU (8 waves: two per SIMD), with at least
-// 256 k per split; the data-parallel schedule forces KS = 1.
+// so KS > 1 is a Stream-K plan whose every tile is split.  KS keeps the
+// grid within one workgroup per CU (8 waves: two per SIMD), with at least
+// 256 k per split; the data-parallel schedule forces KS = 1.  Rounding KS
+// down leaves some CUs idle but runs one round: 65 strips x 3 splits took
+// 204 us at 1 x 16385 x 16384 where 65 x 4 (four workgroups in a second
+// round) took 259.
 static int plan_skinny(const PlanRequest &req, int cus, Plan *out) {
     if (!skinny_fits(req)) return SGEMM_ERR_CONFIG;
     const CfgInfo &c = kCfgs[SGEMM_CFG_SKINNY_16x256];
@@ -194,7 +197,7 @@ static int plan_skinny(const PlanRequest &req, int cus, Plan *out) {
     const int strips = p.tiles_n;
     int ks = 1;
     if (req.sched != SGEMM_SCHED_DP && strips > 0 && req.K > 0) {
-        ks = (cus + strips - 1) / strips;
+        ks = cus / strips > 1 ? cus / strips : 1;
         const int by_k = req.K / 256 > 1 ? req.K / 256 : 1;
         if (ks > by_k) ks = by_k;
         if (req.sched == SGEMM_SCHED_STREAMK && ks < 2 && req.K >= 2) ks = 2;
@@ -221,8 +224,9 @@ static int plan_skinny(const PlanRequest &req, int cus, Plan *out) {
 // The row-dot kernel's plan, in the same terms: a "tile" is a block of
 // rows (all 8 columns), its "K chunks" are the KS splits of K, every
 // workgroup owns one (block, split) step.  KS is at least what fits B's
-// split in LDS; blocks and splits give about two workgroups per CU; a
-// data-parallel schedule needs B's whole K range to fit.
+// split in LDS; beyond that, blocks and splits stay within the resident
+// workgroups of one round (two per CU); a data-parallel schedule needs B's
+// whole K range to fit.
 static int plan_rowdot(const PlanRequest &req, int cus, int occ, Plan *out) {
     if (!rowdot_fits(req)) return SGEMM_ERR_CONFIG;
     const CfgInfo &c = kCfgs[SGEMM_CFG_ROWDOT_N8];
@@ -235,8 +239,9 @@ static int plan_rowdot(const PlanRequest &req, int cus, int occ, Plan *out) {
     int64_t rb = target / ks > 1 ? target / ks : 1;
     if (rb > rb_max) rb = rb_max;
     if (req.sched != SGEMM_SCHED_DP && rb > 0 && rb * ks < target) {
-        // Few rows: split K further (at least 256 k per split).
-        int64_t more = (target + rb - 1) / rb;
+        // Few rows: split K further (at least 256 k per split), within one
+        // resident round.
+        int64_t more = target / rb;
         const int64_t by_k = K / 256 > 1 ? K / 256 : 1;
         if (more > by_k) more = by_k;
         if (more > ks) ks = (int)more;

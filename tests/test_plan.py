@@ -150,6 +150,35 @@ def test_every_step_covered_once(shape, config, sched, cus):
         assert p["dp_tiles"] == 0
 
 
+@pytest.mark.parametrize("shape", [(1, 16385, 16384), (8, 12288, 8192), (4, 20000, 8192), (2, 11008, 4096),
+                                   (1, 16384, 16384), (16, 700, 4096), (3000, 1, 4096), (1000, 3, 1000),
+                                   (1500, 8, 4096), (16384, 1, 16384), (40, 5, 300000)])
+@pytest.mark.parametrize("cus", [256, 132])
+def test_thin_grids_fit_one_resident_round(shape, cus):
+    """A split count chosen freely never adds a second, nearly empty round of
+    workgroups: the skinny kernel holds one workgroup per CU, the row-dot
+    kernel two.  Only the row-dot kernel's LDS limit on B's split may force
+    more splits than that."""
+    M, N, K = shape
+    for config, per_cu in ((sg.CFG_SKINNY_16x256, 1), (sg.CFG_ROWDOT_N8, 2)):
+        try:
+            p = sg.plan(M, N, K, config, sg.SCHED_AUTO, num_cus=cus, occupancy=OCC)
+        except sg.SgemmError:
+            continue
+        check_plan(p, M, N, K)
+        slots = cus * per_cu
+        strips = p["tiles_m"] * p["tiles_n"]
+        if config == sg.CFG_ROWDOT_N8:
+            cols = 1 if N <= 1 else 2 if N == 2 else 4 if N <= 4 else 8
+            forced = -(-K // (16384 // cols))
+            assert p["grid"] <= max(slots, strips * forced)
+        else:
+            assert p["grid"] <= max(slots, strips)
+        # Still splits K where a single pass would leave most CUs idle.
+        if strips * 2 <= slots and K >= 4 * 256:
+            assert p["iters_per_tile"] >= 2
+
+
 def test_stream_k_example_from_the_page():
     """n = 1024, 128x128 tiles, 264 resident blocks: all 64 tiles split, each
     shared by roughly four blocks."""
