@@ -928,6 +928,8 @@ SKINNY_CASES = {
     "m5_ta_beta": (5, 2048, 1500, 1, (0, 0), (0, 0), -1.5, 0.5, sg.SCHED_AUTO),
     "m16_odd_lda_ldc": (16, 1024, 1024, 0, (3, 1), (5, 2), 2.0, -1.0, sg.SCHED_STREAMK),
     "m1_ta_offset": (1, 512, 8192, 1, (0, 1), (1, 1), 1.0, 0.0, sg.SCHED_AUTO),
+    # 43 strips of 256 columns: 5 K splits, 215 workgroups, one round.
+    "m2_uneven_strips": (2, 11008, 4096, 0, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_AUTO),
 }
 
 
@@ -991,6 +993,8 @@ ROWDOT_CASES = {
     "n8_dp": (4099, 8, 2044, 0, 0, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_DP),
     "n8_streamk_odd_ld": (2500, 8, 3000, 1, 4, (3, 1), (5, 2), 2.0, -1.0, sg.SCHED_STREAMK),
     "n1_b_offset": (777, 1, 9999, 0, 1, (0, 1), (1, 1), 1.0, 0.0, sg.SCHED_AUTO),
+    # 375 row blocks and no K split: one round of resident workgroups.
+    "n1_one_round": (3000, 1, 4096, 0, 0, (0, 0), (0, 0), 1.0, 0.0, sg.SCHED_AUTO),
 }
 
 
