@@ -12,7 +12,8 @@
 // split's rows of B (K x N, tiny) in LDS once, k-contiguous per column so
 // that the lanes read consecutive 16-byte quads, and then walks its rows of
 // A: wave v of 8 takes rows v, v + 8, ... of the block, R at a time (R
-// loads of A per k quad share one read of B).  Eight waves per workgroup
+// loads of A per k quad share one read of B; R = 1 with 16-byte loads, 4
+// with 4-byte ones where the block is tall enough).  Eight waves per workgroup
 // (two workgroups per CU by their 64 KiB of LDS) measured 4-28% faster than
 // four (16384 x 1 x 16384: 5.3 against 5.1 TB/s; 8192 x 2 x 8192: 4.9
 // against 3.8).  With KS > 1 each workgroup writes its
@@ -163,14 +164,12 @@ __global__ __launch_bounds__(256) void sgemm_rowdot_sum_kernel(KernelArgs a) {
     }
 }
 
-template <int R, int NR>
+template <int R, int NR, bool VEC>
 hipError_t launch_shape(const KernelArgs &a, hipStream_t s) {
     KernelArgs args = a;
     void *params[] = {&args};
-    // 16-byte loads of A when its rows start on 16-byte boundaries.
-    const bool vec = ((uintptr_t)a.A & 15) == 0 && (a.lda & 3) == 0;
-    const void *f = vec ? (const void *)sgemm_rowdot_kernel<R, NR, true> : (const void *)sgemm_rowdot_kernel<R, NR, false>;
-    hipError_t e = hipLaunchKernel(f, dim3(a.grid), dim3(kThreads), params, 0, s);
+    hipError_t e = hipLaunchKernel((const void *)sgemm_rowdot_kernel<R, NR, VEC>, dim3(a.grid), dim3(kThreads),
+                                   params, 0, s);
     if (e != hipSuccess || a.ipt <= 1) return e;
     const int64_t threads = (int64_t)a.M * a.N;
     int64_t blocks = (threads + 255) / 256;
@@ -178,12 +177,12 @@ hipError_t launch_shape(const KernelArgs &a, hipStream_t s) {
     return hipLaunchKernel((const void *)sgemm_rowdot_sum_kernel, dim3((unsigned)blocks), dim3(256), params, 0, s);
 }
 
-template <int R>
+template <int R, bool VEC>
 hipError_t launch_rows(const KernelArgs &a, hipStream_t s) {
-    if (a.N == 1) return launch_shape<R, 1>(a, s);
-    if (a.N == 2) return launch_shape<R, 2>(a, s);
-    if (a.N <= 4) return launch_shape<R, 4>(a, s);
-    return launch_shape<R, 8>(a, s);
+    if (a.N == 1) return launch_shape<R, 1, VEC>(a, s);
+    if (a.N == 2) return launch_shape<R, 2, VEC>(a, s);
+    if (a.N <= 4) return launch_shape<R, 4, VEC>(a, s);
+    return launch_shape<R, 8, VEC>(a, s);
 }
 
 }  // namespace
@@ -192,9 +191,15 @@ hipError_t launch_rowdot(int cfg, const KernelArgs &a, hipStream_t s) {
     if (cfg != SGEMM_CFG_ROWDOT_N8 || a.N < 1 || a.N > 8 || a.trans_a || a.tiles_m < 1 || a.ipt < 1 ||
         (a.ipt > 1 && !a.partials) || rowdot_k_per(a.K, a.ipt) > kRowdotFloats / rowdot_cols(a.N))
         return hipErrorInvalidValue;
-    // Four rows per wave at a time once a block has at least four per wave.
+    // 16-byte loads when A's rows start on 16-byte boundaries, one row per
+    // wave at a time (measured 1-6% faster than four: 16384 x 8 x 16384 in
+    // 220 against 225 us, 65536 x 4 x 1024 in 46 against 49).  With 4-byte
+    // loads, four rows per wave once a block has at least four per wave
+    // (16384 x 1 x 16383: 259 against 268 us with one).
+    const bool vec = ((uintptr_t)a.A & 15) == 0 && (a.lda & 3) == 0;
+    if (vec) return launch_rows<1, true>(a, s);
     const int rows_per = (a.M + a.tiles_m - 1) / a.tiles_m;
-    return rows_per >= 4 * kWaves ? launch_rows<4>(a, s) : launch_rows<1>(a, s);
+    return rows_per >= 4 * kWaves ? launch_rows<4, false>(a, s) : launch_rows<1, false>(a, s);
 }
 
 hipError_t occupancy_rowdot(int cfg, int *wg_per_cu) {
