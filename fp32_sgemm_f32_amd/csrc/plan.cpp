@@ -128,17 +128,21 @@ static bool covers_well(int cfg, int M, int N) {
 //     231 against 264 on the tiled kernel.  At 4096 x 8 x 4096 the tiled
 //     kernel is faster (26 against 41 us): staging B per workgroup costs as
 //     much as the little A each one streams;
-//   * at most 8 rows, B stored K x N, N and K at least 256: the skinny
-//     kernel, which streams B without computing the
-//     empty rows of a 64-row tile (1 x 16384 x 16384: 5.9 TB/s of B against
-//     4.4 for the tiled kernel and 5.8 for hipBLASLt; 8 x 8192 x 28672: 5.5
-//     against 4.3 and 4.9).  For 9-16 rows (two groups of 8 rows per
-//     workgroup) it only ties the tiled kernel (16 x 16384 x 16384: 4.2
-//     against 4.3 TB/s; 12 rows 4.4 against 4.3) and runs when asked for.
+//   * at most 12 rows (16 when an operand is off the 16-byte grid), B
+//     stored K x N, N and K at least 256: the skinny kernel, which streams
+//     B without computing the empty rows of a 64-row tile (1 x 16384 x
+//     16384: 6.35 TB/s of B against 4.4 for the tiled kernel and 5.6 for
+//     hipBLASLt; 8 x 8192 x 28672: 5.6 against 4.3 and 4.9).  For 9-16 rows
+//     (two groups of 8 rows per workgroup) it beats the tiled kernel up to
+//     12 rows and ties it above (16 x 16384 x 16384: 4.25 against 4.3
+//     TB/s).
 // Layouts the vector kernels cannot load go to the general kernel.
 static int auto_config(const PlanRequest &r, int cus, bool aligned) {
     const int M = r.M, N = r.N, K = r.K;
-    if (skinny_fits(r) && M <= 8 && N >= 256 && K >= 256) return SGEMM_CFG_SKINNY_16x256;
+    // 9-12 rows: 236 against 246 us at 9 x 16384 x 16384, 64 against 70 at
+    // 10 x 8192 x 8192.  Off the 16-byte grid the tiled alternative is the
+    // general kernel (16 x 50257 x 1024: 67 against 180 us).
+    if (skinny_fits(r) && N >= 256 && K >= 256 && (M <= 12 || !aligned)) return SGEMM_CFG_SKINNY_16x256;
     if (rowdot_fits(r) && M >= 256 && K >= 256 && (N <= 2 || !aligned || (int64_t)M * K >= ((int64_t)1 << 26)) &&
         (r.sched != SGEMM_SCHED_DP || K <= kRowdotFloats / rowdot_cols(N)))
         return SGEMM_CFG_ROWDOT_N8;
@@ -202,7 +206,7 @@ static int plan_skinny(const PlanRequest &req, int cus, Plan *out) {
         if (ks > by_k) ks = by_k;
         if (req.sched == SGEMM_SCHED_STREAMK && ks < 2 && req.K >= 2) ks = 2;
     }
-    p.bk = req.K > 0 ? (req.K + ks - 1) / ks : 1;   // k per split
+    p.bk = req.K > 0 ? (req.K + ks - 1) / ks : 1;   // k per split (dealt to it in blocks of up to 512)
     p.ipt = req.K > 0 ? (req.K + p.bk - 1) / p.bk : 0;
     const int tiles = p.tiles_m * p.tiles_n;
     if (tiles == 0 || p.ipt == 0 || (p.ipt == 1 && req.sched != SGEMM_SCHED_STREAMK)) {

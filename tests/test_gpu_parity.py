@@ -937,7 +937,7 @@ SKINNY_CASES = {
 def test_skinny_rows(dev, case):
     import torch
     M, N, K, ta, (apad, aoff), (cpad, coff), alpha, beta, sched = SKINNY_CASES[case]
-    config = sg.CFG_AUTO if M <= 8 else sg.CFG_SKINNY_16x256   # the automatic choice up to 8 rows
+    config = sg.CFG_AUTO if M <= 12 else sg.CFG_SKINNY_16x256   # the automatic choice up to 12 rows
     p = sg.plan(M, N, K, config, sched, num_cus=torch.cuda.get_device_properties(dev).multi_processor_count,
                 trans_a=ta)
     assert p["config"] == sg.CFG_SKINNY_16x256
@@ -1090,6 +1090,7 @@ def test_graph_capture_of_thin_products(dev, shape):
 THIN_MISALIGNED = {
     "skinny_odd_n_offset": (4, 4097, 2000, 0, 1, 0.0, sg.CFG_SKINNY_16x256),
     "skinny_odd_ldb": (7, 1030, 3001, 3, 0, 1.0, sg.CFG_SKINNY_16x256),
+    "skinny_16_rows_odd_n": (16, 4097, 1500, 0, 0, 0.0, sg.CFG_SKINNY_16x256),
     "rowdot_odd_k": (5000, 1, 4097, 0, 0, 0.0, sg.CFG_ROWDOT_N8),
     "rowdot_offset_n3": (3000, 3, 2500, 1, 2, -1.0, sg.CFG_ROWDOT_N8),
 }

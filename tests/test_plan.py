@@ -272,6 +272,14 @@ def test_auto_choices_on_256_cus():
     p = sg.plan(192, 49152, 4096, num_cus=256, occupancy=occ)
     assert (p["tiles_m"], p["group_m"]) == (3, 3)
     check_plan(p, 192, 49152, 4096)
+    # Few rows: the skinny kernel up to 12, and up to 16 when an operand is
+    # off the 16-byte grid (where the tiled alternative is the general
+    # kernel); the tiled kernel for 13-16 aligned rows.
+    for shape in [(1, 16384, 16384), (8, 4096, 4096), (12, 16384, 16384), (9, 256, 256), (16, 50257, 1024),
+                  (13, 4096, 4094)]:
+        assert sg.plan(*shape, num_cus=256, occupancy=occ)["config"] == sg.CFG_SKINNY_16x256, shape
+    for shape in [(16, 16384, 16384), (13, 2048, 2048), (12, 255, 4096), (12, 4096, 252)]:
+        assert sg.plan(*shape, num_cus=256, occupancy=occ)["config"] != sg.CFG_SKINNY_16x256, shape
     # Ragged shapes: the edge-masking kernels of the same regimes, or the
     # general kernel when N or K is not a multiple of 4.
     p = sg.plan(4000, 4000, 4000, num_cus=256, occupancy=occ)
