@@ -128,21 +128,21 @@ static bool covers_well(int cfg, int M, int N) {
 //     231 against 264 on the tiled kernel.  At 4096 x 8 x 4096 the tiled
 //     kernel is faster (26 against 41 us): staging B per workgroup costs as
 //     much as the little A each one streams;
-//   * at most 12 rows (16 when an operand is off the 16-byte grid), B
-//     stored K x N, N and K at least 256: the skinny kernel, which streams
-//     B without computing the empty rows of a 64-row tile (1 x 16384 x
-//     16384: 6.35 TB/s of B against 4.4 for the tiled kernel and 5.6 for
-//     hipBLASLt; 8 x 8192 x 28672: 5.6 against 4.3 and 4.9).  For 9-16 rows
-//     (two groups of 8 rows per workgroup) it beats the tiled kernel up to
-//     12 rows and ties it above (16 x 16384 x 16384: 4.25 against 4.3
-//     TB/s).
+//   * at most 16 rows, B stored K x N, N and K at least 256 (9-16 rows:
+//     also B above 2^22 elements or a layout the tiled kernels cannot
+//     load): the skinny kernel, which streams B without computing the empty rows of a 64-row
+//     tile (1 x 16384 x 16384: 6.35 TB/s of B against 4.4 for the tiled
+//     kernel and 5.6 for hipBLASLt; 8 x 8192 x 28672: 5.6 against 4.3 and
+//     4.9; 16 x 16384 x 16384, on 16 x 16 x 4 matrix-core steps: 4.97
+//     against 4.3 and 5.75).
 // Layouts the vector kernels cannot load go to the general kernel.
 static int auto_config(const PlanRequest &r, int cus, bool aligned) {
     const int M = r.M, N = r.N, K = r.K;
-    // 9-12 rows: 236 against 246 us at 9 x 16384 x 16384, 64 against 70 at
-    // 10 x 8192 x 8192.  Off the 16-byte grid the tiled alternative is the
-    // general kernel (16 x 50257 x 1024: 67 against 180 us).
-    if (skinny_fits(r) && N >= 256 && K >= 256 && (M <= 12 || !aligned)) return SGEMM_CFG_SKINNY_16x256;
+    // 9-16 rows with B of at most 2^22 elements: the tiled kernel, 1-2 us
+    // faster there (16 x 2048 x 2048: 17.2 against 18.8 us), where it can
+    // load the layout.
+    if (skinny_fits(r) && N >= 256 && K >= 256 && (M <= 8 || !aligned || (int64_t)N * K > ((int64_t)1 << 22)))
+        return SGEMM_CFG_SKINNY_16x256;
     if (rowdot_fits(r) && M >= 256 && K >= 256 && (N <= 2 || !aligned || (int64_t)M * K >= ((int64_t)1 << 26)) &&
         (r.sched != SGEMM_SCHED_DP || K <= kRowdotFloats / rowdot_cols(N)))
         return SGEMM_CFG_ROWDOT_N8;

@@ -29,9 +29,8 @@
  *   product runs on the vector kernels, which then write C in place (one
  *   float at a time when C's layout does not qualify; results as unpadded,
  *   C's padding untouched).  Thin products have kernels of their own that
- *   take any layout: at most 12 rows (16 when an operand is off the
- *   16-byte grid) with B stored K x N (SGEMM_CFG_SKINNY_16x256), at most
- *   2 columns, or 8 for large A or a
+ *   take any layout: at most 16 rows with B stored K x N
+ *   (SGEMM_CFG_SKINNY_16x256), at most 2 columns, or 8 for large A or a
  *   layout the tiled kernels cannot load, with A stored M x K
  *   (SGEMM_CFG_ROWDOT_N8).
  *
@@ -149,10 +148,11 @@ extern "C" {
  * (4-byte) alignment. */
 #define SGEMM_CFG_GENERIC_64x64x16  22 /* 256 threads, 4 waves of 32x32 */
 /* At most 16 rows (M <= 16), B stored K x N (any layout; 16-byte loads
- * where B's rows and N are on the 16-byte grid): vector-ALU multiply-adds
- * over the M rows only, B streamed once, K split over the grid.  The
- * automatic choice takes it for such products with N, K >= 256 and M <= 12,
- * or M <= 16 when an operand is off the 16-byte grid. */
+ * where B's rows and N are on the 16-byte grid): multiply-adds over the M
+ * rows only (vector ALU up to 8 rows, 16 x 16 x 4 matrix-core steps for
+ * 9-16), B streamed once, K split over the grid.  The automatic choice
+ * takes it for such products with N, K >= 256 (for M > 8: and N * K > 2^22,
+ * or a layout the tiled kernels cannot load). */
 #define SGEMM_CFG_SKINNY_16x256     23 /* 512 threads, 8 waves over 256 columns */
 /* At most 8 columns (N <= 8, y = A x among them), A stored M x K (any
  * layout; 16-byte loads where A's rows are on the 16-byte grid): per-row

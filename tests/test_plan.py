@@ -272,13 +272,13 @@ def test_auto_choices_on_256_cus():
     p = sg.plan(192, 49152, 4096, num_cus=256, occupancy=occ)
     assert (p["tiles_m"], p["group_m"]) == (3, 3)
     check_plan(p, 192, 49152, 4096)
-    # Few rows: the skinny kernel up to 12, and up to 16 when an operand is
-    # off the 16-byte grid (where the tiled alternative is the general
-    # kernel); the tiled kernel for 13-16 aligned rows.
-    for shape in [(1, 16384, 16384), (8, 4096, 4096), (12, 16384, 16384), (9, 256, 256), (16, 50257, 1024),
-                  (13, 4096, 4094)]:
+    # Few rows: the skinny kernel up to 16 (N and K at least 256); for 9-16
+    # rows only once B has more than 2^22 elements, unless the layout rules
+    # out the tiled kernels.
+    for shape in [(1, 16384, 16384), (8, 4096, 4096), (8, 256, 256), (12, 16384, 16384), (16, 50257, 1024),
+                  (13, 4096, 4094), (16, 16384, 16384), (16, 2049, 2048), (9, 4096, 2048)]:
         assert sg.plan(*shape, num_cus=256, occupancy=occ)["config"] == sg.CFG_SKINNY_16x256, shape
-    for shape in [(16, 16384, 16384), (13, 2048, 2048), (12, 255, 4096), (12, 4096, 252)]:
+    for shape in [(17, 16384, 16384), (12, 255, 4096), (12, 4096, 252), (13, 2048, 2048), (9, 256, 256)]:
         assert sg.plan(*shape, num_cus=256, occupancy=occ)["config"] != sg.CFG_SKINNY_16x256, shape
     # Ragged shapes: the edge-masking kernels of the same regimes, or the
     # general kernel when N or K is not a multiple of 4.
