@@ -113,7 +113,8 @@ class _Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "config", "sched", "tile_m", "tile_n", "tile_k", "threads", "tiles_m", "tiles_n",
         "iters_per_tile", "dp_tiles", "sk_tiles", "grid", "sk_grid", "xcd_remap", "group_m")] + [
-        ("sk_iters", ctypes.c_longlong), ("workspace_bytes", ctypes.c_longlong), ("repacked", ctypes.c_int)]
+        ("sk_iters", ctypes.c_longlong), ("workspace_bytes", ctypes.c_longlong), ("repacked", ctypes.c_int),
+        ("transposed", ctypes.c_int)]
 
 
 _lib = None

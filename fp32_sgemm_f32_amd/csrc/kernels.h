@@ -21,7 +21,9 @@ hipError_t launch_valu(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t launch_skinny(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t occupancy_skinny(int cfg, int *wg_per_cu);
 // The row-dot kernel (N <= 8) and, for a K-split plan, the sum of its splits.
-hipError_t launch_rowdot(int cfg, const KernelArgs &a, hipStream_t s);
+// trans_c: C stored N x M, element (m, n) at C[n * ldc + m] (the transposed
+// product of a call with few rows and B stored N x K).
+hipError_t launch_rowdot(int cfg, const KernelArgs &a, hipStream_t s, int trans_c = 0);
 hipError_t occupancy_rowdot(int cfg, int *wg_per_cu);
 hipError_t occupancy_valu(int cfg, int *wg_per_cu);
 // Sum of the split tiles of a Stream-K launch (tile bm x bn) into C; after

@@ -36,6 +36,12 @@ __device__ __forceinline__ float b_at(const KernelArgs &a, int k, int n) {
     return a.trans_b ? a.B[(int64_t)n * a.ldb + k] : a.B[(int64_t)k * a.ldb + n];
 }
 
+// C(m, n) of the product: C stored M x N, or N x M when trans_c (the
+// transposed product of a call with few rows and B stored N x K).
+__device__ __forceinline__ float *c_at(const KernelArgs &a, int trans_c, int m, int n) {
+    return trans_c ? a.C + (int64_t)n * a.ldc + m : a.C + (int64_t)m * a.ldc + n;
+}
+
 // Sum over the 64 lanes of a wave by a butterfly of fixed order (every lane
 // ends with the same total).
 __device__ __forceinline__ float wave_sum(float v) {
@@ -58,7 +64,7 @@ __device__ __forceinline__ f32x4 a_quad(const float *row, int k, int k_end) {
 }
 
 template <int R, int NR, bool VEC>
-__global__ __launch_bounds__(kThreads) void sgemm_rowdot_kernel(KernelArgs a) {
+__global__ __launch_bounds__(kThreads) void sgemm_rowdot_kernel(KernelArgs a, int trans_c) {
     constexpr int KB = kRowdotFloats / NR;   // k of B per column staged
     constexpr int U = R == 1 ? 8 : 4;        // A quads in flight per lane and row
     __shared__ __attribute__((aligned(16))) float bs[kRowdotFloats];   // bs[n * KB + k]
@@ -133,10 +139,12 @@ __global__ __launch_bounds__(kThreads) void sgemm_rowdot_kernel(KernelArgs a) {
             for (int r = 0; r < R; ++r) {
                 if (!ok[r]) continue;
                 if (ks_count == 1) {
-                    float *c = a.C + (int64_t)(m0 + r) * a.ldc;
 #pragma unroll
                     for (int n = 0; n < NR; ++n)
-                        if (n < a.N) c[n] = epilogue(a, acc[r][n], c + n);
+                        if (n < a.N) {
+                            float *c = c_at(a, trans_c, m0 + r, n);
+                            *c = epilogue(a, acc[r][n], c);
+                        }
                 } else {
                     // Partial dot products: split ks, row m, column n at
                     // partials[(ks * M + m) * 8 + n].
@@ -151,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void sgemm_rowdot_kernel(KernelArgs a) {
 
 // C(m, n) = the KS partial dot products added in split order, then the
 // epilogue: one thread per output.
-__global__ __launch_bounds__(256) void sgemm_rowdot_sum_kernel(KernelArgs a) {
+__global__ __launch_bounds__(256) void sgemm_rowdot_sum_kernel(KernelArgs a, int trans_c) {
     const int64_t total = (int64_t)a.M * a.N;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
          t += (int64_t)gridDim.x * blockDim.x) {
@@ -159,15 +167,15 @@ __global__ __launch_bounds__(256) void sgemm_rowdot_sum_kernel(KernelArgs a) {
         const float *p = a.partials + (int64_t)m * 8 + n;
         float sum = 0.0f;
         for (int s = 0; s < a.ipt; ++s) sum += p[(int64_t)s * a.M * 8];
-        float *c = a.C + (int64_t)m * a.ldc + n;
+        float *c = c_at(a, trans_c, m, n);
         *c = epilogue(a, sum, c);
     }
 }
 
 template <int R, int NR, bool VEC>
-hipError_t launch_shape(const KernelArgs &a, hipStream_t s) {
+hipError_t launch_shape(const KernelArgs &a, int trans_c, hipStream_t s) {
     KernelArgs args = a;
-    void *params[] = {&args};
+    void *params[] = {&args, &trans_c};
     hipError_t e = hipLaunchKernel((const void *)sgemm_rowdot_kernel<R, NR, VEC>, dim3(a.grid), dim3(kThreads),
                                    params, 0, s);
     if (e != hipSuccess || a.ipt <= 1) return e;
@@ -178,16 +186,16 @@ hipError_t launch_shape(const KernelArgs &a, hipStream_t s) {
 }
 
 template <int R, bool VEC>
-hipError_t launch_rows(const KernelArgs &a, hipStream_t s) {
-    if (a.N == 1) return launch_shape<R, 1, VEC>(a, s);
-    if (a.N == 2) return launch_shape<R, 2, VEC>(a, s);
-    if (a.N <= 4) return launch_shape<R, 4, VEC>(a, s);
-    return launch_shape<R, 8, VEC>(a, s);
+hipError_t launch_rows(const KernelArgs &a, int trans_c, hipStream_t s) {
+    if (a.N == 1) return launch_shape<R, 1, VEC>(a, trans_c, s);
+    if (a.N == 2) return launch_shape<R, 2, VEC>(a, trans_c, s);
+    if (a.N <= 4) return launch_shape<R, 4, VEC>(a, trans_c, s);
+    return launch_shape<R, 8, VEC>(a, trans_c, s);
 }
 
 }  // namespace
 
-hipError_t launch_rowdot(int cfg, const KernelArgs &a, hipStream_t s) {
+hipError_t launch_rowdot(int cfg, const KernelArgs &a, hipStream_t s, int trans_c) {
     if (cfg != SGEMM_CFG_ROWDOT_N8 || a.N < 1 || a.N > 8 || a.trans_a || a.tiles_m < 1 || a.ipt < 1 ||
         (a.ipt > 1 && !a.partials) || rowdot_k_per(a.K, a.ipt) > kRowdotFloats / rowdot_cols(a.N))
         return hipErrorInvalidValue;
@@ -197,9 +205,10 @@ hipError_t launch_rowdot(int cfg, const KernelArgs &a, hipStream_t s) {
     // loads, four rows per wave once a block has at least four per wave
     // (16384 x 1 x 16383: 259 against 268 us with one).
     const bool vec = ((uintptr_t)a.A & 15) == 0 && (a.lda & 3) == 0;
-    if (vec) return launch_rows<1, true>(a, s);
+    const int tc = trans_c ? 1 : 0;
+    if (vec) return launch_rows<1, true>(a, tc, s);
     const int rows_per = (a.M + a.tiles_m - 1) / a.tiles_m;
-    return rows_per >= 4 * kWaves ? launch_rows<4, false>(a, s) : launch_rows<1, false>(a, s);
+    return rows_per >= 4 * kWaves ? launch_rows<4, false>(a, tc, s) : launch_rows<1, false>(a, tc, s);
 }
 
 hipError_t occupancy_rowdot(int cfg, int *wg_per_cu) {

@@ -43,13 +43,13 @@ std::mutex g_mu;
 std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
 
-hipError_t launch_cfg(int cfg, const KernelArgs &a, hipStream_t s) {
+hipError_t launch_cfg(int cfg, const KernelArgs &a, hipStream_t s, int trans_c = 0) {
     switch (kCfgs[cfg].kind) {
     case kKindMfma: return launch_mfma(cfg, a, s);
     case kKindMfmaDl: return launch_mfma_dl(cfg, a, s);
     case kKindGeneric: return launch_generic(cfg, a, s);
     case kKindSkinny: return launch_skinny(cfg, a, s);
-    case kKindRowdot: return launch_rowdot(cfg, a, s);
+    case kKindRowdot: return launch_rowdot(cfg, a, s, trans_c);
     default: return launch_valu(cfg, a, s);
     }
 }
@@ -142,10 +142,12 @@ struct Call {
     int repacked = 0;              // already laid out for the vector kernels by run_packed
     int cm = 0, cn = 0;            // C's rows and columns when the operands were padded
                                    // beyond them (run_packed); 0: M and N
+    int tc = 0;                    // C stored N x M: the transposed product of a call
+                                   // with few rows (transposed_route)
 
     // Rows and columns of C, and of A and B as stored.
-    int c_rows() const { return cm ? cm : M; }
-    int c_cols() const { return cn ? cn : N; }
+    int c_rows() const { return tc ? N : cm ? cm : M; }
+    int c_cols() const { return tc ? M : cn ? cn : N; }
     int a_rows() const { return ta ? K : M; }
     int a_cols() const { return ta ? M : K; }
     int b_rows() const { return tb ? N : K; }
@@ -189,6 +191,33 @@ bool vector_layout(const Call &c) { return vector_ab(c) && vector_c(c); }
 // Kernels that read A or B and write C one float at a time where needed, so
 // that no layout calls for repacking them.
 bool any_layout(int cfg) { return kCfgs[cfg].kind == kKindSkinny || kCfgs[cfg].kind == kKindRowdot; }
+
+// Few rows (M <= 8) with B stored N x K, as in x W^T with W row-major: the
+// tiled kernels spend a 64-row tile on them, the skinny kernel reads B along
+// N.  The transposed product C^T = B A^T streams B's rows on the row-dot
+// kernel instead (A as its few columns, C written transposed), where the
+// row-dot kernel's own rule would take that shape: at most 2 rows, B of
+// 2^26 elements or more, or a layout the tiled kernels cannot load.
+bool transposed_route(const Call &c) {
+    if (c.config != SGEMM_CFG_AUTO || c.tc || c.repacked || c.cm || c.cn || !c.tb || c.M > 8 || c.N < 256 ||
+        c.K < 256 || !c.reads_ab())
+        return false;
+    if (!(c.M <= 2 || (int64_t)c.N * c.K >= ((int64_t)1 << 26) || !vector_layout(c))) return false;
+    // The data-parallel schedule needs B's whole K range in LDS.
+    return c.sched != SGEMM_SCHED_DP || c.K <= kRowdotFloats / rowdot_cols(c.M);
+}
+
+// That transposed call: A' = B (N x K, rows of K), B' = A^T (A stored M x K
+// is B' stored N' x K; A stored K x M is B' stored K x N'), C' = C^T.
+Call transposed(const Call &c) {
+    Call q = c;
+    q.M = c.N; q.N = c.M;
+    q.A = c.B; q.lda = c.ldb; q.ta = 0;
+    q.B = c.A; q.ldb = c.lda; q.tb = c.ta ? 0 : 1;
+    q.tc = 1;
+    q.config = SGEMM_CFG_ROWDOT_N8;
+    return q;
+}
 
 // Stream-K workspace of (dev, stream), grown to hold `plan`'s partial
 // tiles.  Caller holds g_mu.
@@ -300,6 +329,8 @@ int run(const Call &c) {
         if ((st = check_device_range(c.B, extent_bytes(c.b_rows(), c.b_cols(), c.ldb), dev)) != SGEMM_OK) return st;
     }
 
+    if (transposed_route(c)) return run(transposed(c));
+
     // C written in place beyond padded operands (run_packed): the edge
     // variants store only C's own rows and columns.
     const bool c_own = c.cm != 0 || c.cn != 0;
@@ -359,10 +390,10 @@ int run(const Call &c) {
         Workspace w;
         if ((st = workspace_for(dev, c.stream, p, &w)) != SGEMM_OK) return st;
         a.partials = w.partials;
-        e = launch_cfg(p.config, a, c.stream);   // the skinny and row-dot kernels add their own splits
+        e = launch_cfg(p.config, a, c.stream, c.tc);   // the skinny and row-dot kernels add their own splits
         if (e == hipSuccess && !any_layout(p.config)) e = launch_sk_fixup(a, p.bm, p.bn, c.stream);
     } else {
-        e = launch_cfg(p.config, a, c.stream);
+        e = launch_cfg(p.config, a, c.stream, c.tc);
     }
     return e == hipSuccess ? SGEMM_OK : hip_fail(e);
 }
@@ -444,6 +475,13 @@ static int plan_for(int ta, int tb, int M, int N, int K, int config, int sched, 
     c.ta = ta;
     c.tb = tb;
     sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu, aligned ? 1 : 0, ta, tb};
+    const bool swap = M > 0 && N > 0 && sgemm::transposed_route(c);
+    if (swap) {
+        const sgemm::Call q = sgemm::transposed(c);
+        req = sgemm::PlanRequest{q.M, q.N, q.K, q.config, sched, num_cus, occupancy, sk_wg_per_cu,
+                                 aligned ? 1 : 0, q.ta, q.tb};
+    }
+    out->transposed = swap ? 1 : 0;
     sgemm::Plan p;
     int st = sgemm::make_plan(req, &p);
     if (st != SGEMM_OK) return st;

@@ -30,7 +30,9 @@
  *   float at a time when C's layout does not qualify; results as unpadded,
  *   C's padding untouched).  Thin products have kernels of their own that
  *   take any layout: at most 16 rows with B stored K x N
- *   (SGEMM_CFG_SKINNY_16x256), at most 2 columns, or 8 for large A or a
+ *   (SGEMM_CFG_SKINNY_16x256); at most 8 rows with B stored N x K (as in
+ *   x W^T with W row-major) run transposed, C^T = B A^T, on the row-dot
+ *   kernel when it would take that shape; at most 2 columns, or 8 for large A or a
  *   layout the tiled kernels cannot load, with A stored M x K
  *   (SGEMM_CFG_ROWDOT_N8).
  *
@@ -272,6 +274,9 @@ typedef struct sgemm_f32_plan_t {
     long long workspace_bytes;
     int repacked;        /* 1: A and B are first copied to padded buffers; the
                             fields above describe the padded product */
+    int transposed;      /* 1: the product runs transposed, C^T = op(B)^T op(A)^T
+                            (few rows with B stored N x K, on the row-dot
+                            kernel); the fields above describe that product */
 } sgemm_f32_plan_t;
 
 int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,

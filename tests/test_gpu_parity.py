@@ -1128,3 +1128,41 @@ def test_thin_kernels_with_unaligned_streamed_operand(dev, case):
     assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref)
     # The plan query (dense operands) picks the same kernel for this shape.
     assert sg.plan(M, N, K)["config"] == cfg
+
+
+# Few rows with B stored N x K (x W^T with W row-major): the product runs
+# transposed, C^T = B A^T, on the row-dot kernel, C written transposed.
+# (M, N, K, trans_a, C pad / offset, alpha, beta)
+TRANSPOSED_THIN = {
+    "gemv_wt": (1, 16384, 4096, 0, (0, 0), 1.0, 0.0),
+    "m2_ta_beta": (2, 300, 300, 1, (0, 0), 1.5, -0.5),
+    "m5_odd_k_padded_c": (5, 1000, 777, 0, (3, 1), 2.0, 1.0),
+    "m8_split": (8, 16384, 8192, 0, (0, 0), 1.0, 0.0),
+    "m3_long_k_ta": (3, 4097, 20000, 1, (1, 2), -1.0, 0.25),
+}
+
+
+@pytest.mark.parametrize("case", list(TRANSPOSED_THIN))
+def test_few_rows_with_b_stored_n_by_k_run_transposed(dev, case):
+    import torch
+    M, N, K, ta, (cpad, coff), alpha, beta = TRANSPOSED_THIN[case]
+    log(f"case transposed thin {case}: shape=({M},{N},{K}) ta={ta} C pad/off={cpad}/{coff} alpha={alpha} beta={beta}")
+    A, B = workloads.generate(M, N, K, "int4", 111)
+    C0 = workloads.generate(M, 1, N, "int4", 112)[0]
+    As = stored(A, ta)
+    Bs = np.ascontiguousarray(B.T)   # B stored N x K
+    ldc = N + cpad
+    buf = torch.full((M * ldc + coff + 4,), float("nan"), dtype=torch.float32, device=dev)
+    Cv = torch.as_strided(buf, (M, N), (ldc, 1), coff)
+    Cv.copy_(to_dev(C0, dev))
+    sg.gemm(to_dev(As, dev), to_dev(Bs, dev), Cv, alpha, beta, ta, 1)
+    torch.cuda.synchronize()
+    C_ref, _ = oracle.gemm_blas(As, Bs, C0, alpha, beta, ta, 1)
+    assert np.array_equal(Cv.cpu().numpy().astype(np.float64), C_ref)
+    full = torch.as_strided(buf, (M, ldc), (ldc, 1), coff).cpu().numpy()
+    assert np.all(np.isnan(full[:, N:])), "ldc padding was written"
+    # The plan query (dense operands) reports the transposed product where
+    # the layout is dense and vector-aligned or M <= 2 or B is large.
+    p = sg.plan(M, N, K, trans_a=ta, trans_b=1)
+    if p["transposed"]:
+        assert p["config"] == sg.CFG_ROWDOT_N8
