@@ -18,7 +18,9 @@ hipError_t launch_generic(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t occupancy_generic(int cfg, int *wg_per_cu);
 hipError_t launch_valu(int cfg, const KernelArgs &a, hipStream_t s);
 // The skinny kernel (M <= 16) and, for a K-split plan, the sum of its splits.
-hipError_t launch_skinny(int cfg, const KernelArgs &a, hipStream_t s);
+// trans_c: C stored N x M, element (m, n) at C[n * ldc + m] (the transposed
+// product of a call with few columns and A stored K x M).
+hipError_t launch_skinny(int cfg, const KernelArgs &a, hipStream_t s, int trans_c = 0);
 hipError_t occupancy_skinny(int cfg, int *wg_per_cu);
 // The row-dot kernel (N <= 8) and, for a K-split plan, the sum of its splits.
 // trans_c: C stored N x M, element (m, n) at C[n * ldc + m] (the transposed

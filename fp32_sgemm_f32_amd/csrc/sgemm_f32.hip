@@ -48,7 +48,7 @@ hipError_t launch_cfg(int cfg, const KernelArgs &a, hipStream_t s, int trans_c =
     case kKindMfma: return launch_mfma(cfg, a, s);
     case kKindMfmaDl: return launch_mfma_dl(cfg, a, s);
     case kKindGeneric: return launch_generic(cfg, a, s);
-    case kKindSkinny: return launch_skinny(cfg, a, s);
+    case kKindSkinny: return launch_skinny(cfg, a, s, trans_c);
     case kKindRowdot: return launch_rowdot(cfg, a, s, trans_c);
     default: return launch_valu(cfg, a, s);
     }
@@ -142,8 +142,8 @@ struct Call {
     int repacked = 0;              // already laid out for the vector kernels by run_packed
     int cm = 0, cn = 0;            // C's rows and columns when the operands were padded
                                    // beyond them (run_packed); 0: M and N
-    int tc = 0;                    // C stored N x M: the transposed product of a call
-                                   // with few rows (transposed_route)
+    int tc = 0;                    // C stored N x M: the transposed product of a thin
+                                   // call (transposed_route)
 
     // Rows and columns of C, and of A and B as stored.
     int c_rows() const { return tc ? N : cm ? cm : M; }
@@ -192,30 +192,42 @@ bool vector_layout(const Call &c) { return vector_ab(c) && vector_c(c); }
 // that no layout calls for repacking them.
 bool any_layout(int cfg) { return kCfgs[cfg].kind == kKindSkinny || kCfgs[cfg].kind == kKindRowdot; }
 
-// Few rows (M <= 8) with B stored N x K, as in x W^T with W row-major: the
-// tiled kernels spend a 64-row tile on them, the skinny kernel reads B along
-// N.  The transposed product C^T = B A^T streams B's rows on the row-dot
-// kernel instead (A as its few columns, C written transposed), where the
-// row-dot kernel's own rule would take that shape: at most 2 rows, B of
-// 2^26 elements or more, or a layout the tiled kernels cannot load.
-bool transposed_route(const Call &c) {
-    if (c.config != SGEMM_CFG_AUTO || c.tc || c.repacked || c.cm || c.cn || !c.tb || c.M > 8 || c.N < 256 ||
-        c.K < 256 || !c.reads_ab())
-        return false;
-    if (!(c.M <= 2 || (int64_t)c.N * c.K >= ((int64_t)1 << 26) || !vector_layout(c))) return false;
-    // The data-parallel schedule needs B's whole K range in LDS.
-    return c.sched != SGEMM_SCHED_DP || c.K <= kRowdotFloats / rowdot_cols(c.M);
+// Thin products whose stored layout the thin kernels cannot read, run as
+// the transposed product C^T = op(B)^T op(A)^T with C written transposed:
+// - few rows (M <= 8) with B stored N x K, as in x W^T with W row-major (the
+//   tiled kernels spend a 64-row tile on them, the skinny kernel reads B
+//   along N): on the row-dot kernel, B's rows streamed, where that kernel's
+//   own rule would take the shape (at most 2 rows, B of 2^26 elements or
+//   more, or a layout the tiled kernels cannot load);
+// - few columns (N <= 16) with A stored K x M, as in X^T v (the row-dot
+//   kernel reads A along K): on the skinny kernel, A's rows streamed, where
+//   its own rule would take the shape (at most 8 columns, A above 2^22
+//   elements, or a layout the tiled kernels cannot load).
+// Returns the configuration of the transposed product, or SGEMM_CFG_AUTO
+// for none.
+int transposed_route(const Call &c) {
+    if (c.config != SGEMM_CFG_AUTO || c.tc || c.repacked || c.cm || c.cn || c.K < 256 || !c.reads_ab())
+        return SGEMM_CFG_AUTO;
+    if (c.tb && c.M <= 8 && c.N >= 256 &&
+        (c.M <= 2 || (int64_t)c.N * c.K >= ((int64_t)1 << 26) || !vector_layout(c)) &&
+        (c.sched != SGEMM_SCHED_DP || c.K <= kRowdotFloats / rowdot_cols(c.M)))   // DP: B's K range in LDS
+        return SGEMM_CFG_ROWDOT_N8;
+    if (c.ta && c.N <= 16 && c.M >= 256 &&
+        (c.N <= 8 || (int64_t)c.M * c.K > ((int64_t)1 << 22) || !vector_layout(c)))
+        return SGEMM_CFG_SKINNY_16x256;
+    return SGEMM_CFG_AUTO;
 }
 
-// That transposed call: A' = B (N x K, rows of K), B' = A^T (A stored M x K
-// is B' stored N' x K; A stored K x M is B' stored K x N'), C' = C^T.
-Call transposed(const Call &c) {
+// That transposed call on configuration cfg: A' = op(B)^T, stored as B is
+// (B stored N x K is A' stored M' x K; B stored K x N is A' stored K x M'),
+// B' = op(A)^T likewise, C' = C^T.
+Call transposed(const Call &c, int cfg) {
     Call q = c;
     q.M = c.N; q.N = c.M;
-    q.A = c.B; q.lda = c.ldb; q.ta = 0;
+    q.A = c.B; q.lda = c.ldb; q.ta = c.tb ? 0 : 1;
     q.B = c.A; q.ldb = c.lda; q.tb = c.ta ? 0 : 1;
     q.tc = 1;
-    q.config = SGEMM_CFG_ROWDOT_N8;
+    q.config = cfg;
     return q;
 }
 
@@ -329,7 +341,8 @@ int run(const Call &c) {
         if ((st = check_device_range(c.B, extent_bytes(c.b_rows(), c.b_cols(), c.ldb), dev)) != SGEMM_OK) return st;
     }
 
-    if (transposed_route(c)) return run(transposed(c));
+    const int tcfg = transposed_route(c);
+    if (tcfg != SGEMM_CFG_AUTO) return run(transposed(c, tcfg));
 
     // C written in place beyond padded operands (run_packed): the edge
     // variants store only C's own rows and columns.
@@ -475,9 +488,10 @@ static int plan_for(int ta, int tb, int M, int N, int K, int config, int sched, 
     c.ta = ta;
     c.tb = tb;
     sgemm::PlanRequest req{M, N, K, config, sched, num_cus, occupancy, sk_wg_per_cu, aligned ? 1 : 0, ta, tb};
-    const bool swap = M > 0 && N > 0 && sgemm::transposed_route(c);
+    const int tcfg = M > 0 && N > 0 ? sgemm::transposed_route(c) : SGEMM_CFG_AUTO;
+    const bool swap = tcfg != SGEMM_CFG_AUTO;
     if (swap) {
-        const sgemm::Call q = sgemm::transposed(c);
+        const sgemm::Call q = sgemm::transposed(c, tcfg);
         req = sgemm::PlanRequest{q.M, q.N, q.K, q.config, sched, num_cus, occupancy, sk_wg_per_cu,
                                  aligned ? 1 : 0, q.ta, q.tb};
     }

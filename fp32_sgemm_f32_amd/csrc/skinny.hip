@@ -47,6 +47,12 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kCols = 256;            // columns per strip: 64 lanes x 4
 constexpr int kBlock = kSkinnyBlock;  // k per A staging block
 
+// C(m, n) of the product: C stored M x N, or N x M when trans_c (the
+// transposed product of a call with few columns and A stored K x M).
+__device__ __forceinline__ float *c_at(const KernelArgs &a, int trans_c, int m, int n) {
+    return trans_c ? a.C + (int64_t)n * a.ldc + m : a.C + (int64_t)m * a.ldc + n;
+}
+
 // A(m, k) of the product (A stored M x K, or K x M when trans_a).
 __device__ __forceinline__ float a_at(const KernelArgs &a, int m, int k) {
     return a.trans_a ? a.A[(int64_t)k * a.lda + m] : a.A[(int64_t)m * a.lda + k];
@@ -91,7 +97,7 @@ __device__ __forceinline__ f32x4 b_quad(const KernelArgs &a, int k, int strip, i
 
 template <int MR, bool VEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void sgemm_skinny_kernel(KernelArgs a) {
+void sgemm_skinny_kernel(KernelArgs a, int trans_c) {
     constexpr int kUnroll = 16;   // B loads in flight per lane
     // A block (k-major, MR floats per k), then the waves' sums.
     __shared__ __attribute__((aligned(16))) float as[kBlock * MR];
@@ -174,11 +180,13 @@ void sgemm_skinny_kernel(KernelArgs a) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             if (m >= a.M) break;
-            float *c = a.C + (int64_t)m * a.ldc;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = lane_col<VEC>(strip, lane, j);
-                if (VEC || n < a.N) c[n] = epilogue(a, acc[m][j], c + n);
+                if (VEC || n < a.N) {
+                    float *c = c_at(a, trans_c, m, n);
+                    *c = epilogue(a, acc[m][j], c);
+                }
             }
         }
     } else {
@@ -215,7 +223,7 @@ __device__ __forceinline__ int mf_col(int strip, int g, int q, int c) {
 
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void sgemm_skinny_mfma_kernel(KernelArgs a) {
+void sgemm_skinny_mfma_kernel(KernelArgs a, int trans_c) {
     constexpr int kGroup = 16;            // k per group: four 4-k steps, 16 B loads in flight per lane
     __shared__ __attribute__((aligned(16))) float as[kBlock * 16];            // [k][16 rows]
     __shared__ __attribute__((aligned(16))) float red[(kWaves / 2) * 16 * 4 * 64];   // [slot][step][r][lane]
@@ -324,7 +332,7 @@ void sgemm_skinny_mfma_kernel(KernelArgs a) {
                 const int m = 4 * kq + r;
                 if (m >= a.M) continue;
                 if (ks_count == 1) {
-                    float *cp = a.C + (int64_t)m * a.ldc + n;
+                    float *cp = c_at(a, trans_c, m, n);
                     *cp = epilogue(a, acc[4 * g + q][r], cp);
                 } else {
                     // partials[(ks * 16 + m) * Np + n], Np = strips * 256.
@@ -337,7 +345,7 @@ void sgemm_skinny_mfma_kernel(KernelArgs a) {
 // C(m, n..n+3) = the KS partial sums added in split order, then the
 // epilogue: one thread per 4 outputs (the last quad of a row may end at N),
 // up to 8 splits' loads in flight.
-__global__ __launch_bounds__(256) void sgemm_skinny_sum_kernel(KernelArgs a) {
+__global__ __launch_bounds__(256) void sgemm_skinny_sum_kernel(KernelArgs a, int trans_c) {
     const int quads = (a.N + 3) / 4;
     const int64_t total = (int64_t)a.M * quads;
     const int64_t np = (int64_t)a.tiles_n * kCols;
@@ -356,17 +364,19 @@ __global__ __launch_bounds__(256) void sgemm_skinny_sum_kernel(KernelArgs a) {
             for (int u = 0; u < 8; ++u)
                 if (s0 + u < ks_count) sum += v[u];
         }
-        float *c = a.C + (int64_t)m * a.ldc + n;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (n + j < a.N) c[j] = epilogue(a, sum[j], c + j);
+            if (n + j < a.N) {
+                float *c = c_at(a, trans_c, m, n + j);
+                *c = epilogue(a, sum[j], c);
+            }
     }
 }
 
 // The KS partial sums are added by a second kernel when K is split.
-hipError_t launch_with_sum(const void *f, const KernelArgs &a, hipStream_t s) {
+hipError_t launch_with_sum(const void *f, const KernelArgs &a, int trans_c, hipStream_t s) {
     KernelArgs args = a;
-    void *params[] = {&args};
+    void *params[] = {&args, &trans_c};
     hipError_t e = hipLaunchKernel(f, dim3(a.grid), dim3(kThreads), params, 0, s);
     if (e != hipSuccess || a.ipt <= 1) return e;
     const int64_t threads = (int64_t)a.M * ((a.N + 3) / 4);
@@ -377,7 +387,7 @@ hipError_t launch_with_sum(const void *f, const KernelArgs &a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_skinny(int cfg, const KernelArgs &a, hipStream_t s) {
+hipError_t launch_skinny(int cfg, const KernelArgs &a, hipStream_t s, int trans_c) {
     if (cfg != SGEMM_CFG_SKINNY_16x256 || a.M < 1 || a.M > 16 || a.trans_b ||
         (a.ipt > 1 && !a.partials))
         return hipErrorInvalidValue;
@@ -387,7 +397,7 @@ hipError_t launch_skinny(int cfg, const KernelArgs &a, hipStream_t s) {
     if (a.M <= 4) f = vec ? (const void *)sgemm_skinny_kernel<4, true> : (const void *)sgemm_skinny_kernel<4, false>;
     else if (a.M <= 8) f = vec ? (const void *)sgemm_skinny_kernel<8, true> : (const void *)sgemm_skinny_kernel<8, false>;
     else f = vec ? (const void *)sgemm_skinny_mfma_kernel<true> : (const void *)sgemm_skinny_mfma_kernel<false>;
-    return launch_with_sum(f, a, s);
+    return launch_with_sum(f, a, trans_c ? 1 : 0, s);
 }
 
 hipError_t occupancy_skinny(int cfg, int *wg_per_cu) {

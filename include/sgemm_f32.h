@@ -32,7 +32,9 @@
  *   take any layout: at most 16 rows with B stored K x N
  *   (SGEMM_CFG_SKINNY_16x256); at most 8 rows with B stored N x K (as in
  *   x W^T with W row-major) run transposed, C^T = B A^T, on the row-dot
- *   kernel when it would take that shape; at most 2 columns, or 8 for large A or a
+ *   kernel, and at most 16 columns with A stored K x M (as in X^T v) on the
+ *   skinny kernel, each when that kernel would take the transposed shape;
+ *   at most 2 columns, or 8 for large A or a
  *   layout the tiled kernels cannot load, with A stored M x K
  *   (SGEMM_CFG_ROWDOT_N8).
  *
@@ -275,8 +277,9 @@ typedef struct sgemm_f32_plan_t {
     int repacked;        /* 1: A and B are first copied to padded buffers; the
                             fields above describe the padded product */
     int transposed;      /* 1: the product runs transposed, C^T = op(B)^T op(A)^T
-                            (few rows with B stored N x K, on the row-dot
-                            kernel); the fields above describe that product */
+                            (few rows with B stored N x K on the row-dot
+                            kernel, few columns with A stored K x M on the
+                            skinny kernel); the fields above describe it */
 } sgemm_f32_plan_t;
 
 int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,

@@ -1166,3 +1166,39 @@ def test_few_rows_with_b_stored_n_by_k_run_transposed(dev, case):
     p = sg.plan(M, N, K, trans_a=ta, trans_b=1)
     if p["transposed"]:
         assert p["config"] == sg.CFG_ROWDOT_N8
+
+
+# Few columns with A stored K x M (X^T v with X row-major): the product runs
+# transposed, C^T = op(B)^T A_stored, on the skinny kernel, C written
+# transposed.  (M, N, K, trans_b, C pad / offset, alpha, beta)
+TRANSPOSED_FEW_COLUMNS = {
+    "xt_v": (16384, 1, 4096, 0, (0, 0), 1.0, 0.0),
+    "n8_tb_beta": (3000, 8, 2500, 1, (0, 0), 1.5, -0.5),
+    "n12_split_padded_c": (4096, 12, 8192, 0, (2, 1), 2.0, 1.0),
+    "n16_odd_m": (4099, 16, 3000, 0, (0, 0), 1.0, 0.0),
+    "n3_small_tb": (1000, 3, 1000, 1, (1, 1), -1.0, 0.5),
+}
+
+
+@pytest.mark.parametrize("case", list(TRANSPOSED_FEW_COLUMNS))
+def test_few_columns_with_a_stored_k_by_m_run_transposed(dev, case):
+    import torch
+    M, N, K, tb, (cpad, coff), alpha, beta = TRANSPOSED_FEW_COLUMNS[case]
+    log(f"case transposed few columns {case}: shape=({M},{N},{K}) tb={tb} C pad/off={cpad}/{coff} "
+        f"alpha={alpha} beta={beta}")
+    A, B = workloads.generate(M, N, K, "int4", 113)
+    C0 = workloads.generate(M, 1, N, "int4", 114)[0]
+    As = stored(A, 1)   # A stored K x M
+    Bs = stored(B, tb)
+    ldc = N + cpad
+    buf = torch.full((M * ldc + coff + 4,), float("nan"), dtype=torch.float32, device=dev)
+    Cv = torch.as_strided(buf, (M, N), (ldc, 1), coff)
+    Cv.copy_(to_dev(C0, dev))
+    sg.gemm(to_dev(As, dev), to_dev(Bs, dev), Cv, alpha, beta, 1, tb)
+    torch.cuda.synchronize()
+    C_ref, _ = oracle.gemm_blas(As, Bs, C0, alpha, beta, 1, tb)
+    assert np.array_equal(Cv.cpu().numpy().astype(np.float64), C_ref)
+    full = torch.as_strided(buf, (M, ldc), (ldc, 1), coff).cpu().numpy()
+    assert np.all(np.isnan(full[:, N:])), "ldc padding was written"
+    p = sg.plan(M, N, K, trans_a=1, trans_b=tb)
+    assert p["transposed"] == 1 and p["config"] == sg.CFG_SKINNY_16x256
