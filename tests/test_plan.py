@@ -384,3 +384,40 @@ def test_empty_shapes_plan_no_work():
     for shape in [(0, 128, 32), (128, 0, 32), (128, 128, 0)]:
         p = sg.plan(*shape, num_cus=256, occupancy=OCC)
         assert p["sk_tiles"] == 0 and p["workspace_bytes"] == 0
+
+
+def test_thin_products_in_other_storage_orders_run_transposed():
+    """Few rows with B stored N x K go to the row-dot kernel, and few
+    columns with A stored K x M to the skinny kernel, as the transposed
+    product (C^T = op(B)^T op(A)^T), where that kernel's own rule would take
+    the transposed shape; the plan is the transposed product's."""
+    occ = OCC
+
+    def plan(M, N, K, ta, tb, sched=sg.SCHED_AUTO, config=sg.CFG_AUTO):
+        return sg.plan(M, N, K, config, sched, num_cus=256, occupancy=occ, trans_a=ta, trans_b=tb)
+
+    # x W^T: at most 2 rows, B of 2^26 elements or more, or an unaligned layout.
+    for shape in [(1, 16384, 16384), (2, 4096, 1024), (8, 16384, 8192), (5, 1000, 777), (8, 4096, 4095)]:
+        p = plan(*shape, 0, 1)
+        assert (p["config"], p["transposed"]) == (sg.CFG_ROWDOT_N8, 1), shape
+        M, N, K = shape
+        assert p["tiles_m"] * p["tile_m"] >= N and p["tiles_n"] == 1   # rows of the transposed product: N
+        check_plan(p, N, M, K)
+    # Not taken: more than 8 rows, a small aligned B with 3-8 rows, N or K
+    # under 256, B stored K x N, a forced configuration, or the data-parallel
+    # schedule with B's K range beyond LDS.
+    for shape, ta, tb, sched, config in [((9, 16384, 16384), 0, 1, 0, 0), ((4, 4096, 4096), 0, 1, 0, 0),
+                                         ((1, 255, 4096), 0, 1, 0, 0), ((1, 4096, 255), 0, 1, 0, 0),
+                                         ((1, 16384, 16384), 0, 0, 0, 0),
+                                         ((1, 16384, 16384), 0, 1, 0, sg.CFG_DL_64x64x64),
+                                         ((1, 4096, 32768), 0, 1, sg.SCHED_DP, 0)]:
+        assert plan(*shape, ta, tb, sched, config)["transposed"] == 0, (shape, ta, tb, sched, config)
+    # X^T v: at most 8 columns, A above 2^22 elements, or an unaligned layout.
+    for shape, tb in [((16384, 1, 16384), 0), ((4096, 12, 4096), 0), ((1000, 3, 1000), 1), ((4099, 16, 3000), 0)]:
+        p = plan(*shape, 1, tb)
+        assert (p["config"], p["transposed"]) == (sg.CFG_SKINNY_16x256, 1), shape
+        M, N, K = shape
+        check_plan(p, N, M, K)
+    for shape, tb in [((300, 12, 300), 0), ((16384, 17, 16384), 0), ((255, 1, 4096), 0), ((16384, 1, 16384), 1)]:
+        p = plan(*shape, 0 if shape == (16384, 1, 16384) else 1, tb)
+        assert p["transposed"] == 0, shape
