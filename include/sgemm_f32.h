@@ -23,7 +23,7 @@
  *   16-byte aligned, the 16-byte vector kernels run (tile edges masked
  *   where the shape is not a multiple of the tile).  Any other layout runs
  *   on a general kernel with element-wise bounds checks, except that with
- *   the automatic configuration, M, N, K >= 64 and M * N * K at least 2^25,
+ *   the automatic configuration and M * N * K at least 2^25,
  *   A and B are first copied on `stream` into zero-padded aligned buffers
  *   of the library (each only when its own layout does not qualify) and the
  *   product runs on the vector kernels, which then write C in place (one

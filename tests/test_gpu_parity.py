@@ -759,6 +759,10 @@ REPACK_CASES = {
     # Only C off the vector grid: nothing copied, C stored one float at a time.
     "c_offset_beta": (0, 0, 1024, 1024, 1024, (0, 0, 0), (0, 0, 1), 1.0, 1.0),
     "tt_c_odd_ld": (1, 1, 1024, 1024, 1024, (0, 0, 3), (0, 0, 0), -1.0, 0.5),
+    # A side shorter than the thin kernels leave to the tiled ones: 9 columns
+    # (B's rows of 9 floats) and 33 rows.
+    "nine_columns": (0, 0, 4096, 9, 4100, (0, 0, 0), (0, 0, 0), 1.0, 0.0),
+    "thirty_three_rows_beta": (0, 0, 33, 4097, 4096, (0, 0, 0), (0, 0, 0), 2.0, 1.0),
 }
 
 
