@@ -1206,3 +1206,48 @@ def test_few_columns_with_a_stored_k_by_m_run_transposed(dev, case):
     assert np.all(np.isnan(full[:, N:])), "ldc padding was written"
     p = sg.plan(M, N, K, trans_a=1, trans_b=tb)
     assert p["transposed"] == 1 and p["config"] == sg.CFG_SKINNY_16x256
+
+
+@pytest.mark.parametrize("case", ["x_wt", "xt_v"])
+def test_graph_capture_of_transposed_thin_products(dev, case):
+    """The transposed routes (x W^T on the row-dot kernel, X^T v on the
+    skinny kernel, both with K split) captured after an eager call: every
+    replay, with a new small operand and eager work in between, matches the
+    oracle and the eager result exactly (integer inputs)."""
+    import torch
+    if case == "x_wt":
+        M, N, K, ta, tb = 2, 4096, 16384, 0, 1       # A: x (2 x K), B stored N x K
+    else:
+        M, N, K, ta, tb = 4096, 4, 16384, 1, 0       # A stored K x M, B: v (K x 4)
+    p = sg.plan(M, N, K, num_cus=torch.cuda.get_device_properties(dev).multi_processor_count,
+                trans_a=ta, trans_b=tb)
+    assert p["transposed"] == 1 and p["sk_tiles"] > 0
+    log(f"case graph capture transposed thin {case} ({M},{N},{K}) ta={ta} tb={tb} plan={p}")
+    s = torch.cuda.Stream(device=dev)
+    A0, B0 = workloads.generate(M, N, K, "int4", 115)
+    As, Bs = stored(A0, ta), stored(B0, tb)
+    Ad, Bd = to_dev(As, dev), to_dev(Bs, dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    with torch.cuda.stream(s):
+        sg.gemm(Ad, Bd, C, 1.0, 0.0, ta, tb)                # eager: workspace ready
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        sg.gemm(Ad, Bd, C, 1.0, 0.0, ta, tb)
+    torch.cuda.synchronize()
+    small_is_a = case == "x_wt"
+    for r in range(3):
+        X = workloads.generate(M, N, K, "int4", 240 + r)[0 if small_is_a else 1]
+        if small_is_a:
+            As = stored(X, ta); Ad.copy_(to_dev(As, dev))
+        else:
+            Bs = stored(X, tb); Bd.copy_(to_dev(Bs, dev))
+        E = torch.empty_like(C)
+        sg.gemm(Ad, Bd, E, 1.0, 0.0, ta, tb)                # eager reference on the device
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        C_ref, _ = oracle.gemm_blas(As, Bs, np.zeros((M, N), np.float32), 1.0, 0.0, ta, tb)
+        got = C.cpu().numpy()
+        assert np.array_equal(got.astype(np.float64), C_ref), f"replay {r}"
+        assert np.array_equal(got, E.cpu().numpy()), f"replay {r} vs eager"
