@@ -37,6 +37,26 @@ def test_exports_match_header():
         assert hasattr(lib, name)
 
 
+def test_plan_struct_matches_header():
+    """The binding's plan structure has the header's fields, in order, with
+    the same C types (int / long long), so the plan query fills it as the
+    library writes it."""
+    import ctypes
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct sgemm_f32_plan_t \{(.*?)\} sgemm_f32_plan_t;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        m = re.match(r"(long long|int)\s+(.*)", decl)
+        assert m, decl
+        ctype = ctypes.c_longlong if m.group(1) == "long long" else ctypes.c_int
+        fields += [(name.strip(), ctype) for name in m.group(2).split(",")]
+    assert [(n, t) for n, t in sg._Plan._fields_] == fields
+
+
 def test_granule():
     # Any shape: ragged edges are masked.
     assert sg.granule() == (1, 1, 1)
