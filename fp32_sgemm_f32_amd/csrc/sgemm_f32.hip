@@ -39,7 +39,8 @@ struct Workspace {
     int64_t pack_bytes = 0;
 };
 
-std::mutex g_mu;
+// Recursive: a repacked call holds it across its nested call of run().
+std::recursive_mutex g_mu;
 std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
 
@@ -74,7 +75,7 @@ int env_int(const char *name, int dflt) {
 // Compute-unit count and per-configuration occupancy of the current device
 // (queried once per device).
 int device_info(int dev, DeviceInfo *out) {
-    std::lock_guard<std::mutex> lock(g_mu);
+    std::lock_guard<std::recursive_mutex> lock(g_mu);
     DeviceInfo &d = g_devices[dev];
     if (!d.ready) {
         int cus = 0;
@@ -252,7 +253,7 @@ int workspace_for(int dev, hipStream_t s, const Plan &p, Workspace *out) {
 
 // Repacking buffer of (dev, stream) holding at least `bytes`.  Takes g_mu.
 int pack_space_for(int dev, hipStream_t s, int64_t bytes, float **out) {
-    std::lock_guard<std::mutex> lock(g_mu);
+    std::lock_guard<std::recursive_mutex> lock(g_mu);
     Workspace &w = g_workspaces[{dev, s}];
     if (w.pack_bytes < bytes) {
         hipError_t e = hipStreamSynchronize(s);   // the old buffer may still be in use
@@ -300,7 +301,13 @@ bool worth_repacking(const Call &c) {
 // columns (one float at a time when its layout rules out vector stores), so
 // it is neither copied in nor back.  All on the caller's stream, in the
 // library's per-stream repacking buffer.
+//
+// The lock is held from taking the buffer to the last launch of the product:
+// another thread's call on the same stream could otherwise enqueue its own
+// copies into the same buffer between this call's copy and its GEMM, or
+// grow the buffer (free it) before this call's copy is enqueued.
 int run_packed(const Call &c, int dev) {
+    std::lock_guard<std::recursive_mutex> lock(g_mu);
     const int Mp = c.ta ? up4(c.M) : c.M, Np = up4(c.N), Kp = up4(c.K);
     const int ar = c.ta ? Kp : Mp, ac = c.ta ? Mp : Kp;     // A as stored, padded
     const int br = c.tb ? Np : Kp, bc = c.tb ? Kp : Np;
@@ -404,7 +411,7 @@ int run(const Call &c) {
         // Workspace acquisition and launch under the lock, so that a
         // concurrent call on the same stream cannot replace the buffers
         // between the two.
-        std::lock_guard<std::mutex> lock(g_mu);
+        std::lock_guard<std::recursive_mutex> lock(g_mu);
         Workspace w;
         if ((st = workspace_for(dev, c.stream, p, &w)) != SGEMM_OK) return st;
         a.partials = w.partials;
@@ -545,7 +552,7 @@ SGEMM_API int sgemm_f32_gemm_plan(int trans_a, int trans_b, int M, int N, int K,
 }
 
 SGEMM_API int sgemm_f32_release(void) {
-    std::lock_guard<std::mutex> lock(sgemm::g_mu);
+    std::lock_guard<std::recursive_mutex> lock(sgemm::g_mu);
     int st = SGEMM_OK;
     for (auto &kv : sgemm::g_workspaces) {
         if (kv.second.partials && hipFree(kv.second.partials) != hipSuccess) st = SGEMM_ERR_HIP;
