@@ -1,14 +1,15 @@
-"""Generated code of the direct-to-LDS kernels (no GPU): their K loops must
-hold no vector ALU instruction between the MFMAs.
+"""Generated code of the direct-to-LDS kernels (no GPU), compiled here for
+gfx950:
 
-On gfx950 one vector ALU instruction between two dependent
-v_mfma_f32_32x32x2_f32 stalls the second for most of an MFMA's duration,
-and these kernels read their LDS operands with inline-asm loads whose
-results arrive later (waited for with explicit s_waitcnt): a register copy
-the compiler might insert between such a load and its wait would read the
-value too early.  Both show up as vector ALU instructions in the loop blocks
-that carry the MFMAs, which this test compiles the source for gfx950 and
-looks for."""
+* correctness: these kernels read their LDS operands with inline-asm loads
+  whose results arrive later and are waited for with explicit s_waitcnt; the
+  compiler does not know they are in flight and could copy or reuse a
+  destination before its wait.  A dataflow pass over every kernel's control
+  flow graph (asm_hazards) finds any instruction that names the destination
+  of an LDS read not yet covered by an `s_waitcnt lgkmcnt`;
+* speed: their K loops hold no vector ALU instruction between the MFMAs (on
+  gfx950 one between two dependent v_mfma_f32_32x32x2_f32 stalls the second
+  for most of an MFMA's duration), and no kernel spills to scratch."""
 import os
 import re
 import shutil
@@ -16,6 +17,7 @@ import subprocess
 
 import pytest
 
+import asm_hazards
 from fp32_sgemm_f32_amd import build
 
 SRC = os.path.join(build.CSRC, "gemm_mfma_dl.hip")
@@ -108,3 +110,71 @@ def test_no_kernel_spills_to_scratch(dl_asm):
     for name, body in descriptors:
         m = re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", body)
         assert m and m.group(1) == "0", f"{name}: private segment {m and m.group(1)}"
+
+
+def test_no_lds_read_used_before_its_wait(dl_asm):
+    """No instruction of any direct-to-LDS kernel (any block, loop or not,
+    split or whole-tile instance) reads or writes a register that an LDS
+    read is still loading."""
+    fs = asm_hazards.functions(dl_asm, r"_Z\w*sgemm_mfma_dl_kernel\w*")
+    assert len(fs) == 2 * (9 + 4 * 3 + 4 * 4)
+    bad = {name[:100]: found[:3] for name, blocks in fs.items() if (found := asm_hazards.hazards(blocks))}
+    assert not bad, f"LDS read destinations used before their wait: {bad}"
+
+
+PLANTED = {
+    # name: (instructions, hazards expected)
+    "copy_before_wait": (["ds_read_b128 v[0:3], v8", "v_mov_b32 v10, v2"], 1),
+    "wait_then_copy": (["ds_read_b128 v[0:3], v8", "s_waitcnt lgkmcnt(0)", "v_mov_b32 v10, v2"], 0),
+    # lgkmcnt(1) covers a read only once another LDS operation follows it.
+    "partial_wait_too_early": (["ds_read_b32 v0, v8", "s_waitcnt lgkmcnt(1)", "v_add_f32 v1, v0, v0"], 1),
+    "partial_wait_covered": (["ds_read_b32 v0, v8", "ds_read_b32 v1, v9", "s_waitcnt lgkmcnt(1)",
+                              "v_add_f32 v2, v0, v0"], 0),
+    "partial_wait_newest_pending": (["ds_read_b32 v0, v8", "ds_read_b32 v1, v9", "s_waitcnt lgkmcnt(1)",
+                                     "v_add_f32 v2, v1, v1"], 1),
+    # A scalar load completes out of order: it does not cover the LDS read.
+    "scalar_load_does_not_count": (["ds_read_b32 v0, v8", "s_load_dword s0, s[2:3], 0x0",
+                                    "s_waitcnt lgkmcnt(1)", "v_mov_b32 v1, v0"], 1),
+    "mfma_operand_early": (["ds_read_b128 v[4:7], v8", "v_mfma_f32_32x32x2_f32 a[0:15], v4, v5, a[0:15]"], 1),
+    "overwritten_in_flight": (["ds_read_b32 v0, v8", "v_mov_b32 v0, 0"], 1),
+    "address_of_next_read": (["ds_read_b32 v0, v8", "ds_read_b32 v1, v0"], 1),
+    "raw_immediate_wait": (["ds_read_b32 v0, v8", "s_waitcnt 0xc07f", "v_mov_b32 v1, v0"], 0),
+}
+
+
+@pytest.mark.parametrize("case", list(PLANTED))
+def test_hazard_check_on_planted_snippets(case):
+    ins, expected = PLANTED[case]
+    assert len(asm_hazards.hazards([("entry", ins)])) == expected
+
+
+def test_hazard_check_follows_branches_and_loops():
+    # A read issued at the end of a loop body, used at the loop head before
+    # any wait: only the back edge carries it.
+    loop = [("entry", ["s_mov_b32 s0, 0"]),
+            (".LBB0_1:", ["v_mov_b32 v5, v0", "s_waitcnt lgkmcnt(0)", "ds_read_b32 v0, v8",
+                          "s_cmp_lt_i32 s0, 4", "s_cbranch_scc1 .LBB0_1"]),
+            ("tail", ["s_endpgm"])]
+    assert len(asm_hazards.hazards(loop)) == 1
+    # A read pending only on the taken side of a branch.
+    branch = [("entry", ["s_cmp_eq_u32 s0, 0", "s_cbranch_scc1 .LBB0_2"]),
+              ("u1", ["ds_read_b32 v0, v8", "s_branch .LBB0_3"]),
+              (".LBB0_2:", ["s_nop 0"]),
+              (".LBB0_3:", ["v_mov_b32 v1, v0", "s_endpgm"])]
+    assert len(asm_hazards.hazards(branch)) == 1
+
+
+def test_hazard_check_catches_a_removed_wait(dl_asm):
+    """Deleting one lgkmcnt wait ahead of an MFMA in a real kernel's K loop
+    must be caught."""
+    fs = asm_hazards.functions(dl_asm, r"_Z\w*sgemm_mfma_dl_kernel\w*")
+    name = sorted(fs)[0]
+    blocks = fs[name]
+    for bi, (label, ins) in enumerate(blocks):
+        for k in range(len(ins) - 1):
+            if ins[k].startswith("s_waitcnt lgkmcnt") and ins[k + 1].startswith("v_mfma"):
+                planted = list(blocks)
+                planted[bi] = (label, ins[:k] + ins[k + 1:])
+                assert asm_hazards.hazards(planted), (name, label, k)
+                return
+    pytest.fail("no lgkmcnt wait ahead of an MFMA found")
