@@ -1,21 +1,27 @@
 """Benchmark of the FP32 GEMM (C = A @ B, row-major, AB only) on one MI355X.
 
 Prints ONE JSON line on stdout: FP32 SGEMM TFLOP/s (2*M*N*K / t) of the
-headline 4096^3 workload (or --workload), with inputs resident in HBM, K
-back-to-back calls timed between two device synchronisations (after W
-untimed calls, continued to at least --warm-seconds so that the shader clock
-has ramped up), plus:
-  * "roofline": per-launch kernel time from HIP events recorded on the
-    launch stream, against the MI355X FP32 matrix peak (157.3 TFLOP/s);
-  * "cpu_baseline": the FP64 CPU oracle timed on a bounded row sample of the
-    same product, on this host's cores.
-The line also carries the median single-call time with a 512 MiB buffer
-written before each call (caches flushed: "cold_median_event_tflops").
-Details (every workload with --all, the plan, a torch.matmul context figure)
-go to stderr and to --detail FILE.
+headline 4096^3 workload (or --workload / --shape).  The timing protocol is
+the one the page "Beyond Kernel 7: Closing the Gap to cuBLAS on an H100 FP32
+GEMM" uses for its confirmed result, with the cache flush sized for MI355X:
+before every timed call a 512 MiB buffer is written (more than the 32 MiB of
+L2 plus the 256 MiB MALL, so A and B come from HBM), outside the HIP-event
+pair that times the call; `value` is the median of the K single-call times.
+The line also carries:
+  * "warm": the same calls back to back with nothing between them (A and B
+    then stay in the caches);
+  * "sizes": the other measured workloads (1024^3 and its integer variant,
+    2048^3, 256^3, 1024 x 1024 x 16384), flushed and warm medians each;
+  * "roofline": algorithmic FLOPs per launch over the kernel's mean launch
+    duration in the flushed timed region (HIP events on the launch stream),
+    against the MI355X FP32 matrix peak (157.3 TFLOP/s);
+  * "cpu_baseline": the FP64 CPU oracle timed on a bounded sample of the
+    same product on this host's cores.
+Details (the plan, a torch.matmul context figure with --torch) go to stderr
+and to --detail FILE.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--warm-seconds 0.5] [--workload NAME]
-                       [--config N] [--sched N] [--all] [--no-cpu-baseline]
+                       [--shape MxNxK] [--config N] [--sched N] [--no-sizes] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -33,16 +39,14 @@ import workloads  # noqa: E402
 
 PEAK_FP32_TFLOPS = 157.3          # MI355X dense FP32 (vector with packed FMA, or matrix)
 PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
-PEAK_HBM_GBS = 8000.0
-# The pages' own kernel at 4096^3 on an H100 (context, other hardware): "Beyond
-# Kernel 7", section "The confirmed result", k13f 2761.2 us = 49.8 TFLOP/s.
-PAGES_4096_TFLOPS = 49.8
+FLUSH_MIB = 512                   # written before each timed call: > L2 (32 MiB) + MALL (256 MiB)
+FLUSHED_WARMUP_CALLS, FLUSHED_WARMUP_S = 20, 0.1
 
-# HBM-side bytes per launch of the headline kernel, from two rocprofv3 --pmc
-# runs (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by what the
-# same counter reads for a plain 256 MiB device copy (FETCH_SIZE 2.0, WRITE_SIZE
-# 1.0); see profiles/sgemm_4096_dl_256x256x16_counters.md.  Valid only for the
-# kernel sources they were taken on (digest below); otherwise reported null.
+# HBM-side bytes per launch of the headline kernel in the flushed protocol,
+# from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE in KiB per dispatch),
+# each scaled by what the same counter reads for a plain 256 MiB device copy
+# (FETCH_SIZE 2.0, WRITE_SIZE 1.0).  Valid only for the kernel sources they
+# were taken on (digest below); otherwise reported null.
 TRAFFIC = {
     "kernel": "dl_256x256x16", "workload": "sgemm_4096",
     "source_digest": "c901998312e62bc7",
@@ -94,10 +98,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--config", type=int, default=0)
     ap.add_argument("--sched", type=int, default=0)
-    ap.add_argument("--all", action="store_true", help="also time every workload (details only)")
-    ap.add_argument("--cold", action="store_true", help="with --all: also time the other workloads with "
-                    "caches flushed before each call (the headline always is)")
-    ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed timing of the headline")
+    ap.add_argument("--no-sizes", action="store_true", help="skip the other workloads")
+    ap.add_argument("--size-steps", type=int, default=30, help="timed calls per other workload and protocol")
     ap.add_argument("--torch", action="store_true", help="also time torch.matmul (context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -132,13 +134,11 @@ def warm_up(fn, calls, min_seconds):
     return done
 
 
-def time_region(fn, stream, steps, warmup, min_warm_s=0.0):
-    """The timed region: `steps` back-to-back calls between two device
-    synchronisations, with one HIP event pair recorded on `stream` around
-    them (nothing between the calls).  Returns (wall s, event ms, warm-up
-    calls made)."""
+def time_region(fn, stream, steps):
+    """`steps` back-to-back calls between two device synchronisations, with
+    one HIP event pair recorded on `stream` around them (nothing between the
+    calls).  Returns (wall s, event ms)."""
     import torch
-    warm = warm_up(fn, warmup, min_warm_s)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -147,19 +147,17 @@ def time_region(fn, stream, steps, warmup, min_warm_s=0.0):
         fn()
     end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return wall, start.elapsed_time(end), warm
+    return time.perf_counter() - t0, start.elapsed_time(end)
 
 
-def time_calls(fn, stream, steps, warmup, flush=None, min_warm_s=0.0):
-    """Per-call HIP-event times (ms) on `stream` (an event pair around each
-    call: the distribution of single-call times), plus the total wall of the
-    run and the warm-up calls made."""
+def time_calls(fn, stream, steps, flush=None):
+    """`steps` calls between two device synchronisations, each inside its
+    own HIP event pair on `stream`; `flush` (if given) runs before each pair,
+    outside it.  Returns (per-call ms, wall s of the whole region)."""
     import torch
-    warm = warm_up(fn, warmup, min_warm_s)
-    torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         if flush is not None:
@@ -169,11 +167,19 @@ def time_calls(fn, stream, steps, warmup, flush=None, min_warm_s=0.0):
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return per, wall, warm
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
 
 
-def bench_workload(sg, w, args, dev, stream, cold=False, with_torch=False):
+def stats(per_ms, flops):
+    med = statistics.median(per_ms)
+    return {"median_ms": med, "mean_ms": statistics.fmean(per_ms), "min_ms": min(per_ms),
+            "p90_ms": float(np.percentile(per_ms, 90)), "tflops_median": flops / (med * 1e-3) / 1e12}
+
+
+def bench_workload(sg, w, dev, stream, flush, steps, warmup, warm_seconds, config=0, sched=0,
+                   with_torch=False):
+    """One workload: a correctness sanity check, the warm-up, then the
+    flushed timed region (the headline protocol), then the warm ones."""
     import torch
     A, B = workloads.generate_workload(w)
     Ad = torch.from_numpy(A).to(dev)
@@ -183,7 +189,7 @@ def bench_workload(sg, w, args, dev, stream, cold=False, with_torch=False):
 
     def call():
         st = sg.sgemm_raw(w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), w.N, Cd.data_ptr(), w.N,
-                          stream.cuda_stream, args.config, args.sched)
+                          stream.cuda_stream, config, sched)
         if st != sg.OK:
             raise sg.SgemmError(st)
 
@@ -199,45 +205,34 @@ def bench_workload(sg, w, args, dev, stream, cold=False, with_torch=False):
     sane = bool(torch.all(err <= 1e-5 * scale).item()) and bool(torch.isfinite(Cd).all().item())
     del ref, scale, err
 
-    with torch.cuda.stream(stream):
-        wall, region_ms, warm = time_region(call, stream, args.steps, args.warmup, args.warm_seconds)
-        # Single-call distribution, in a second pass (the event pairs around
-        # each call put gaps between the kernels, so they stay out of the
-        # timed region).
-        per, _, _ = time_calls(call, stream, args.steps, 0)
     flops = w.flops
+    with torch.cuda.stream(stream):
+        warm_calls = warm_up(call, warmup, warm_seconds)
+        # Flushed calls, untimed, before the flushed timed region: after a run
+        # of back-to-back calls the first ~20 flushed ones on MI355X take up to
+        # 20% longer and settle over ~20 ms (measured: 1092, 1084, 1070, ...
+        # 915 us at 4096^3), a transient of the switch, not of the protocol.
+        warm_up(lambda: (flush(), call()), FLUSHED_WARMUP_CALLS, FLUSHED_WARMUP_S)
+        cold, cold_wall = time_calls(call, stream, steps, flush=flush)
+        region_wall, region_ms = time_region(call, stream, steps)
+        warm, _ = time_calls(call, stream, steps)
     res = {
-        "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist, "seed": w.seed,
-        "sane": sane,
-        "steps": args.steps, "warmup": args.warmup, "warmup_calls": warm,
-        "wall_s": wall,
-        "ms_per_step": wall / args.steps * 1e3,
-        "tflops": flops * args.steps / wall / 1e12,
-        "region_event_ms_per_call": region_ms / args.steps,
-        "event_ms_median": statistics.median(per),
-        "event_ms_mean": statistics.fmean(per),
-        "event_ms_min": min(per),
-        "event_ms_p90": float(np.percentile(per, 90)),
-        "tflops_median": flops / (statistics.median(per) * 1e-3) / 1e12,
-        "plan": sg.plan(w.M, w.N, w.K, args.config, args.sched,
+        "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist, "seed": w.seed, "sane": sane,
+        "steps": steps, "warmup_calls": warm_calls,
+        "cold": dict(stats(cold, flops), wall_s=cold_wall),
+        "warm": dict(stats(warm, flops), region_ms_per_call=region_ms / steps,
+                     region_tflops=flops * steps / region_wall / 1e12),
+        "plan": sg.plan(w.M, w.N, w.K, config, sched,
                         num_cus=torch.cuda.get_device_properties(dev).multi_processor_count),
     }
-    if cold:
-        flush_buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-        with torch.cuda.stream(stream):
-            per_c, _, _ = time_calls(call, stream, max(20, args.steps // 2), 3,
-                                  flush=lambda: flush_buf.fill_(1.0), min_warm_s=args.warm_seconds)
-        res["cold_event_ms_median"] = statistics.median(per_c)
-        res["cold_tflops_median"] = flops / (statistics.median(per_c) * 1e-3) / 1e12
-        del flush_buf
     if with_torch:
         torch.backends.cuda.matmul.allow_tf32 = False
         out = torch.empty_like(Cd)
+        fn = lambda: torch.matmul(Ad, Bd, out=out)  # noqa: E731
         with torch.cuda.stream(stream):
-            per_t, _, _ = time_calls(lambda: torch.matmul(Ad, Bd, out=out), stream, args.steps, args.warmup,
-                                  min_warm_s=args.warm_seconds)
-        res["torch_matmul_event_ms_median"] = statistics.median(per_t)
-        res["torch_matmul_tflops_median"] = flops / (statistics.median(per_t) * 1e-3) / 1e12
+            warm_up(fn, warmup, warm_seconds)
+            per_t, _ = time_calls(fn, stream, steps, flush=flush)
+        res["torch_matmul_cold"] = stats(per_t, flops)
     del Ad, Bd, Cd
     torch.cuda.empty_cache()
     return res
@@ -270,6 +265,17 @@ def cpu_baseline(w, budget_s):
             "sample": f"{what}, FP64 triple loop (also forms sum|a*b|), {spent:.1f} s on {threads} threads"}
 
 
+def size_entry(sg, r):
+    c, wm = r["cold"], r["warm"]
+    return {"kernel": sg.CFG_NAMES[r["plan"]["config"]], "sched": sg.SCHED_NAMES[r["plan"]["sched"]],
+            "cold_median_tflops": round(c["tflops_median"], 3),
+            "cold_frac": round(c["tflops_median"] / PEAK_FP32_TFLOPS, 4),
+            "cold_median_us": round(c["median_ms"] * 1e3, 2),
+            "warm_median_tflops": round(wm["tflops_median"], 3),
+            "warm_frac": round(wm["tflops_median"] / PEAK_FP32_TFLOPS, 4),
+            "warm_median_us": round(wm["median_ms"] * 1e3, 2), "sane": r["sane"]}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -289,56 +295,56 @@ def main():
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         with torch.cuda.stream(stream):
-            per, wall, _ = time_calls(lambda: dst.copy_(src), stream, args.steps, args.warmup)
+            warm_up(lambda: dst.copy_(src), args.warmup, 0.0)
+            per, _ = time_calls(lambda: dst.copy_(src), stream, args.steps)
         t = statistics.median(per) * 1e-3
         print(json.dumps({"metric": "device copy GB/s (read + write)", "value": round(2 * n * 4 / t / 1e9, 1),
                           "unit": "GB/s", "bytes_read": n * 4, "bytes_written": n * 4,
                           "median_ms": round(t * 1e3, 4), "steps": args.steps}), flush=True)
         return
 
+    flush_buf = torch.empty(FLUSH_MIB * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    flush = lambda: flush_buf.fill_(1.0)  # noqa: E731
+
     if args.shape:
         M, N, K = (int(x) for x in args.shape.lower().split("x"))
         w = workloads.Workload(f"sgemm_{M}x{N}x{K}", M, N, K, args.dist, args.seed)
     else:
         w = workloads.WORKLOADS[args.workload]
-    head = bench_workload(sg, w, args, dev, stream, cold=not args.no_cold, with_torch=args.torch)
+    head = bench_workload(sg, w, dev, stream, flush, args.steps, args.warmup, args.warm_seconds,
+                          args.config, args.sched, with_torch=args.torch)
     log(json.dumps(head))
     detail = {"headline": head, "device": props.name, "cus": props.multi_processor_count}
-    if args.all:
-        rest = []
+
+    sizes = {}
+    if not args.no_sizes and not args.shape:
         for name, ww in workloads.WORKLOADS.items():
             if name == w.name:
                 continue
-            r = bench_workload(sg, ww, args, dev, stream, cold=args.cold, with_torch=args.torch)
+            r = bench_workload(sg, ww, dev, stream, flush, args.size_steps, args.warmup, args.warm_seconds,
+                               with_torch=args.torch)
             log(json.dumps(r))
-            rest.append(r)
-        detail["others"] = rest
-        if not args.no_cpu_baseline:
-            # The FP64 oracle on each workload (a bounded row sample, whole
-            # product where it fits the budget) beside the GPU's median.
-            for r in [head] + rest:
-                ww = w if r is head else workloads.WORKLOADS[r["workload"]]
-                cpu_r = cpu_baseline(ww, min(args.cpu_seconds, 6.0))
-                r["cpu_oracle"] = cpu_r
-                r["gpu_over_oracle"] = r["tflops_median"] / cpu_r["value"]
-                log(f"{ww.name}: oracle {cpu_r['value'] * 1e3:.1f} GFLOP/s ({cpu_r['sample']}); "
-                    f"GPU median {r['tflops_median']:.1f} TFLOP/s = {r['gpu_over_oracle']:.0f}x")
+            detail.setdefault("others", []).append(r)
+            sizes[name] = size_entry(sg, r)
 
-    achieved = w.flops / (head["region_event_ms_per_call"] * 1e-3) / 1e12
-    traffic = None
-    if (TRAFFIC["kernel"] == sg.CFG_NAMES[head["plan"]["config"]] and TRAFFIC["workload"] == w.name
-            and TRAFFIC["source_digest"] == kernel_source_digest()):
-        traffic = TRAFFIC["bytes"]
-    # The vector-ALU kernel is bounded by the FP32 vector rate (157.3 TFLOP/s
-    # too), the skinny and row-dot kernels (at most 16 rows / 8 columns) by
-    # HBM: their algorithmic bytes are A, B and C once, 4 (MK + KN + MN);
-    # the others by the FP32 matrix-core rate.
+    cold = head["cold"]
     cfg = head["plan"]["config"]
+    # The kernel's mean launch duration over the flushed timed region.
+    mean_s = cold["mean_ms"] * 1e-3
     if cfg in (sg.CFG_SKINNY_16x256, sg.CFG_ROWDOT_N8):
-        gbps = 4 * (w.M * w.K + w.K * w.N + w.M * w.N) / (head["region_event_ms_per_call"] * 1e-3) / 1e9
+        # At most 16 rows / 8 columns: bounded by HBM; algorithmic bytes are
+        # A, B and C once, 4 (MK + KN + MN).
+        gbps = 4 * (w.M * w.K + w.K * w.N + w.M * w.N) / mean_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "traffic_unit": "bytes per launch"}
     else:
+        traffic = None
+        if (TRAFFIC["kernel"] == sg.CFG_NAMES[cfg] and TRAFFIC["workload"] == w.name
+                and TRAFFIC["source_digest"] == kernel_source_digest()):
+            traffic = TRAFFIC["bytes"]
+        achieved = w.flops / mean_s / 1e12
+        # The vector-ALU kernel is bounded by the FP32 vector rate (157.3
+        # TFLOP/s too), the others by the FP32 matrix-core rate.
         bound = "alu" if cfg == sg.CFG_VALU_128x128x8 else "mfma"
         roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic,
@@ -347,32 +353,40 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
         log(json.dumps(cpu))
-    cfg_name = sg.CFG_NAMES[head["plan"]["config"]]
+    warm = head["warm"]
     line = {
         "metric": "FP32 SGEMM TFLOPS (2MNK/s)",
-        "value": round(head["tflops"], 3),
+        "value": round(cold["tflops_median"], 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "warmup_calls": head["warmup_calls"],
-        "ms_per_step": round(head["ms_per_step"], 5),
+        "ms_per_step": round(cold["wall_s"] / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(head["tflops"] / PAGES_4096_TFLOPS, 3) if w.name == "sgemm_4096" else None,
+        "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist, "seed": w.seed,
-                   "kernel": cfg_name, "sched": sg.SCHED_NAMES[head["plan"]["sched"]],
+                   "kernel": sg.CFG_NAMES[cfg], "sched": sg.SCHED_NAMES[head["plan"]["sched"]],
                    "grid": head["plan"]["grid"], "parallelism": "single-gpu",
+                   "protocol": f"median of {args.steps} single-call HIP-event times, {FLUSH_MIB} MiB "
+                               "written before each call outside the events (caches flushed)",
                    **({"repacked": True} if head["plan"]["repacked"] else {})},
-        "frac_of_fp32_peak": round(head["tflops"] / PEAK_FP32_TFLOPS, 4),
-        "median_event_tflops": round(head["tflops_median"], 3),
-        "cold_median_event_tflops": (round(head["cold_tflops_median"], 3) if "cold_tflops_median" in head
-                                     else None),
+        "frac_of_fp32_peak": round(cold["tflops_median"] / PEAK_FP32_TFLOPS, 4),
+        "median_us": round(cold["median_ms"] * 1e3, 2),
+        "min_us": round(cold["min_ms"] * 1e3, 2),
+        "p90_us": round(cold["p90_ms"] * 1e3, 2),
+        "warm": {"median_tflops": round(warm["tflops_median"], 3),
+                 "frac": round(warm["tflops_median"] / PEAK_FP32_TFLOPS, 4),
+                 "median_us": round(warm["median_ms"] * 1e3, 2),
+                 "region_tflops": round(warm["region_tflops"], 3)},
+        "sizes": sizes,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "sane": head["sane"],
+        "vs_cpu_baseline": round(cold["tflops_median"] / cpu["value"], 1) if cpu else None,
+        "sane": head["sane"] and all(s["sane"] for s in sizes.values()),
     }
     if args.detail:
         detail["line"] = line
