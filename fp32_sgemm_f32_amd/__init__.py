@@ -22,6 +22,9 @@ ERR_ALIAS = 5
 ERR_HIP = 6
 ERR_POINTER = 7
 ERR_CONFIG = 8
+ERR_SCRATCH = 9
+# Scratch memory of gemm_noalloc per device (SGEMM_F32_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Kernel configurations (SGEMM_CFG_*).
 CFG_AUTO = 0
@@ -140,6 +143,8 @@ def library():
     lib.sgemm_f32_gemm.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, vp]
     lib.sgemm_f32_gemm_ex.restype = i
     lib.sgemm_f32_gemm_ex.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, vp, i, i]
+    lib.sgemm_f32_gemm_noalloc.restype = i
+    lib.sgemm_f32_gemm_noalloc.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, vp]
     lib.sgemm_f32_granule.restype = None
     lib.sgemm_f32_granule.argtypes = [ctypes.POINTER(i)] * 3
     lib.sgemm_f32_status_string.restype = ctypes.c_char_p
@@ -212,6 +217,14 @@ def gemm_raw(trans_a, trans_b, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_p
                                   stream)
     return lib.sgemm_f32_gemm_ex(trans_a, trans_b, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc,
                                  stream, config, sched)
+
+
+def gemm_noalloc_raw(trans_a, trans_b, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc, stream=0) -> int:
+    """sgemm_f32_gemm_noalloc with integer device addresses (no device memory
+    allocated: scratch from the library's fixed per-device array); returns
+    the status."""
+    return library().sgemm_f32_gemm_noalloc(trans_a, trans_b, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta,
+                                            C_ptr, ldc, stream)
 
 
 def gemm(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False, config=CFG_AUTO,

@@ -44,6 +44,16 @@ std::recursive_mutex g_mu;
 std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
 
+// Scratch memory of the no-allocation entry point (sgemm_f32_gemm_noalloc):
+// the Stream-K partial tiles and the repacked copies of its calls, in a
+// file-scope device array that every device running the library holds from
+// module load to process exit.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the symbol): each device's
+// copy is looked up once with hipGetSymbolAddress and kept in g_scratch.
+constexpr int64_t kScratchBytes = SGEMM_F32_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::map<int, char *> g_scratch;   // device -> address of its copy of `scratch`
+
 hipError_t launch_cfg(int cfg, const KernelArgs &a, hipStream_t s, int trans_c = 0) {
     switch (kCfgs[cfg].kind) {
     case kKindMfma: return launch_mfma(cfg, a, s);
@@ -91,6 +101,22 @@ int device_info(int dev, DeviceInfo *out) {
         d.ready = true;
     }
     *out = d;
+    return SGEMM_OK;
+}
+
+// Device address of the scratch array on device dev (current), looked up on
+// the first call for that device.
+int scratch_of(int dev, char **out) {
+    std::lock_guard<std::recursive_mutex> lock(g_mu);
+    auto it = g_scratch.find(dev);
+    if (it == g_scratch.end()) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (!ptr) return hip_fail(hipErrorInvalidSymbol);
+        it = g_scratch.emplace(dev, (char *)ptr).first;
+    }
+    *out = it->second;
     return SGEMM_OK;
 }
 
@@ -145,6 +171,9 @@ struct Call {
                                    // beyond them (run_packed); 0: M and N
     int tc = 0;                    // C stored N x M: the transposed product of a thin
                                    // call (transposed_route)
+    char *scratch = nullptr;       // set: take the Stream-K partials and the repacked
+    int64_t scratch_bytes = 0;     // copies from here (the device address of the
+                                   // no-allocation scratch array), allocate nothing
 
     // Rows and columns of C, and of A and B as stored.
     int c_rows() const { return tc ? N : cm ? cm : M; }
@@ -318,8 +347,14 @@ int run_packed(const Call &c, int dev) {
     const int64_t b_bytes = pb ? round256((int64_t)br * bc * 4) : 0;
     float *buf = nullptr;
     int st = SGEMM_OK;
-    if (a_bytes + b_bytes > 0 && (st = pack_space_for(dev, c.stream, a_bytes + b_bytes, &buf)) != SGEMM_OK)
+    if (c.scratch) {
+        // No allocation: the copies at the start of the scratch array.
+        if (a_bytes + b_bytes > c.scratch_bytes) return SGEMM_ERR_SCRATCH;
+        buf = (float *)c.scratch;
+    } else if (a_bytes + b_bytes > 0 &&
+               (st = pack_space_for(dev, c.stream, a_bytes + b_bytes, &buf)) != SGEMM_OK) {
         return st;
+    }
     float *Ap = buf, *Bp = (float *)((char *)buf + a_bytes);
     PackJob jobs[2];
     int njobs = 0;
@@ -334,6 +369,10 @@ int run_packed(const Call &c, int dev) {
     if (pb) { q.B = Bp; q.ldb = bc; }
     if (Mp != c.M || Np != c.N || !vector_c(c)) { q.cm = c.M; q.cn = c.N; }
     q.repacked = 1;
+    if (c.scratch) {   // the rest of the array for the product's partial tiles
+        q.scratch = c.scratch + a_bytes + b_bytes;
+        q.scratch_bytes = c.scratch_bytes - (a_bytes + b_bytes);
+    }
     return run(q);
 }
 
@@ -348,7 +387,9 @@ int run(const Call &c) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e);
     if ((st = check_device_range(c.C, extent_bytes(c.c_rows(), c.c_cols(), c.ldc), dev)) != SGEMM_OK) return st;
-    if (c.reads_ab()) {
+    // Repacked operands are the library's own copies, the caller's were
+    // checked before they were copied.
+    if (c.reads_ab() && !c.repacked) {
         if ((st = check_device_range(c.A, extent_bytes(c.a_rows(), c.a_cols(), c.lda), dev)) != SGEMM_OK) return st;
         if ((st = check_device_range(c.B, extent_bytes(c.b_rows(), c.b_cols(), c.ldb), dev)) != SGEMM_OK) return st;
     }
@@ -383,6 +424,14 @@ int run(const Call &c) {
         req.config = p.edge || c.ta || c.tb ? SGEMM_CFG_GENERIC_64x64x16 : staged_equivalent(p.config);
         if ((st = make_plan(req, &p)) != SGEMM_OK) return st;
     }
+    if (c.scratch && p.workspace_bytes > c.scratch_bytes) {
+        // No allocation, and the split tiles' partials do not fit the
+        // scratch array: the same configuration with whole tiles only.
+        req.config = p.config;
+        req.sched = SGEMM_SCHED_DP;
+        if (make_plan(req, &p) != SGEMM_OK || p.workspace_bytes > c.scratch_bytes) return SGEMM_ERR_SCRATCH;
+        if (c_own) p.edge = 1;
+    }
 
     if (!c.reads_ab()) {
         // No product: C = beta * C (zeros for the plain product, K == 0).
@@ -411,10 +460,17 @@ int run(const Call &c) {
         // Workspace acquisition and launch under the lock, so that a
         // concurrent call on the same stream cannot replace the buffers
         // between the two.
+        // (The no-allocation path shares one array per device: under the
+        // lock, two threads' calls on one stream cannot interleave their
+        // GEMM and sum kernels either.)
         std::lock_guard<std::recursive_mutex> lock(g_mu);
-        Workspace w;
-        if ((st = workspace_for(dev, c.stream, p, &w)) != SGEMM_OK) return st;
-        a.partials = w.partials;
+        if (c.scratch) {
+            a.partials = (float *)c.scratch;
+        } else {
+            Workspace w;
+            if ((st = workspace_for(dev, c.stream, p, &w)) != SGEMM_OK) return st;
+            a.partials = w.partials;
+        }
         e = launch_cfg(p.config, a, c.stream, c.tc);   // the skinny and row-dot kernels add their own splits
         if (e == hipSuccess && !any_layout(p.config)) e = launch_sk_fixup(a, p.bm, p.bn, c.stream);
     } else {
@@ -462,6 +518,22 @@ SGEMM_API int sgemm_f32_gemm_ex(int trans_a, int trans_b, int M, int N, int K, f
                                   config, sched));
 }
 
+SGEMM_API int sgemm_f32_gemm_noalloc(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+                                     int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                                     hipStream_t stream) {
+    if (trans_a < 0 || trans_a > 1 || trans_b < 0 || trans_b > 1) return SGEMM_ERR_CONFIG;
+    sgemm::Call c = sgemm::blas(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                                SGEMM_CFG_AUTO, SGEMM_SCHED_AUTO);
+    int st = sgemm::check_args(c);
+    if (st != SGEMM_OK || M == 0 || N == 0) return st;
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return sgemm::hip_fail(e);
+    if ((st = sgemm::scratch_of(dev, &c.scratch)) != SGEMM_OK) return st;
+    c.scratch_bytes = sgemm::kScratchBytes;
+    return sgemm::run(c);
+}
+
 SGEMM_API void sgemm_f32_granule(int *gm, int *gn, int *gk) {
     if (gm) *gm = sgemm::kGranM;
     if (gn) *gn = sgemm::kGranN;
@@ -479,6 +551,7 @@ SGEMM_API const char *sgemm_f32_status_string(int status) {
     case SGEMM_ERR_HIP: return "HIP runtime error";
     case SGEMM_ERR_POINTER: return "not device memory of the current device, or extent past its allocation";
     case SGEMM_ERR_CONFIG: return "unknown or inapplicable kernel configuration or schedule";
+    case SGEMM_ERR_SCRATCH: return "the no-allocation call needs more scratch memory than its fixed maximum";
     default: return "unknown status";
     }
 }

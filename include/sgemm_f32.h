@@ -78,7 +78,8 @@
  *   concurrently, and a later call on that stream that needs a larger
  *   workspace (it replaces the buffers) or sgemm_f32_release() invalidates
  *   those graphs — size the workspace with the largest shape before
- *   capturing.
+ *   capturing.  sgemm_f32_gemm_noalloc (below) needs no eager call: it
+ *   never allocates.
  *
  * Environment (read on every call; for tuning and measurement, not needed
  * for correct results):
@@ -113,6 +114,8 @@ extern "C" {
                                   the matrix extent runs past the end of its allocation */
 #define SGEMM_ERR_CONFIG    8  /* unknown kernel configuration/schedule, or a forced one that
                                   cannot run this shape or layout */
+#define SGEMM_ERR_SCRATCH   9  /* sgemm_f32_gemm_noalloc: the repacked copies the call needs do
+                                  not fit SGEMM_F32_NOALLOC_SCRATCH_BYTES */
 
 /* Kernel configurations (sgemm_f32_ex / sgemm_f32_plan).  "MFMA" configs
  * run the product on the FP32 matrix cores (v_mfma_f32_32x32x2_f32: full
@@ -235,6 +238,36 @@ int sgemm_f32_gemm_ex(int trans_a, int trans_b, int M, int N, int K, float alpha
                       const float *B, int ldb, float beta,
                       float *C, int ldc,
                       hipStream_t stream, int config, int sched);
+
+/*
+ * sgemm_f32_gemm that allocates no memory, for callers that cannot call
+ * hipMalloc: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results and errors as
+ * sgemm_f32_gemm (automatic configuration and schedule), except where
+ * sgemm_f32_gemm would take device memory:
+ *   - Stream-K partial tiles and repacked copies of A and B (see "Fast and
+ *     general layouts") go to a fixed scratch array of
+ *     SGEMM_F32_NOALLOC_SCRATCH_BYTES in the library's code object, one per
+ *     device, held from the library's load on that device until the process
+ *     ends (its address is looked up on the first call on each device);
+ *   - a split schedule whose partial tiles do not fit (or do not fit beside
+ *     the repacked copies) runs data-parallel instead: whole tiles, no
+ *     partials (results within the same tolerance; exact on integer inputs);
+ *   - repacked copies that do not fit the array are refused with
+ *     SGEMM_ERR_SCRATCH before anything is enqueued.
+ * Nothing needs clearing between calls: every partial tile and every padded
+ * copy is written in full before it is read.  Every call on a device shares
+ * that device's array and leaves its contents behind: calls on one stream
+ * are ordered by the stream (also from several host threads), but calls
+ * whose execution overlaps on one GPU (on different streams, or graphs
+ * replayed concurrently) race on the array and give wrong results.
+ */
+#define SGEMM_F32_NOALLOC_SCRATCH_BYTES (64LL << 20)   /* 64 MiB per device */
+int sgemm_f32_gemm_noalloc(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                           const float *A, int lda,
+                           const float *B, int ldb, float beta,
+                           float *C, int ldc,
+                           hipStream_t stream);
 
 /* Shape multiples accepted by sgemm_f32: 1, 1, 1 (any shape; any pointer
  * may be NULL). */

@@ -63,8 +63,8 @@ def test_granule():
 
 
 def test_status_strings():
-    texts = [sg.status_string(s) for s in range(0, 9)]
-    assert all(texts) and len(set(texts)) == 9
+    texts = [sg.status_string(s) for s in range(0, 10)]
+    assert all(texts) and len(set(texts)) == 10
     assert sg.status_string(12345) == "unknown status"
 
 

@@ -1,0 +1,141 @@
+"""The no-allocation entry point, sgemm_f32_gemm_noalloc, through the C-ABI:
+its results against sgemm_f32_gemm's on the same inputs.
+
+It runs the same kernels as sgemm_f32_gemm with the Stream-K partial tiles
+and the repacked copies taken from the library's fixed per-device scratch
+array.  Where that holds them the plan is the same, so the results are the
+same bit for bit; a split schedule too large for it runs data-parallel
+(compared on integer inputs: exact either way); repacked copies too large
+for it are refused with SGEMM_ERR_SCRATCH and C is left untouched.  Each
+case makes two calls in a row, the second with a smaller input, so that the
+second reuses the array the first left behind.
+"""
+import numpy as np
+import pytest
+
+import fp32_sgemm_f32_amd as sg
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    sg.library()
+    return torch.device("cuda:0")
+
+
+def stored(X, trans):
+    return np.ascontiguousarray(X.T) if trans else X
+
+
+def run_both(dev, ta, tb, M, N, K, alpha, beta, dist, seed, c_pad=0):
+    """C from sgemm_f32_gemm and from sgemm_f32_gemm_noalloc on the same
+    operands (C0 the same start for both), plus the host copies."""
+    import torch
+    A, B = workloads.generate(M, N, K, dist, seed)
+    As, Bs = stored(A, ta), stored(B, tb)
+    C0 = workloads.generate(M, 1, N, dist, seed + 1)[0]
+    Ad = torch.from_numpy(np.ascontiguousarray(As)).to(dev)
+    Bd = torch.from_numpy(np.ascontiguousarray(Bs)).to(dev)
+    ldc = N + c_pad
+    outs = []
+    for fn in (sg.gemm_raw, sg.gemm_noalloc_raw):
+        Cbuf = torch.full((M, ldc), float("nan"), dtype=torch.float32, device=dev)
+        Cbuf[:, :N] = torch.from_numpy(C0).to(dev)
+        s = torch.cuda.current_stream(dev)
+        st = fn(ta, tb, M, N, K, alpha, Ad.data_ptr(), As.shape[1], Bd.data_ptr(), Bs.shape[1], beta,
+                Cbuf.data_ptr(), ldc, s.cuda_stream)
+        assert st == sg.OK, (fn.__name__, st, sg.status_string(st))
+        outs.append(Cbuf)
+    torch.cuda.synchronize()
+    ref, noalloc = (c.cpu().numpy() for c in outs)
+    assert np.all(np.isnan(noalloc[:, N:])), "ldc padding was written"
+    return As, Bs, C0, ref[:, :N], noalloc[:, :N]
+
+
+# (name, [first call, second smaller call]); each call
+# (ta, tb, M, N, K, alpha, beta, dist).
+CASES = {
+    # Stream-K partials in the scratch array (64x64 tiles, split remainder).
+    "streamk": [(0, 0, 1000, 1028, 2048, 1.0, 0.0, "uniform"), (520, 516, 1500, 1.0, 0.0, "uniform")],
+    # Repacked copies (odd N / odd K) and the split partials behind them.
+    "repacked": [(0, 0, 1031, 1027, 1409, 1.0, 0.0, "uniform"), (0, 1, 515, 771, 1021, -0.5, 2.0, "normal")],
+    # Whole tiles: no scratch at all; storage orders and beta.
+    "whole_tiles": [(1, 1, 2048, 2048, 1024, 1.5, -1.0, "normal"), (1, 0, 1024, 1024, 512, 1.0, 0.0, "uniform")],
+    # Thin products on the skinny and row-dot kernels with their K splits.
+    "thin": [(0, 0, 8, 8192, 8192, 1.0, 0.0, "uniform"), (4096, 1, 4096, 1.0, 0.0, "uniform")],
+}
+
+
+def unpack(call):
+    if len(call) == 6:   # (M, N, K, alpha, beta, dist) after a first call: same storage order
+        return (0, 0) + tuple(call)
+    return call
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_noalloc_matches_gemm(dev, case):
+    for i, call in enumerate(CASES[case]):
+        ta, tb, M, N, K, alpha, beta, dist = unpack(call)
+        p = sg.plan(M, N, K, trans_a=ta, trans_b=tb)
+        log(f"case noalloc {case} call {i}: ta={ta} tb={tb} shape=({M},{N},{K}) alpha={alpha} beta={beta} "
+            f"config={sg.CFG_NAMES[p['config']]} sched={sg.SCHED_NAMES[p['sched']]} "
+            f"workspace={p['workspace_bytes']} repacked={p['repacked']}")
+        # C's rows padded by 4 floats (kept on the 16-byte grid), or by 3 in
+        # one call (C stored a float at a time, through the repacking path
+        # with nothing to copy).
+        c_pad = 3 if (case, i) == ("whole_tiles", 0) else 4
+        As, Bs, C0, ref, noalloc = run_both(dev, ta, tb, M, N, K, alpha, beta, dist, 300 + 10 * i, c_pad=c_pad)
+        C_ref, S = oracle.gemm_blas(As, Bs, C0, alpha, beta, ta, tb)
+        ok, worst = oracle.within_bound(noalloc, C_ref, S, TOL)
+        log(f"  max|err|/S = {worst:.3e}")
+        assert ok
+        # Same plan, same kernels: the same bits as the allocating call.
+        assert np.array_equal(ref.view(np.uint32), noalloc.view(np.uint32))
+
+
+def test_noalloc_split_too_large_runs_whole_tiles(dev):
+    """256x256 tiles with a split remainder need 128 MiB of partial tiles,
+    beyond the 64 MiB array: the no-allocation call runs whole tiles
+    (integer inputs, so both schedules give the exact product), then a
+    smaller split call that fits reuses the array."""
+    M, N, K = 4096, 4100, 1024
+    p = sg.plan(M, N, K)
+    assert p["sched"] == sg.SCHED_STREAMK and p["workspace_bytes"] > sg.NOALLOC_SCRATCH_BYTES
+    for i, (m, n, k) in enumerate([(M, N, K), (1000, 1028, 1024)]):
+        log(f"case noalloc split beyond the array, call {i}: shape=({m},{n},{k})")
+        As, Bs, _, ref, noalloc = run_both(dev, 0, 0, m, n, k, 1.0, 0.0, "int4", 400 + i)
+        exact, _ = oracle.gemm(As, Bs)
+        assert np.array_equal(noalloc.astype(np.float64), exact)
+        assert np.array_equal(ref.astype(np.float64), exact)
+
+
+def test_noalloc_refuses_copies_beyond_the_array(dev):
+    """A repacked product whose copies exceed the array: SGEMM_ERR_SCRATCH
+    before anything is enqueued (C untouched); a smaller repacked call after
+    it runs."""
+    import torch
+    M, N, K = 4099, 4097, 4096   # B's copy alone is 64 MiB + a row
+    A, B = workloads.generate(M, N, K, "int4", 500)
+    Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    C = torch.full((M, N), 7.0, dtype=torch.float32, device=dev)
+    log(f"case noalloc refuses copies: shape=({M},{N},{K})")
+    st = sg.gemm_noalloc_raw(0, 0, M, N, K, 1.0, Ad.data_ptr(), K, Bd.data_ptr(), N, 0.0, C.data_ptr(), N,
+                             torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    assert st == sg.ERR_SCRATCH
+    assert bool((C == 7.0).all().item())
+    del Ad, Bd, C
+    As, Bs, _, ref, noalloc = run_both(dev, 0, 0, 515, 771, 1021, 1.0, 0.0, "int4", 501)
+    exact, _ = oracle.gemm(As, Bs)
+    assert np.array_equal(noalloc.astype(np.float64), exact)
