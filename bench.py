@@ -16,7 +16,9 @@ The line also carries:
     duration in the flushed timed region (HIP events on the launch stream),
     against the MI355X FP32 matrix peak (157.3 TFLOP/s);
   * "cpu_baseline": the FP64 CPU oracle timed on a bounded sample of the
-    same product on this host's cores.
+    same product on this host's cores;
+  * "fixed_shape": the same product on the kernel compiled for its exact
+    shape (SGEMM_SCHED_FIXED), same protocol, beside the runtime kernel.
 Details (the plan, a torch.matmul context figure with --torch) go to stderr
 and to --detail FILE.
 
@@ -177,7 +179,7 @@ def stats(per_ms, flops):
 
 
 def bench_workload(sg, w, dev, stream, flush, steps, warmup, warm_seconds, config=0, sched=0,
-                   with_torch=False):
+                   with_torch=False, alt_scheds=()):
     """One workload: a correctness sanity check, the warm-up, then the
     flushed timed region (the headline protocol), then the warm ones."""
     import torch
@@ -187,11 +189,15 @@ def bench_workload(sg, w, dev, stream, flush, steps, warmup, warm_seconds, confi
     Cd = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
     del A, B
 
-    def call():
-        st = sg.sgemm_raw(w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), w.N, Cd.data_ptr(), w.N,
-                          stream.cuda_stream, config, sched)
-        if st != sg.OK:
-            raise sg.SgemmError(st)
+    def call_with(cfg, sch):
+        def call():
+            st = sg.sgemm_raw(w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), w.N, Cd.data_ptr(), w.N,
+                              stream.cuda_stream, cfg, sch)
+            if st != sg.OK:
+                raise sg.SgemmError(st)
+        return call
+
+    call = call_with(config, sched)
 
     # Sanity check before timing (the parity proof is the test suite): a
     # sample of rows against an FP64 product on the device.
@@ -225,6 +231,16 @@ def bench_workload(sg, w, dev, stream, flush, steps, warmup, warm_seconds, confi
         "plan": sg.plan(w.M, w.N, w.K, config, sched,
                         num_cus=torch.cuda.get_device_properties(dev).multi_processor_count),
     }
+    # Other schedules of the same call (the compile-time-shape kernel), under
+    # the same flushed protocol, right after.
+    for sch in alt_scheds:
+        fn = call_with(config, sch)
+        with torch.cuda.stream(stream):
+            warm_up(fn, warmup, warm_seconds)
+            warm_up(lambda: (flush(), fn()), FLUSHED_WARMUP_CALLS, FLUSHED_WARMUP_S)
+            per_c, _ = time_calls(fn, stream, steps, flush=flush)
+            per_w, _ = time_calls(fn, stream, steps)
+        res.setdefault("alt", {})[sg.SCHED_NAMES[sch]] = {"cold": stats(per_c, flops), "warm": stats(per_w, flops)}
     if with_torch:
         torch.backends.cuda.matmul.allow_tf32 = False
         out = torch.empty_like(Cd)
@@ -311,8 +327,14 @@ def main():
         w = workloads.Workload(f"sgemm_{M}x{N}x{K}", M, N, K, args.dist, args.seed)
     else:
         w = workloads.WORKLOADS[args.workload]
+    # The kernel compiled for this exact product, if there is one (reported
+    # beside the runtime kernel that `value` measures).
+    try:
+        fixed = [sg.SCHED_FIXED] if sg.plan(w.M, w.N, w.K, args.config, sg.SCHED_FIXED)["fixed_shape"] else []
+    except sg.SgemmError:
+        fixed = []
     head = bench_workload(sg, w, dev, stream, flush, args.steps, args.warmup, args.warm_seconds,
-                          args.config, args.sched, with_torch=args.torch)
+                          args.config, args.sched, with_torch=args.torch, alt_scheds=fixed)
     log(json.dumps(head))
     detail = {"headline": head, "device": props.name, "cus": props.multi_processor_count}
 
@@ -383,6 +405,10 @@ def main():
                  "median_us": round(warm["median_ms"] * 1e3, 2),
                  "region_tflops": round(warm["region_tflops"], 3)},
         "sizes": sizes,
+        "fixed_shape": ({"cold_median_tflops": round(head["alt"]["fixed"]["cold"]["tflops_median"], 3),
+                         "warm_median_tflops": round(head["alt"]["fixed"]["warm"]["tflops_median"], 3),
+                         "cold_vs_value": round(head["alt"]["fixed"]["cold"]["tflops_median"] / cold["tflops_median"], 4)}
+                        if "alt" in head else None),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "vs_cpu_baseline": round(cold["tflops_median"] / cpu["value"], 1) if cpu else None,

@@ -99,7 +99,8 @@ CFG_TILES = {
 SCHED_AUTO = 0
 SCHED_DP = 1
 SCHED_STREAMK = 2
-SCHED_NAMES = {SCHED_AUTO: "auto", SCHED_DP: "dp", SCHED_STREAMK: "streamk"}
+SCHED_FIXED = 3
+SCHED_NAMES = {SCHED_AUTO: "auto", SCHED_DP: "dp", SCHED_STREAMK: "streamk", SCHED_FIXED: "fixed"}
 
 
 class SgemmError(RuntimeError):
@@ -117,7 +118,7 @@ class _Plan(ctypes.Structure):
         "config", "sched", "tile_m", "tile_n", "tile_k", "threads", "tiles_m", "tiles_n",
         "iters_per_tile", "dp_tiles", "sk_tiles", "grid", "sk_grid", "xcd_remap", "group_m")] + [
         ("sk_iters", ctypes.c_longlong), ("workspace_bytes", ctypes.c_longlong), ("repacked", ctypes.c_int),
-        ("transposed", ctypes.c_int)]
+        ("transposed", ctypes.c_int), ("fixed_shape", ctypes.c_int)]
 
 
 _lib = None

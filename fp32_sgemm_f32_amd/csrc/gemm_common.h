@@ -51,13 +51,53 @@ __device__ __forceinline__ V epilogue(const KernelArgs &a, V v, const float *p) 
     return r;
 }
 
+// The launch geometry as a kernel reads it.  RuntimeShape: from the
+// argument block.  FixedShape: one dense row-major product C (M x N) =
+// A (M x K) B (K x N), known when the kernel is compiled ("Beyond Kernel 7:
+// Closing the Gap to cuBLAS on an H100 FP32 GEMM", section "Kernel 13", the
+// size-specialised build): leading dimensions K, N, N, whole BM x BN tiles
+// of BK-deep chunks, one workgroup per tile (data-parallel), the XCD remap,
+// tile groups of GM rows; every field below is then a constant.
+struct RuntimeShape {
+    static constexpr bool kFixed = false;
+    __device__ static int lda(const KernelArgs &a) { return a.lda; }
+    __device__ static int ldb(const KernelArgs &a) { return a.ldb; }
+    __device__ static int ldc(const KernelArgs &a) { return a.ldc; }
+    __device__ static int ipt(const KernelArgs &a) { return a.ipt; }
+    __device__ static int tiles_m(const KernelArgs &a) { return a.tiles_m; }
+    __device__ static int tiles_n(const KernelArgs &a) { return a.tiles_n; }
+    __device__ static int dp_tiles(const KernelArgs &a) { return a.dp_tiles; }
+    __device__ static int grid(const KernelArgs &a) { return a.grid; }
+    __device__ static int xcd_remap(const KernelArgs &a) { return a.xcd_remap; }
+    __device__ static int group_m(const KernelArgs &a) { return a.group_m; }
+};
+
+template <int M, int N, int K, int BM, int BN, int BK, int GM>
+struct FixedShape {
+    static constexpr bool kFixed = true;
+    static constexpr int TM = M / BM, TN = N / BN, TILES = TM * TN;
+    static_assert(M % BM == 0 && N % BN == 0 && K % BK == 0, "whole tiles");
+    static_assert(TILES % 8 == 0 && TM % GM == 0, "XCD remap and whole tile groups");
+    __device__ static constexpr int lda(const KernelArgs &) { return K; }
+    __device__ static constexpr int ldb(const KernelArgs &) { return N; }
+    __device__ static constexpr int ldc(const KernelArgs &) { return N; }
+    __device__ static constexpr int ipt(const KernelArgs &) { return K / BK; }
+    __device__ static constexpr int tiles_m(const KernelArgs &) { return TM; }
+    __device__ static constexpr int tiles_n(const KernelArgs &) { return TN; }
+    __device__ static constexpr int dp_tiles(const KernelArgs &) { return TILES; }
+    __device__ static constexpr int grid(const KernelArgs &) { return TILES; }
+    __device__ static constexpr int xcd_remap(const KernelArgs &) { return 1; }
+    __device__ static constexpr int group_m(const KernelArgs &) { return GM; }
+};
+
 // Workgroups are handed to the 8 XCDs round-robin by blockIdx.  With the
 // remap, XCD x runs logical ids [x*grid/8, (x+1)*grid/8): neighbouring tiles
 // (and the K-split pieces of one tile) land on one XCD and share its L2.
+template <class SH = RuntimeShape>
 __device__ __forceinline__ int logical_wg(const KernelArgs &a) {
     int w = (int)blockIdx.x;
-    if (a.xcd_remap) {
-        const int per = a.grid >> 3;
+    if (SH::xcd_remap(a)) {
+        const int per = SH::grid(a) >> 3;
         w = (w & 7) * per + (w >> 3);
     }
     return w;
@@ -65,12 +105,14 @@ __device__ __forceinline__ int logical_wg(const KernelArgs &a) {
 
 // Tile id -> (tile row, tile column): groups of group_m tile rows, walked
 // down each column of the group before moving right.
+template <class SH = RuntimeShape>
 __device__ __forceinline__ void tile_coords(const KernelArgs &a, int t, int &tm, int &tn) {
-    const int gsz = a.group_m * a.tiles_n;
+    const int group_m = SH::group_m(a);
+    const int gsz = group_m * SH::tiles_n(a);
     const int g = t / gsz;
-    const int first = g * a.group_m;
-    int rows = a.tiles_m - first;
-    if (rows > a.group_m) rows = a.group_m;
+    const int first = g * group_m;
+    int rows = SH::tiles_m(a) - first;
+    if (rows > group_m) rows = group_m;
     const int r = t - g * gsz;
     tm = first + r % rows;
     tn = r / rows;
@@ -116,16 +158,20 @@ __device__ __forceinline__ float *partial_ptr(const KernelArgs &a, int w, int sl
 // SPLIT = false is the whole-tile-only instance (sk_tiles == 0): it carries
 // none of the split bookkeeping, which keeps its register allocation to the
 // main loop's needs.
-template <class Core, bool SPLIT>
+//
+// SH supplies the launch geometry (RuntimeShape, or a FixedShape for a
+// kernel compiled for one product, which has no split part).
+template <class Core, bool SPLIT, class SH = RuntimeShape>
 __device__ __forceinline__ void run_gemm(const KernelArgs &a, float *lds) {
+    static_assert(!(SPLIT && SH::kFixed), "a compile-time shape runs whole tiles only");
     Core core;
-    const int w = logical_wg(a);
+    const int w = logical_wg<SH>(a);
 
-    for (int t = w; t < a.dp_tiles; t += a.grid) {
+    for (int t = w; t < SH::dp_tiles(a); t += SH::grid(a)) {
         int tm, tn;
-        tile_coords(a, t, tm, tn);
+        tile_coords<SH>(a, t, tm, tn);
         core.zero();
-        core.mainloop(a, lds, tm, tn, 0, a.ipt);
+        core.mainloop(a, lds, tm, tn, 0, SH::ipt(a));
         core.store_c(a, tm, tn);
     }
     if (!SPLIT || w >= a.sk_grid) return;

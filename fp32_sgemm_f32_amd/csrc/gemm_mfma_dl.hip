@@ -187,9 +187,12 @@ struct GroupOps<false, F> {
 // of each operand, and N, multiples of 4): loads through buffer resources
 // with rows / columns / k beyond the matrix masked to zeros, stores masked.
 // TA: A stored K x M (m-contiguous); TB: B stored N x K (k-contiguous).
+// SH: the launch geometry, from the arguments or fixed at compile time for
+// one product (gemm_common.h).
 template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int S_, int KSPLIT = 1, int LA_ = 1,
-          bool EDGE = false, bool TA = false, bool TB = false>
+          bool EDGE = false, bool TA = false, bool TB = false, class SH = RuntimeShape>
 struct MfmaDlCore {
+    using Shape = SH;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
     static constexpr int LA = LA_;                  // groups of operand reads ahead of the MFMAs
     static constexpr int NS = LA == 1 ? 2 : 4;      // operand register sets
@@ -228,6 +231,7 @@ struct MfmaDlCore {
     static_assert(S >= 3 && L * (S - 2) < 64, "ring depth (loads run S-2 chunks ahead) / vmcnt range");
     static_assert(LDS_FLOATS * 4 + 16 <= 160 * 1024, "LDS budget");
     static_assert(KSPLIT == 1 || TILE_FLOATS <= LDS_FLOATS, "room to add the K groups' sums");
+    static_assert(!SH::kFixed || (!EDGE && !TA && !TB), "a compile-time shape: whole tiles, A M x K, B K x N");
 
     floatx16 acc[FM][FN];
 
@@ -315,28 +319,29 @@ struct MfmaDlCore {
         g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         // EDGE: valid k values in the tile's last chunk (a k-contiguous
         // operand needs K a multiple of 4, so its quads are all in or out).
-        const int kt = EDGE ? a.K - (a.ipt - 1) * BK : BK;
+        const int kt = EDGE ? a.K - (SH::ipt(a) - 1) * BK : BK;
         const int m_lim = a.M - tm * BM, n_lim = a.N - tn * BN;
 #pragma unroll
         for (int u = 0; u < A_PW; ++u)
-            dma_lane<AKC, BM>(g.wave + NW * u, lane, a.lda, m_lim, kt, [](int r) { return r; }, g.va[u], g.va_t[u]);
+            dma_lane<AKC, BM>(g.wave + NW * u, lane, SH::lda(a), m_lim, kt, [](int r) { return r; }, g.va[u],
+                              g.va_t[u]);
 #pragma unroll
         for (int u = 0; u < B_PW; ++u)
-            dma_lane<BKC, BN>(g.wave + NW * u, lane, a.ldb, n_lim, kt, [](int r) { return b_kc_col(r); }, g.vb[u],
+            dma_lane<BKC, BN>(g.wave + NW * u, lane, SH::ldb(a), n_lim, kt, [](int r) { return b_kc_col(r); }, g.vb[u],
                               g.vb_t[u]);
         if constexpr (AKC) {
-            g.ga = (const char *)(a.A + (int64_t)tm * BM * a.lda + (int64_t)k0 * BK);
+            g.ga = (const char *)(a.A + (int64_t)tm * BM * SH::lda(a) + (int64_t)k0 * BK);
             g.a_step = (int64_t)BK * 4;
         } else {
-            g.ga = (const char *)(a.A + (int64_t)k0 * BK * a.lda + (int64_t)tm * BM);
-            g.a_step = (int64_t)BK * a.lda * 4;
+            g.ga = (const char *)(a.A + (int64_t)k0 * BK * SH::lda(a) + (int64_t)tm * BM);
+            g.a_step = (int64_t)BK * SH::lda(a) * 4;
         }
         if constexpr (BKC) {
-            g.gb = (const char *)(a.B + (int64_t)tn * BN * a.ldb + (int64_t)k0 * BK);
+            g.gb = (const char *)(a.B + (int64_t)tn * BN * SH::ldb(a) + (int64_t)k0 * BK);
             g.b_step = (int64_t)BK * 4;
         } else {
-            g.gb = (const char *)(a.B + (int64_t)k0 * BK * a.ldb + (int64_t)tn * BN);
-            g.b_step = (int64_t)BK * a.ldb * 4;
+            g.gb = (const char *)(a.B + (int64_t)k0 * BK * SH::ldb(a) + (int64_t)tn * BN);
+            g.b_step = (int64_t)BK * SH::ldb(a) * 4;
         }
         if constexpr (EDGE) {
             g.rsa = buffer_rsrc(g.ga);
@@ -568,10 +573,18 @@ struct MfmaDlCore {
     __device__ __forceinline__ void mainloop(const KernelArgs &a, float *lds, int tm, int tn, int k0, int k1) {
         Geo g;
         setup(g, a, lds, tm, tn, k0);
-        const int nch = k1 - k0;
+        int nch = k1 - k0;
+        if constexpr (SH::kFixed) {
+            // A compile-time shape makes the chunk count a constant; kept
+            // opaque, so that the compiler keeps the loop over the ring as
+            // written instead of unrolling or re-peeling it (which moved the
+            // operand registers of the in-flight LDS reads).
+            asm volatile("" : "+s"(nch));
+        }
         // EDGE: the range's last chunk is the tile's last, with k beyond K,
         // when it reaches the end of a K not a multiple of BK.
-        const int tail_ch = __builtin_amdgcn_readfirstlane(EDGE && k1 == a.ipt && a.K % BK != 0 ? nch - 1 : -1);
+        const int tail_ch =
+            __builtin_amdgcn_readfirstlane(EDGE && k1 == SH::ipt(a) && a.K % BK != 0 ? nch - 1 : -1);
 
         // A previous tile of this workgroup may still read the ring.
         wait_counts<0, 0>();
@@ -642,7 +655,8 @@ struct MfmaDlCore {
         const int lr = lane & 31, lh = lane >> 5;
         const int row0 = tm * BM + wm * WTM + (AKC ? 4 : 4 * FM) * lh, col0 = tn * BN + wn * WTN + FN * lr;
         if (EDGE && col0 >= a.cn) return;
-        float *c = a.C + (int64_t)row0 * a.ldc + col0;
+        const int ldc = SH::ldc(a);
+        float *c = a.C + (int64_t)row0 * ldc + col0;
         if (EDGE && a.c_scalar) {
             // C with a leading dimension or base off the vector grid, or
             // columns that end inside a lane's group: one float at a time.
@@ -653,7 +667,7 @@ struct MfmaDlCore {
                     const int rho = 8 * (r >> 2) + (r & 3);
                     const int dr = AKC ? i * 32 + rho : FM * rho + i;
                     if (row0 + dr >= a.cm) continue;
-                    float *p = c + (int64_t)dr * a.ldc;
+                    float *p = c + (int64_t)dr * ldc;
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
                         if (col0 + j < a.cn) p[j] = epilogue(a, acc[i][j][r], p + j);
@@ -667,7 +681,7 @@ struct MfmaDlCore {
                 const int rho = 8 * (r >> 2) + (r & 3);
                 const int dr = AKC ? i * 32 + rho : FM * rho + i;
                 if (EDGE && row0 + dr >= a.cm) continue;
-                float *p = c + (int64_t)dr * a.ldc;
+                float *p = c + (int64_t)dr * ldc;
                 if constexpr (FN == 1) {
                     *p = epilogue(a, acc[i][0][r], p);
                 } else if constexpr (FN == 2) {
@@ -707,7 +721,7 @@ struct MfmaDlCore {
 template <class Core, bool SPLIT>
 __global__ __launch_bounds__(Core::NT) void sgemm_mfma_dl_kernel(KernelArgs a) {
     __shared__ __attribute__((aligned(1024))) float lds[Core::LDS_FLOATS];
-    run_gemm<Core, SPLIT>(a, lds);
+    run_gemm<Core, SPLIT, typename Core::Shape>(a, lds);
     // No load may still write this workgroup's LDS once its waves are gone.
     wait_counts<0, 0>();
 }
@@ -737,6 +751,18 @@ SGEMM_DL_LAYOUT_CORES(Dl64x64x64, 64, 64, 64, 2, 2, 3, 1, 2)
 SGEMM_DL_LAYOUT_CORES(Dl128x128x32, 128, 128, 32, 2, 2, 3, 1, 2)
 SGEMM_DL_LAYOUT_CORES(Dl256x256x16, 256, 256, 16, 4, 2, 3, 1, 1)
 #undef SGEMM_DL_LAYOUT_CORES
+
+// Kernels compiled for one product each (SGEMM_SCHED_FIXED): the automatic
+// choice's configuration and tile order for the measured square and long-K
+// products, in the order of kFixedShapes (plan.cpp).
+using DlFixed4096 = MfmaDlCore<256, 256, 16, 4, 2, 3, 1, 1, false, false, false,
+                               FixedShape<4096, 4096, 4096, 256, 256, 16, 4>>;
+using DlFixed2048 = MfmaDlCore<128, 128, 32, 2, 2, 3, 1, 2, false, false, false,
+                               FixedShape<2048, 2048, 2048, 128, 128, 32, 4>>;
+using DlFixed1024 = MfmaDlCore<64, 64, 64, 2, 2, 3, 1, 2, false, false, false,
+                               FixedShape<1024, 1024, 1024, 64, 64, 64, 4>>;
+using DlFixed1024x16384 = MfmaDlCore<64, 64, 64, 2, 2, 3, 1, 2, false, false, false,
+                                     FixedShape<1024, 1024, 16384, 64, 64, 64, 4>>;
 
 template <class Core>
 static hipError_t launch(const KernelArgs &a, hipStream_t s) {
@@ -796,6 +822,28 @@ hipError_t launch_mfma_dl(int cfg, const KernelArgs &a, hipStream_t s) {
     case id: return launch<core>(a, s);
         SGEMM_DL_CONFIGS(X)
 #undef X
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// A compile-time-shape kernel: whole tiles only, its own grid.
+template <class Core>
+static hipError_t launch_whole(const KernelArgs &a, hipStream_t s) {
+    KernelArgs args = a;
+    void *params[] = {&args};
+    return hipLaunchKernel((const void *)sgemm_mfma_dl_kernel<Core, false>,
+                           dim3(Core::Shape::TILES), dim3(Core::NT), params, 0, s);
+}
+
+// The compile-time-shape kernel kFixedShapes[idx]; the plan has checked
+// that the call is that product (dense, whole tiles, data-parallel).
+hipError_t launch_mfma_dl_fixed(int idx, const KernelArgs &a, hipStream_t s) {
+    if (a.sk_tiles != 0) return hipErrorInvalidValue;
+    switch (idx) {
+    case 0: return launch_whole<DlFixed4096>(a, s);
+    case 1: return launch_whole<DlFixed2048>(a, s);
+    case 2: return launch_whole<DlFixed1024>(a, s);
+    case 3: return launch_whole<DlFixed1024x16384>(a, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -14,6 +14,8 @@ hipError_t launch_mfma(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t occupancy_mfma(int cfg, int *wg_per_cu);
 hipError_t launch_mfma_dl(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t occupancy_mfma_dl(int cfg, int *wg_per_cu);
+// The direct-to-LDS kernel compiled for the product kFixedShapes[idx].
+hipError_t launch_mfma_dl_fixed(int idx, const KernelArgs &a, hipStream_t s);
 hipError_t launch_generic(int cfg, const KernelArgs &a, hipStream_t s);
 hipError_t occupancy_generic(int cfg, int *wg_per_cu);
 hipError_t launch_valu(int cfg, const KernelArgs &a, hipStream_t s);

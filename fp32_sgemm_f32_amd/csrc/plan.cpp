@@ -45,6 +45,14 @@ const int kNumCfgs = SGEMM_NUM_CFGS;
 
 static_assert(sizeof(kCfgs) / sizeof(kCfgs[0]) == SGEMM_NUM_CFGS, "config table size");
 
+const FixedShapeInfo kFixedShapes[] = {
+    {4096, 4096, 4096, SGEMM_CFG_DL_256x256x16, 4},
+    {2048, 2048, 2048, SGEMM_CFG_DL_128x128x32, 4},
+    {1024, 1024, 1024, SGEMM_CFG_DL_64x64x64, 4},
+    {1024, 1024, 16384, SGEMM_CFG_DL_64x64x64, 4},
+};
+const int kNumFixedShapes = sizeof(kFixedShapes) / sizeof(kFixedShapes[0]);
+
 int64_t workspace_bytes(int grid, int sk_tiles, int bm, int bn) {
     if (sk_tiles <= 0) return 0;
     return (int64_t)grid * 2 * bm * bn * 4;
@@ -278,11 +286,34 @@ static int plan_rowdot(const PlanRequest &req, int cus, int occ, Plan *out) {
     return SGEMM_OK;
 }
 
+// The compile-time-shape kernel for a request: the data-parallel plan of
+// the same configuration, which must be the one a kFixedShapes entry was
+// compiled for (shape, configuration, tile order, one workgroup per tile).
+static int plan_fixed(const PlanRequest &req, Plan *out) {
+    PlanRequest r = req;
+    r.sched = SGEMM_SCHED_DP;
+    Plan p;
+    const int st = make_plan(r, &p);
+    if (st != SGEMM_OK) return st;
+    if (!req.aligned || req.trans_a || req.trans_b || p.edge || p.sk_tiles) return SGEMM_ERR_CONFIG;
+    for (int i = 0; i < kNumFixedShapes; ++i) {
+        const FixedShapeInfo &f = kFixedShapes[i];
+        if (f.M == req.M && f.N == req.N && f.K == req.K && f.config == p.config && f.group_m == p.group_m &&
+            p.xcd_remap && p.grid == p.tiles_m * p.tiles_n) {
+            p.fixed = i + 1;
+            *out = p;
+            return SGEMM_OK;
+        }
+    }
+    return SGEMM_ERR_CONFIG;
+}
+
 int make_plan(const PlanRequest &req, Plan *out) {
     const int M = req.M, N = req.N, K = req.K;
     if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SHAPE;
     if (req.config < 0 || req.config >= kNumCfgs) return SGEMM_ERR_CONFIG;
-    if (req.sched < SGEMM_SCHED_AUTO || req.sched > SGEMM_SCHED_STREAMK) return SGEMM_ERR_CONFIG;
+    if (req.sched < SGEMM_SCHED_AUTO || req.sched > SGEMM_SCHED_FIXED) return SGEMM_ERR_CONFIG;
+    if (req.sched == SGEMM_SCHED_FIXED) return plan_fixed(req, out);
     const int cus = req.num_cus > 0 ? req.num_cus : 1;
 
     int cfg = req.config;

@@ -72,7 +72,20 @@ struct Plan {
     int edge;            // the shape is not a multiple of the tile: masked loads and stores
     int64_t sk_iters;
     int64_t workspace_bytes;
+    int fixed = 0;       // 1 + index into kFixedShapes: the kernel compiled for this product
 };
+
+// Products that have a kernel compiled for their exact shape
+// (SGEMM_SCHED_FIXED): dense row-major A (M x K), B (K x N), C (M x N), the
+// configuration and tile-row grouping the automatic choice gives them.  The
+// instances in gemm_mfma_dl.hip follow this order.
+struct FixedShapeInfo {
+    int M, N, K;
+    int config;
+    int group_m;
+};
+extern const FixedShapeInfo kFixedShapes[];
+extern const int kNumFixedShapes;
 
 // Returns an SGEMM_* status; fills *out on success.
 int make_plan(const PlanRequest &req, Plan *out);

@@ -380,8 +380,14 @@ int run(const Call &c) {
     int st = check_args(c);
     if (st != SGEMM_OK) return st;
     if (c.config < 0 || c.config >= SGEMM_NUM_CFGS) return SGEMM_ERR_CONFIG;
-    if (c.sched < SGEMM_SCHED_AUTO || c.sched > SGEMM_SCHED_STREAMK) return SGEMM_ERR_CONFIG;
+    if (c.sched < SGEMM_SCHED_AUTO || c.sched > SGEMM_SCHED_FIXED) return SGEMM_ERR_CONFIG;
     if (c.M == 0 || c.N == 0) return SGEMM_OK;
+    // The compile-time-shape kernels know the leading dimensions and run
+    // the plain product only: anything else is refused before any work.
+    if (c.sched == SGEMM_SCHED_FIXED &&
+        (c.ta || c.tb || c.tc || c.repacked || c.cm || c.cn || !c.reads_ab() || c.lda != c.K || c.ldb != c.N ||
+         c.ldc != c.N || !vector_layout(c) || (c.scaled && !(c.alpha == 1.0f && c.beta == 0.0f))))
+        return SGEMM_ERR_CONFIG;
 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -473,6 +479,8 @@ int run(const Call &c) {
         }
         e = launch_cfg(p.config, a, c.stream, c.tc);   // the skinny and row-dot kernels add their own splits
         if (e == hipSuccess && !any_layout(p.config)) e = launch_sk_fixup(a, p.bm, p.bn, c.stream);
+    } else if (p.fixed) {
+        e = launch_mfma_dl_fixed(p.fixed - 1, a, c.stream);
     } else {
         e = launch_cfg(p.config, a, c.stream, c.tc);
     }
@@ -611,6 +619,7 @@ static int plan_for(int ta, int tb, int M, int N, int K, int config, int sched, 
     out->group_m = p.group_m;
     out->sk_iters = p.sk_iters;
     out->workspace_bytes = p.workspace_bytes;
+    out->fixed_shape = p.fixed ? 1 : 0;
     return SGEMM_OK;
 }
 

@@ -176,6 +176,16 @@ extern "C" {
 #define SGEMM_SCHED_AUTO     0  /* whole tiles in full waves, Stream-K for the rest */
 #define SGEMM_SCHED_DP       1  /* one workgroup per output tile, full K each */
 #define SGEMM_SCHED_STREAMK  2  /* every tile's K range split evenly over a resident grid */
+/* Data-parallel, on the automatic configuration's kernel compiled for this
+ * exact product (every size, leading dimension and the tile order fixed at
+ * compile time; "Beyond Kernel 7: Closing the Gap to cuBLAS on an H100 FP32
+ * GEMM", section "Kernel 13", the size-specialised build).  Compiled for
+ * M x N x K = 4096^3, 2048^3, 1024^3 and 1024 x 1024 x 16384, with lda = K,
+ * ldb = ldc = N, 16-byte aligned A, B, C and the plain product (sgemm_f32,
+ * or sgemm_f32_gemm with alpha = 1, beta = 0, no transposes); anything else
+ * returns SGEMM_ERR_CONFIG.  Results are those of SGEMM_SCHED_DP bit for
+ * bit (same kernel body, same summation order). */
+#define SGEMM_SCHED_FIXED    3
 
 /*
  * C = A * B.  Requirements: M, N, K >= 0; lda >= K, ldb >= N, ldc >= N;
@@ -313,6 +323,7 @@ typedef struct sgemm_f32_plan_t {
                             (few rows with B stored N x K on the row-dot
                             kernel, few columns with A stored K x M on the
                             skinny kernel); the fields above describe it */
+    int fixed_shape;     /* 1: SGEMM_SCHED_FIXED, the kernel compiled for this product */
 } sgemm_f32_plan_t;
 
 int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,

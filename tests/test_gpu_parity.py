@@ -637,6 +637,52 @@ def test_workload_full_size_storage_orders(dev, name, layout):
     check(C.cpu().numpy(), C_ref, S, f"{name} ta={ta} tb={tb}")
 
 
+@pytest.mark.parametrize("name", ["sgemm_4096", "sgemm_2048", "sgemm_1024", "sgemm_1024_int",
+                                  "sgemm_1024x1024x16384"])
+def test_compile_time_shape_kernels(dev, name):
+    """SGEMM_SCHED_FIXED (the kernel compiled for the product's exact shape):
+    every element against the oracle (the integer variant exact), and the
+    same bits as the runtime kernel of the same configuration, which sums in
+    the same order."""
+    w = workloads.WORKLOADS[name]
+    log(f"case compile-time shape {name} {w.shape}")
+    A, B, C_ref, S = full_reference(w)
+    C_fixed = gpu_matmul(A, B, dev, sched=sg.SCHED_FIXED)
+    C_dp = gpu_matmul(A, B, dev, sched=sg.SCHED_DP)
+    assert np.array_equal(C_fixed.view(np.uint32), C_dp.view(np.uint32))
+    if w.dist == "int4":
+        assert np.array_equal(C_fixed.astype(np.float64), C_ref)
+    else:
+        check(C_fixed, C_ref, S, f"{name} fixed")
+
+
+def test_compile_time_shape_refuses_other_calls(dev):
+    """Only the dense plain product of a compiled shape runs on those kernels;
+    a padded leading dimension, scaling, a transposed operand or another
+    shape is refused before any work (C untouched)."""
+    import torch
+    M = N = K = 1024
+    A, B = workloads.generate(M, N, K, "int4", 130)
+    Ad, Bd = to_dev(A, dev), to_dev(B, dev)
+    Cbuf = torch.full((M, N + 4), 5.0, dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+    cases = {
+        "padded_ldc": lambda: sg.sgemm_raw(M, N, K, Ad.data_ptr(), K, Bd.data_ptr(), N, Cbuf.data_ptr(), N + 4, s,
+                                           sg.CFG_AUTO, sg.SCHED_FIXED),
+        "scaled": lambda: sg.gemm_raw(0, 0, M, N, K, 2.0, Ad.data_ptr(), K, Bd.data_ptr(), N, 0.0, Cbuf.data_ptr(),
+                                      N + 4, s, sg.CFG_AUTO, sg.SCHED_FIXED),
+        "transposed_b": lambda: sg.gemm_raw(0, 1, M, N, K, 1.0, Ad.data_ptr(), K, Bd.data_ptr(), K, 0.0,
+                                            Cbuf.data_ptr(), N + 4, s, sg.CFG_AUTO, sg.SCHED_FIXED),
+        "other_shape": lambda: sg.sgemm_raw(M, N, 512, Ad.data_ptr(), K, Bd.data_ptr(), N, Cbuf.data_ptr(), N + 4,
+                                            s, sg.CFG_AUTO, sg.SCHED_FIXED),
+    }
+    for case, fn in cases.items():
+        log(f"case compile-time shape refusal {case}")
+        assert fn() == sg.ERR_CONFIG, case
+    torch.cuda.synchronize()
+    assert bool((Cbuf == 5.0).all().item())
+
+
 # Leading dimensions just beyond the reach of the direct-to-LDS kernels'
 # 32-bit source offsets (BM or BK rows of A, BK or BN rows of B, times the
 # leading dimension, under 2^32 bytes; 2^31 for the edge-masking ones): the

@@ -65,17 +65,22 @@ def kernels(asm):
     return out
 
 
+# 9 whole-tile configurations (A M x K, B K x N), the 4 configurations of
+# the automatic choice in the 3 other storage orders and with edge masking in
+# all 4, each with and without Stream-K; plus the 4 kernels compiled for one
+# product each (whole tiles only).
+N_KERNELS = 2 * (9 + 4 * 3 + 4 * 4) + 4
+
+
 def test_every_configuration_is_compiled(dl_asm):
     ks = kernels(dl_asm)
-    # 9 whole-tile configurations (A M x K, B K x N), the 4 configurations of
-    # the automatic choice in the 3 other storage orders and with edge
-    # masking in all 4, each with and without Stream-K.
-    assert len(ks) == 2 * (9 + 4 * 3 + 4 * 4)
+    assert len(ks) == N_KERNELS
+    assert sum("FixedShape" in k for k in ks) == 4
 
 
 def is_edge(name):
     # MfmaDlCore<..., EDGE, TA, TB>: the three booleans close the argument list.
-    m = re.search(r"ELb([01])ELb[01]ELb[01]EE", name)
+    m = re.search(r"ELb([01])ELb[01]ELb[01]E(?:E|NS_1\d(?:Runtime|Fixed)Shape)", name)
     assert m, name
     return m.group(1) == "1"
 
@@ -106,7 +111,7 @@ def test_no_kernel_spills_to_scratch(dl_asm):
     its state in registers: a private segment would mean spills to scratch
     memory."""
     descriptors = re.findall(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", dl_asm, re.S)
-    assert len(descriptors) == 2 * (9 + 4 * 3 + 4 * 4)
+    assert len(descriptors) == N_KERNELS
     for name, body in descriptors:
         m = re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", body)
         assert m and m.group(1) == "0", f"{name}: private segment {m and m.group(1)}"
@@ -117,7 +122,7 @@ def test_no_lds_read_used_before_its_wait(dl_asm):
     split or whole-tile instance) reads or writes a register that an LDS
     read is still loading."""
     fs = asm_hazards.functions(dl_asm, r"_Z\w*sgemm_mfma_dl_kernel\w*")
-    assert len(fs) == 2 * (9 + 4 * 3 + 4 * 4)
+    assert len(fs) == N_KERNELS
     bad = {name[:100]: found[:3] for name, blocks in fs.items() if (found := asm_hazards.hazards(blocks))}
     assert not bad, f"LDS read destinations used before their wait: {bad}"
 

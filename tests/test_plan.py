@@ -421,3 +421,42 @@ def test_thin_products_in_other_storage_orders_run_transposed():
     for shape, tb in [((300, 12, 300), 0), ((16384, 17, 16384), 0), ((255, 1, 4096), 0), ((16384, 1, 16384), 1)]:
         p = plan(*shape, 0 if shape == (16384, 1, 16384) else 1, tb)
         assert p["transposed"] == 0, shape
+
+
+FIXED_SHAPES = [((4096, 4096, 4096), sg.CFG_DL_256x256x16), ((2048, 2048, 2048), sg.CFG_DL_128x128x32),
+                ((1024, 1024, 1024), sg.CFG_DL_64x64x64), ((1024, 1024, 16384), sg.CFG_DL_64x64x64)]
+
+
+@pytest.mark.parametrize("shape,config", FIXED_SHAPES, ids=lambda x: "x".join(map(str, x)) if isinstance(x, tuple) else "")
+def test_compile_time_shape_plans(shape, config):
+    """SGEMM_SCHED_FIXED: the automatic choice's configuration, data-parallel,
+    with the same grid and tile order as the runtime plan of the shape."""
+    p = sg.plan(*shape, sched=sg.SCHED_FIXED)
+    q = sg.plan(*shape, sched=sg.SCHED_DP)
+    assert p["fixed_shape"] == 1 and q["fixed_shape"] == 0
+    assert p["config"] == config and p["sched"] == sg.SCHED_DP and p["sk_tiles"] == 0
+    for k in ("config", "grid", "group_m", "xcd_remap", "tiles_m", "tiles_n", "iters_per_tile"):
+        assert p[k] == q[k], k
+    assert sg.plan(*shape)["fixed_shape"] == 0      # the automatic choice keeps the runtime kernels
+
+
+@pytest.mark.parametrize("case", ["other_shape", "ragged", "forced_other_config", "transposed_a", "transposed_b",
+                                  "thin"])
+def test_compile_time_shape_refused_elsewhere(case):
+    kw = {}
+    shape = (4096, 4096, 4096)
+    if case == "other_shape":
+        shape = (4096, 4096, 2048)
+    elif case == "ragged":
+        shape = (1000, 1024, 1024)
+    elif case == "forced_other_config":
+        kw["config"] = sg.CFG_DL_128x128x32
+    elif case == "transposed_a":
+        kw["trans_a"] = 1
+    elif case == "transposed_b":
+        kw["trans_b"] = 1
+    elif case == "thin":
+        shape = (8, 4096, 4096)
+    with pytest.raises(sg.SgemmError) as e:
+        sg.plan(*shape, sched=sg.SCHED_FIXED, **kw)
+    assert e.value.status == sg.ERR_CONFIG
