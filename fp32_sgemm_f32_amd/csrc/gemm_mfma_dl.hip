@@ -193,6 +193,7 @@ template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int S_, int KSPLI
           bool EDGE = false, bool TA = false, bool TB = false, class SH = RuntimeShape>
 struct MfmaDlCore {
     using Shape = SH;
+    static constexpr bool kEdge = EDGE;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
     static constexpr int LA = LA_;                  // groups of operand reads ahead of the MFMAs
     static constexpr int NS = LA == 1 ? 2 : 4;      // operand register sets
@@ -234,6 +235,7 @@ struct MfmaDlCore {
     static_assert(!SH::kFixed || (!EDGE && !TA && !TB), "a compile-time shape: whole tiles, A M x K, B K x N");
 
     floatx16 acc[FM][FN];
+    int tiles_started = 0;   // uniform: tiles (or split ranges) this workgroup has begun
 
     __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -586,9 +588,13 @@ struct MfmaDlCore {
         const int tail_ch =
             __builtin_amdgcn_readfirstlane(EDGE && k1 == SH::ipt(a) && a.K % BK != 0 ? nch - 1 : -1);
 
-        // A previous tile of this workgroup may still read the ring.
-        wait_counts<0, 0>();
-        lds_barrier();
+        // A previous tile of this workgroup may still read the ring (not
+        // before the workgroup's first tile: its waves start on an idle
+        // ring).
+        if (tiles_started++ > 0) {
+            wait_counts<0, 0>();
+            lds_barrier();
+        }
         // Chunks 0 .. S-2 up front (stage = chunk); chunk c+S-1 is loaded
         // during chunk c.
         issue_prologue<0>(g, nch, tail_ch);
@@ -721,7 +727,17 @@ struct MfmaDlCore {
 template <class Core, bool SPLIT>
 __global__ __launch_bounds__(Core::NT) void sgemm_mfma_dl_kernel(KernelArgs a) {
     __shared__ __attribute__((aligned(1024))) float lds[Core::LDS_FLOATS];
-    run_gemm<Core, SPLIT, typename Core::Shape>(a, lds);
+    // Every argument the first tile needs, in scalar registers before
+    // anything else: the compiler would otherwise load the tile-order fields,
+    // branch on them, and only then load the operand pointers, two dependent
+    // round trips to the argument memory before the first global load.
+    using SH = typename Core::Shape;
+    asm volatile("" ::"s"(a.A), "s"(a.B), "s"(a.C), "s"(SH::lda(a)), "s"(SH::ldb(a)), "s"(SH::ldc(a)),
+                 "s"(SH::ipt(a)), "s"(SH::grid(a)), "s"(SH::dp_tiles(a)), "s"(SH::tiles_m(a)), "s"(SH::tiles_n(a)),
+                 "s"(SH::group_m(a)), "s"(SH::xcd_remap(a)), "s"(a.scaled), "s"(a.alpha), "s"(a.beta));
+    if constexpr (Core::kEdge)
+        asm volatile("" ::"s"(a.M), "s"(a.N), "s"(a.K), "s"(a.cm), "s"(a.cn), "s"(a.c_scalar));
+    run_gemm<Core, SPLIT, SH>(a, lds);
     // No load may still write this workgroup's LDS once its waves are gone.
     wait_counts<0, 0>();
 }
