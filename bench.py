@@ -47,12 +47,13 @@ FLUSHED_WARMUP_CALLS, FLUSHED_WARMUP_S = 20, 0.1
 # HBM-side bytes per launch of the headline kernel in the flushed protocol,
 # from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE in KiB per dispatch),
 # each scaled by what the same counter reads for a plain 256 MiB device copy
-# (FETCH_SIZE 2.0, WRITE_SIZE 1.0).  Valid only for the kernel sources they
-# were taken on (digest below); otherwise reported null.
+# (FETCH_SIZE 2.0, WRITE_SIZE 1.0); see
+# profiles/sgemm_4096_dl_256x256x16_counters.md.  Valid only for the kernel
+# sources they were taken on (digest below); otherwise reported null.
 TRAFFIC = {
     "kernel": "dl_256x256x16", "workload": "sgemm_4096",
-    "source_digest": "c901998312e62bc7",
-    "bytes": 469864950,
+    "source_digest": "e36efc96dfff3f8a",
+    "bytes": 469863927,
 }
 KERNEL_SOURCES = ("fp32_sgemm_f32_amd/csrc/gemm_mfma_dl.hip", "fp32_sgemm_f32_amd/csrc/gemm_common.h")
 
