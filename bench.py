@@ -368,7 +368,7 @@ def main():
         achieved = w.flops / mean_s / 1e12
         # The vector-ALU kernel is bounded by the FP32 vector rate (157.3
         # TFLOP/s too), the others by the FP32 matrix-core rate.
-        bound = "alu" if cfg == sg.CFG_VALU_128x128x8 else "mfma"
+        bound = "alu" if cfg in (sg.CFG_VALU_128x128x8, sg.CFG_VALU_256x128x8) else "mfma"
         roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic,
                     "traffic_unit": "bytes per launch"}

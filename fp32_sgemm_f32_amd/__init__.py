@@ -52,7 +52,8 @@ CFG_DL_256x128x16 = 21
 CFG_GENERIC_64x64x16 = 22
 CFG_SKINNY_16x256 = 23
 CFG_ROWDOT_N8 = 24
-NUM_CFGS = 25
+CFG_VALU_256x128x8 = 25
+NUM_CFGS = 26
 CFG_NAMES = {
     CFG_AUTO: "auto",
     CFG_MFMA_256x256x16: "mfma_256x256x16",
@@ -79,6 +80,7 @@ CFG_NAMES = {
     CFG_GENERIC_64x64x16: "generic_64x64x16",
     CFG_SKINNY_16x256: "skinny_16x256",
     CFG_ROWDOT_N8: "rowdot_n8",
+    CFG_VALU_256x128x8: "valu_256x128x8",
 }
 # (tile_m, tile_n, tile_k) of each configuration.
 CFG_TILES = {
@@ -93,6 +95,7 @@ CFG_TILES = {
     CFG_DL_64x64x32_K2: (64, 64, 32), CFG_DL_128x128x32_K2: (128, 128, 32),
     CFG_DL_64x64x64: (64, 64, 64), CFG_DL_128x256x16: (128, 256, 16),
     CFG_DL_256x128x16: (256, 128, 16), CFG_GENERIC_64x64x16: (64, 64, 16),
+    CFG_VALU_256x128x8: (256, 128, 8),
 }
 
 # Schedules (SGEMM_SCHED_*).

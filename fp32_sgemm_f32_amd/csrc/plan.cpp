@@ -40,6 +40,7 @@ const CfgInfo kCfgs[] = {
     {SGEMM_CFG_GENERIC_64x64x16, 64, 64, 16, 256, kKindGeneric, 2, true, true, "generic_64x64x16"},
     {SGEMM_CFG_SKINNY_16x256, 16, 256, kSkinnyBlock, 512, kKindSkinny, 1, true, true, "skinny_16x256"},
     {SGEMM_CFG_ROWDOT_N8, 8, 8, 0, 512, kKindRowdot, 2, true, true, "rowdot_n8"},
+    {SGEMM_CFG_VALU_256x128x8, 256, 128, 8, 256, kKindValu, 2, false, false, "valu_256x128x8"},
 };
 const int kNumCfgs = SGEMM_NUM_CFGS;
 

@@ -167,7 +167,11 @@ extern "C" {
  * it for such products with M, K >= 256 and N <= 2, or N <= 8 once
  * M * K >= 2^26 or when the layout rules out the tiled kernels. */
 #define SGEMM_CFG_ROWDOT_N8         24 /* 512 threads, 8 waves over rows of A */
-#define SGEMM_NUM_CFGS              25 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
+/* The register-tiled outer product of scalar FP32 fused multiply-adds with a
+ * 16 x 8 tile per lane (0.75 bytes of LDS operands per multiply-add) and the
+ * next k step's operands read during the current one. */
+#define SGEMM_CFG_VALU_256x128x8    25 /* 256 threads, 16x8 outputs per lane */
+#define SGEMM_NUM_CFGS              26 /* configurations are 1 .. SGEMM_NUM_CFGS-1 */
 /* The configurations not named above as running other shapes or storage
  * orders need A stored M x K, B stored K x N, the vector layout and a shape
  * their tile divides. */

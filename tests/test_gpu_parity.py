@@ -318,7 +318,7 @@ def test_storage_orders_integer_inputs_bit_exact(dev, config, layout):
 
 
 @pytest.mark.parametrize("config", [sg.CFG_MFMA_256x256x16, sg.CFG_MFMA_128x128x32, sg.CFG_VALU_128x128x8,
-                                    sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_GENERIC_64x64x16,
+                                    sg.CFG_VALU_256x128x8, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32_K2, sg.CFG_GENERIC_64x64x16,
                                     sg.CFG_SKINNY_16x256, sg.CFG_ROWDOT_N8],
                          ids=lambda c: sg.CFG_NAMES[c])
 def test_blas_scaling_on_every_kernel_family(dev, config):
@@ -395,7 +395,8 @@ def test_padded_leading_dimensions_and_untouched_gap(dev, config):
     check(Cn[:, :N], C_ref, S, "padded")
 
 
-@pytest.mark.parametrize("config", [sg.CFG_MFMA_128x128x32, sg.CFG_MFMA_256x256x16, sg.CFG_VALU_128x128x8],
+@pytest.mark.parametrize("config", [sg.CFG_MFMA_128x128x32, sg.CFG_MFMA_256x256x16, sg.CFG_VALU_128x128x8,
+                                    sg.CFG_VALU_256x128x8],
                          ids=lambda c: sg.CFG_NAMES[c])
 def test_repeatable_and_fully_written(dev, config):
     """C pre-filled with NaN is fully overwritten; repeated split runs are

@@ -183,3 +183,46 @@ def test_hazard_check_catches_a_removed_wait(dl_asm):
                 assert asm_hazards.hazards(planted), (name, label, k)
                 return
     pytest.fail("no lgkmcnt wait ahead of an MFMA found")
+
+
+VALU_SRC = os.path.join(build.CSRC, "gemm_valu.hip")
+
+
+@pytest.fixture(scope="module")
+def valu_asm(tmp_path_factory):
+    if not _hipcc_available():
+        pytest.skip("hipcc not found")
+    out = str(tmp_path_factory.mktemp("asm") / "valu.s")
+    cmd = [build.hipcc(), *[f for f in build.COMMON if f not in ("-fPIC", "-fvisibility=hidden")],
+           "-x", "hip", "--cuda-device-only", "-S", VALU_SRC, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return open(out).read()
+
+
+def test_valu_multiply_adds_avoid_the_accumulator_bank(valu_asm):
+    """The vector-ALU cores issue v_fmac_f32 with the row operand a as the
+    second source: a multiply-add whose accumulator shares that source's VGPR
+    bank (register number mod 4) runs 27% slower on gfx950, and with b there
+    the compiler put almost every one in that case.  With a there, 2 of a
+    row's 8 accumulators share its bank when the row is allocated
+    contiguously (25%; measured 28-31%): fail above 40%."""
+    fs = asm_hazards.functions(valu_asm, r"_Z\w*sgemm_valu_kernel\w*")
+    assert len(fs) == 4   # two cores, each with and without the split part
+    for name, blocks in fs.items():
+        fmacs = [i for _, ins in blocks for i in ins if i.startswith("v_fmac_f32")]
+        same = 0
+        for ins in fmacs:
+            dst, _src0, src1 = (x.strip() for x in ins.split(None, 1)[1].split(","))
+            if dst.startswith("v") and src1.startswith("v") and int(dst[1:]) % 4 == int(src1[1:]) % 4:
+                same += 1
+        assert len(fmacs) >= 512, name
+        assert same / len(fmacs) <= 0.40, f"{name}: {same}/{len(fmacs)} multiply-adds with src1 in the accumulator's bank"
+
+
+def test_valu_loops_hold_no_lds_read_hazard(valu_asm):
+    """The vector-ALU cores' LDS reads are the compiler's own; the dataflow
+    check holds for them too."""
+    fs = asm_hazards.functions(valu_asm, r"_Z\w*sgemm_valu_kernel\w*")
+    bad = {n[:80]: h[:3] for n, b in fs.items() if (h := asm_hazards.hazards(b))}
+    assert not bad, bad

@@ -13,7 +13,7 @@ import pytest
 
 import fp32_sgemm_f32_amd as sg
 
-OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1, 2, 1, 1, 1, 2, 1, 1, 2, 2, 2, 1, 2]
+OCC = [0, 1, 2, 1, 1, 2, 1, 2, 4, 2, 2, 1, 1, 2, 1, 1, 1, 2, 1, 1, 2, 2, 2, 1, 2, 2]
 EDGE_CFGS = {sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64, sg.CFG_DL_128x128x32, sg.CFG_DL_256x256x16,
              sg.CFG_GENERIC_64x64x16}
 
