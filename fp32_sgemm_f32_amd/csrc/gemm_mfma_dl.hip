@@ -688,12 +688,15 @@ struct MfmaDlCore {
                 const int dr = AKC ? i * 32 + rho : FM * rho + i;
                 if (EDGE && row0 + dr >= a.cm) continue;
                 float *p = c + (int64_t)dr * ldc;
+                // Non-temporal stores: nothing in this kernel reads C back
+                // (measured +0.8-1% at 2048^3 and 1024^3, level at 4096^3).
                 if constexpr (FN == 1) {
-                    *p = epilogue(a, acc[i][0][r], p);
+                    __builtin_nontemporal_store(epilogue(a, acc[i][0][r], p), p);
                 } else if constexpr (FN == 2) {
-                    *(f32x2 *)p = epilogue(a, f32x2{acc[i][0][r], acc[i][1][r]}, p);
+                    __builtin_nontemporal_store(epilogue(a, f32x2{acc[i][0][r], acc[i][1][r]}, p), (f32x2 *)p);
                 } else {
-                    *(f32x4 *)p = epilogue(a, f32x4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]}, p);
+                    __builtin_nontemporal_store(
+                        epilogue(a, f32x4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]}, p), (f32x4 *)p);
                 }
             }
     }
