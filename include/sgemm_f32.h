@@ -114,8 +114,9 @@ extern "C" {
                                   the matrix extent runs past the end of its allocation */
 #define SGEMM_ERR_CONFIG    8  /* unknown kernel configuration/schedule, or a forced one that
                                   cannot run this shape or layout */
-#define SGEMM_ERR_SCRATCH   9  /* sgemm_f32_gemm_noalloc: the repacked copies the call needs do
-                                  not fit SGEMM_F32_NOALLOC_SCRATCH_BYTES */
+#define SGEMM_ERR_SCRATCH   9  /* sgemm_f32_gemm_noalloc: the scratch the call needs (repacked
+                                  copies, or split partials of a kernel that cannot run
+                                  unsplit) exceeds SGEMM_F32_NOALLOC_SCRATCH_BYTES */
 
 /* Kernel configurations (sgemm_f32_ex / sgemm_f32_plan).  "MFMA" configs
  * run the product on the FP32 matrix cores (v_mfma_f32_32x32x2_f32: full
@@ -267,8 +268,10 @@ int sgemm_f32_gemm_ex(int trans_a, int trans_b, int M, int N, int K, float alpha
  *   - a split schedule whose partial tiles do not fit (or do not fit beside
  *     the repacked copies) runs data-parallel instead: whole tiles, no
  *     partials (results within the same tolerance; exact on integer inputs);
+ *     where the kernel cannot run unsplit (the row-dot kernel when B's K
+ *     range exceeds its LDS), the call is refused with SGEMM_ERR_SCRATCH;
  *   - repacked copies that do not fit the array are refused with
- *     SGEMM_ERR_SCRATCH before anything is enqueued.
+ *     SGEMM_ERR_SCRATCH, both before anything is enqueued.
  * Nothing needs clearing between calls: every partial tile and every padded
  * copy is written in full before it is read.  Every call on a device shares
  * that device's array and leaves its contents behind: calls on one stream
