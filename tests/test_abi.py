@@ -166,3 +166,25 @@ def test_tflops_accounting_matches_pages():
         hi = workloads.tflops(n, n, n, t - half)
         p_half = 0.5 * 10.0 ** -len(printed.split(".")[1])
         assert lo - p_half <= float(printed) <= hi + p_half, tag
+
+
+def noalloc(M, N, K, A=ALIGNED, lda=None, B=ALIGNED + (1 << 30), ldb=None, C=ALIGNED + (2 << 30), ldc=None,
+            ta=0, tb=0):
+    lda = (M if ta else K) if lda is None else lda
+    ldb = (K if tb else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return sg.gemm_noalloc_raw(ta, tb, M, N, K, 1.0, A, lda, B, ldb, 0.0, C, ldc, 0)
+
+
+def test_noalloc_rejects_bad_arguments_before_the_device():
+    """The no-allocation call checks its arguments as sgemm_f32_gemm does,
+    before it looks up any device memory (no GPU needed for these)."""
+    assert noalloc(-1, 64, 64) == sg.ERR_SHAPE
+    assert noalloc(64, 64, 64, lda=60) == sg.ERR_LD
+    assert noalloc(64, 64, 64, ldc=60) == sg.ERR_LD
+    assert noalloc(64, 64, 64, A=0) == sg.ERR_NULL
+    assert noalloc(64, 64, 64, C=ALIGNED + (2 << 30) + 2) == sg.ERR_ALIGN
+    assert noalloc(64, 64, 64, C=ALIGNED + 1024) == sg.ERR_ALIAS
+    assert noalloc(64, 64, 64, ta=2) == sg.ERR_CONFIG
+    assert noalloc(0, 64, 64, A=0, B=0, C=0) == sg.OK
+    assert noalloc(64, 0, 64, A=0, B=0, C=0) == sg.OK

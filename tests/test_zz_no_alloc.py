@@ -139,3 +139,87 @@ def test_noalloc_refuses_copies_beyond_the_array(dev):
     As, Bs, _, ref, noalloc = run_both(dev, 0, 0, 515, 771, 1021, 1.0, 0.0, "int4", 501)
     exact, _ = oracle.gemm(As, Bs)
     assert np.array_equal(noalloc.astype(np.float64), exact)
+
+
+def test_noalloc_calls_from_two_threads_on_one_stream(dev):
+    """Two host threads make no-allocation calls on ONE stream with no host
+    synchronisation: repacked products (copies in the shared scratch array)
+    and split ones (partials there).  Each call's copies, product and sum
+    must run back to back on the stream, or another thread's copies or
+    partials would land in between.  Integer inputs: every result exact."""
+    import threading
+    import torch
+    log("case noalloc, two threads, one stream")
+    shapes = [(515, 771, 1021), (1000, 1028, 1024)]
+    assert sg.plan(*shapes[0])["repacked"] == 1 and sg.plan(*shapes[1])["sched"] == sg.SCHED_STREAMK
+    s = torch.cuda.Stream(device=dev)
+    data = []
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = workloads.generate(M, N, K, "int4", 600 + i)
+        outs = [torch.full((M, N), float("nan"), dtype=torch.float32, device=dev) for _ in range(10)]
+        data.append((M, N, K, A, B, torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev), outs))
+    torch.cuda.synchronize()
+    errors = []
+    go = threading.Barrier(2)
+
+    def worker(i):
+        try:
+            M, N, K, _, _, Ad, Bd, outs = data[i]
+            go.wait()
+            for C in outs:
+                st = sg.gemm_noalloc_raw(0, 0, M, N, K, 1.0, Ad.data_ptr(), K, Bd.data_ptr(), N, 0.0, C.data_ptr(),
+                                         N, s.cuda_stream)
+                assert st == sg.OK, st
+        except Exception as e:  # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for _, _, _, A, B, _, _, outs in data:
+        exact, _ = oracle.gemm(A, B)
+        for C in outs:
+            assert np.array_equal(C.cpu().numpy().astype(np.float64), exact)
+
+
+def test_noalloc_graph_capture_and_replay(dev):
+    """A no-allocation split call (partials in the scratch array) captured
+    into a HIP graph replays correctly, with new A written and eager work
+    (an allocating call of another shape) run between the replays; every
+    replay matches the oracle and the eager result exactly (integer
+    inputs).  Nothing has to be sized by an eager call of the same shape
+    first."""
+    import torch
+    M, N, K = 1000, 1028, 1024
+    assert sg.plan(M, N, K)["sched"] == sg.SCHED_STREAMK
+    log(f"case noalloc graph capture shape=({M},{N},{K})")
+    s = torch.cuda.Stream(device=dev)
+    A0, B = workloads.generate(M, N, K, "int4", 610)
+    Ad, Bd = torch.from_numpy(A0).to(dev), torch.from_numpy(B).to(dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    # An eager call of another, smaller shape (nothing about this shape is prepared).
+    small = torch.empty((64, 64), dtype=torch.float32, device=dev)
+    assert sg.gemm_noalloc_raw(0, 0, 64, 64, 64, 1.0, Ad.data_ptr(), K, Bd.data_ptr(), N, 0.0, small.data_ptr(), 64,
+                               s.cuda_stream) == sg.OK
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st = sg.gemm_noalloc_raw(0, 0, M, N, K, 1.0, Ad.data_ptr(), K, Bd.data_ptr(), N, 0.0, C.data_ptr(), N,
+                                 s.cuda_stream)
+    assert st == sg.OK
+    torch.cuda.synchronize()
+    for r in range(3):
+        A_r = workloads.generate(M, N, K, "int4", 620 + r)[0]
+        Ad.copy_(torch.from_numpy(A_r).to(dev))
+        E = sg.matmul(Ad, Bd)                     # eager, allocating entry point
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        exact, _ = oracle.gemm(A_r, B)
+        got = C.cpu().numpy()
+        assert np.array_equal(got.astype(np.float64), exact), f"replay {r}"
+        assert np.array_equal(got, E.cpu().numpy()), f"replay {r} vs eager"
