@@ -98,54 +98,26 @@ static int pick_group_m(int tiles_m, int run) {
     return best;
 }
 
-static int64_t tiles_of(int cfg, int M, int N) {
-    const int bm = kCfgs[cfg].bm, bn = kCfgs[cfg].bn;
-    return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-}
-
-// The tiles of `cfg` cover M x N with at least 90% of their area inside it
-// (a side much narrower than the tile wastes the rest of every tile).
-static bool covers_well(int cfg, int M, int N) {
-    const int64_t area = tiles_of(cfg, M, N) * kCfgs[cfg].bm * kCfgs[cfg].bn;
-    return 10 * (int64_t)M * N >= 9 * area;
-}
-
-// Automatic choice, from timings of the configurations on MI355X (256 CUs;
-// all direct-to-LDS, every storage order):
-//   * 256x256x16 tiles (8 waves) when every CU gets at least one (149
-//     TFLOP/s at 4096^3, 142 at 6144^3; the register-staged kernel of the
-//     same tile measured 0-5% slower);
-//   * else 128x128x32 tiles when they fill whole waves (140 at 2048^3,
-//     143 at 2048x4096x2048);
-//     either only when the tiles lie at least 90% inside C (65536x128x2048
-//     on 256x256 tiles, half of each outside: 74, on 128x128 tiles: 139);
-//   * else 64x64 tiles (146 at 1024x1024x16384, 106 at 1024^3, 141 at
-//     3072^3, where 128x128 tiles leave a part wave: 137), with 64-deep K
-//     chunks unless 32-deep ones need one chunk fewer in pairs, i.e. an odd
-//     number of 32-deep chunks (the last 64-deep chunk would then be at most
-//     half used: 1292^3 runs at 96 TFLOP/s with 32-deep chunks, 90 with
-//     64-deep ones), or C is narrow (at most 8 tiles across one side) with
-//     at least two waves of tiles: the 32-deep kernel fits two workgroups
-//     per CU and keeps twice the loads in flight, which such shapes, with
-//     little reuse of the long operand, need (131072x64x1024: 114 against
-//     105; 8192x384x4096: 144 against 140).
+// Automatic choice of the kernel family:
 //   * at most 2 columns (or 8 once A has 2^26 elements, or when the tiled
 //     kernels cannot load the layout), A stored M x K, M and K at least 256:
-//     the row-dot kernel (per-row
-//     dot products streaming A; y = A x).  16384 x 1 x 16384: 209 us against
-//     1190 on the general kernel and 216 for hipBLASLt; 16384 x 8 x 16384:
-//     231 against 264 on the tiled kernel.  At 4096 x 8 x 4096 the tiled
-//     kernel is faster (26 against 41 us): staging B per workgroup costs as
-//     much as the little A each one streams;
+//     the row-dot kernel (per-row dot products streaming A; y = A x).
+//     16384 x 1 x 16384: 209 us against 1190 on the general kernel and 216
+//     for hipBLASLt; 16384 x 8 x 16384: 231 against 264 on the tiled kernel.
+//     At 4096 x 8 x 4096 the tiled kernel is faster (26 against 41 us):
+//     staging B per workgroup costs as much as the little A each one streams;
 //   * at most 16 rows, B stored K x N, N and K at least 256 (9-16 rows:
 //     also B above 2^22 elements or a layout the tiled kernels cannot
-//     load): the skinny kernel, which streams B without computing the empty rows of a 64-row
-//     tile (1 x 16384 x 16384: 6.35 TB/s of B against 4.4 for the tiled
-//     kernel and 5.6 for hipBLASLt; 8 x 8192 x 28672: 5.6 against 4.3 and
-//     4.9; 16 x 16384 x 16384, on 16 x 16 x 4 matrix-core steps: 4.97
-//     against 4.3 and 5.75).
-// Layouts the vector kernels cannot load go to the general kernel.
-static int auto_config(const PlanRequest &r, int cus, bool aligned) {
+//     load): the skinny kernel, which streams B without computing the empty
+//     rows of a 64-row tile (1 x 16384 x 16384: 6.35 TB/s of B against 4.4
+//     for the tiled kernel and 5.6 for hipBLASLt; 8 x 8192 x 28672: 5.6
+//     against 4.3 and 4.9; 16 x 16384 x 16384, on 16 x 16 x 4 matrix-core
+//     steps: 4.97 against 4.3 and 5.75);
+//   * layouts the vector kernels cannot load: the general kernel;
+//   * everything else: the direct-to-LDS tiles, configuration and schedule
+//     by the cost model below (kTiledChoice).
+constexpr int kTiledChoice = -1;
+static int auto_config(const PlanRequest &r, bool aligned) {
     const int M = r.M, N = r.N, K = r.K;
     // 9-16 rows with B of at most 2^22 elements: the tiled kernel, 1-2 us
     // faster there (16 x 2048 x 2048: 17.2 against 18.8 us), where it can
@@ -156,14 +128,78 @@ static int auto_config(const PlanRequest &r, int cus, bool aligned) {
         (r.sched != SGEMM_SCHED_DP || K <= kRowdotFloats / rowdot_cols(N)))
         return SGEMM_CFG_ROWDOT_N8;
     if (!aligned) return SGEMM_CFG_GENERIC_64x64x16;
-    const int big = SGEMM_CFG_DL_256x256x16, mid = SGEMM_CFG_DL_128x128x32, small = SGEMM_CFG_DL_64x64x64,
-              small32 = SGEMM_CFG_DL_64x64x32;
-    if (tiles_of(big, M, N) >= cus && covers_well(big, M, N)) return big;
-    const int64_t mid_tiles = tiles_of(mid, M, N);
-    if (mid_tiles >= cus && mid_tiles % cus == 0 && covers_well(mid, M, N)) return mid;
-    const int small_m = (M + 63) / 64, small_n = (N + 63) / 64;
-    const bool narrow = (small_m <= 8 || small_n <= 8) && tiles_of(small, M, N) >= 2 * (int64_t)cus;
-    return ((K + 31) / 32) % 2 == 1 || narrow ? small32 : small;
+    return kTiledChoice;
+}
+
+// Cost model of the automatic choice among the direct-to-LDS configurations
+// and their schedules, in microseconds of kernel time.  A tile's K chunk
+// takes 2 BM BN BK FLOPs at the CU's matrix-core rate (256 FLOPs per clock at
+// 2.3 GHz) times the configuration's efficiency, and each tile a workgroup
+// runs adds a fixed cost (its first loads, the C store), hidden in part when
+// a second workgroup shares the CU.  Data-parallel: the CU with the most
+// tiles sets the time.  Split: the full waves of whole tiles, then the
+// longest split range, with a tile's fixed cost for every tile that range
+// touches, then the summing kernel (a launch, and its traffic: every partial
+// tile read, the split tiles of C written).  Writing C bounds
+// the time from below.  On a narrow C (at most 8 tiles of 64 across a side,
+// at least two waves of them) the 64x64x32 configuration, two workgroups per
+// CU, keeps more loads in flight while the long operand streams with little
+// reuse, and its efficiency is scaled up by 3% (fits gave 2-3%; alternating
+// rounds on four such shapes measured it 1-5% faster than 64x64x64).
+// The coefficients are least-squares fits (on log time) to back-to-back
+// timings of both schedules of each configuration on 236 seeded shapes,
+// sides log-uniform in 64..16384, on one MI355X.  With the fit to any three
+// of the four sweeps, the choice on the fourth came within 0.3-0.8% of its
+// fastest candidate (geometric mean per shape), where the earlier fixed
+// rules were 3.6-15% off (worst single shape 1.18x against 3.8x, at small K,
+// where splitting tiles cost more than it balanced).  The values below are
+// the fit to all four.
+struct CostCoef {
+    int cfg;
+    double eff;       // fraction of the matrix-core rate in the K loop
+    double tile_us;   // fixed cost of one tile
+};
+static const CostCoef kCostCoefs[] = {
+    {SGEMM_CFG_DL_256x256x16, 1.014, 3.855},
+    {SGEMM_CFG_DL_128x128x32, 0.9906, 3.097},
+    {SGEMM_CFG_DL_64x64x64, 0.9407, 1.909},
+    {SGEMM_CFG_DL_64x64x32, 0.9069, 1.684},
+};
+constexpr double kCuFlopsPerUs = 256.0 * 2300.0;
+constexpr double kNarrowEff64x64x32 = 1.03;  // 64x64x32 on a narrow C
+constexpr double kSumLaunchUs = 3.776;       // summing kernel: launch and fixed cost
+constexpr double kSumBytesPerUs = 5.609e6;   // summing kernel: partial tiles read, C written
+constexpr double kStoreBytesPerUs = 3.05e6;  // C written by the GEMM kernel
+
+static int64_t ceil_div(int64_t a, int64_t b) { return b > 0 ? (a + b - 1) / b : 0; }
+
+double plan_cost(const Plan &p, int M, int N, int cus, int occ) {
+    const CostCoef *cc = nullptr;
+    for (const CostCoef &x : kCostCoefs)
+        if (x.cfg == p.config) cc = &x;
+    if (!cc || cus < 1) return -1.0;
+    if (occ < 1) occ = 1;
+    double eff = cc->eff;
+    const int64_t tm64 = ceil_div(M, 64), tn64 = ceil_div(N, 64);
+    if (p.config == SGEMM_CFG_DL_64x64x32 && (tm64 <= 8 || tn64 <= 8) && tm64 * tn64 >= 2 * (int64_t)cus)
+        eff *= kNarrowEff64x64x32;
+    const double chunk_us = 2.0 * p.bm * p.bn * p.bk / (kCuFlopsPerUs * eff);
+    double t;
+    if (p.sk_tiles == 0) {
+        const int64_t n = ceil_div(p.dp_tiles, cus);
+        t = (double)n * p.ipt * chunk_us + (double)ceil_div(n, occ) * cc->tile_us;
+    } else {
+        const int64_t waves = p.dp_tiles > 0 && p.grid > 0 ? p.dp_tiles / p.grid : 0;
+        const int64_t longest = ceil_div(p.sk_iters, p.sk_grid);
+        int64_t segments = ceil_div(longest, p.ipt) + (p.ipt > 0 && longest % p.ipt ? 1 : 0);
+        if (segments > p.sk_tiles) segments = p.sk_tiles;
+        t = (double)waves * (p.ipt * chunk_us + cc->tile_us) + (double)longest * chunk_us +
+            (double)segments * cc->tile_us;
+        const double tile_bytes = 4.0 * p.bm * p.bn;
+        t += kSumLaunchUs + ((double)p.sk_grid + 2.0 * p.sk_tiles) * tile_bytes / kSumBytesPerUs;
+    }
+    const double c_us = 4.0 * M * N / kStoreBytesPerUs;
+    return t > c_us ? t : c_us;
 }
 
 int staged_equivalent(int cfg) {
@@ -309,20 +345,17 @@ static int plan_fixed(const PlanRequest &req, Plan *out) {
     return SGEMM_ERR_CONFIG;
 }
 
-int make_plan(const PlanRequest &req, Plan *out) {
-    const int M = req.M, N = req.N, K = req.K;
-    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SHAPE;
-    if (req.config < 0 || req.config >= kNumCfgs) return SGEMM_ERR_CONFIG;
-    if (req.sched < SGEMM_SCHED_AUTO || req.sched > SGEMM_SCHED_FIXED) return SGEMM_ERR_CONFIG;
-    if (req.sched == SGEMM_SCHED_FIXED) return plan_fixed(req, out);
-    const int cus = req.num_cus > 0 ? req.num_cus : 1;
+// Internal schedule of the automatic choice: whole tiles in full waves, the
+// remainder split (what SGEMM_SCHED_AUTO runs when it splits).
+constexpr int kSchedSplitRest = -100;
 
-    int cfg = req.config;
+// Plan of a tiled configuration (not the skinny or row-dot kernels) under
+// `sched`: SGEMM_SCHED_AUTO (the rules below), SGEMM_SCHED_DP,
+// SGEMM_SCHED_STREAMK (every tile split) or kSchedSplitRest.
+static int plan_tiled(const PlanRequest &req, int cfg, int sched, int cus, Plan *out) {
+    const int M = req.M, N = req.N, K = req.K;
     const bool aligned = req.aligned != 0, transposed = req.trans_a || req.trans_b;
-    if (cfg == SGEMM_CFG_AUTO) cfg = auto_config(req, cus, aligned);
     const CfgInfo &c = kCfgs[cfg];
-    if (c.kind == kKindSkinny) return plan_skinny(req, cus, out);
-    if (c.kind == kKindRowdot) return plan_rowdot(req, cus, occ_of(req, cfg), out);
     if (!fits(c, M, N, K, aligned, transposed)) return SGEMM_ERR_CONFIG;
 
     Plan p{};
@@ -339,14 +372,13 @@ int make_plan(const PlanRequest &req, Plan *out) {
     const int sk_per_cu = req.sk_wg_per_cu > 0 ? req.sk_wg_per_cu : 1;
     const int cap = cus * (sk_per_cu < occ ? sk_per_cu : occ);
 
-    int sched = req.sched;
     if (tiles == 0 || p.ipt == 0) sched = SGEMM_SCHED_DP;  // nothing to split
     if (sched == SGEMM_SCHED_AUTO) {
         if (tiles >= cus && tiles % cus == 0) sched = SGEMM_SCHED_DP;
         else if (tiles < cus && p.ipt < 2 * kMinSkIters) sched = SGEMM_SCHED_DP;  // too short to split
         else if (tiles > cus && tiles <= (int64_t)occ * cus && 100 * (int64_t)tiles >= 85 * (int64_t)occ * cus)
             sched = SGEMM_SCHED_DP;   // one resident wave, nearly full: every tile runs at once
-        else sched = SGEMM_SCHED_STREAMK;
+        else sched = kSchedSplitRest;
     }
 
     if (sched == SGEMM_SCHED_DP) {
@@ -359,7 +391,7 @@ int make_plan(const PlanRequest &req, Plan *out) {
         // part runs on the first sk_grid logical workgroups, each owning a
         // contiguous run of at least kMinSkIters (tile, K chunk) steps when
         // there are that many.
-        int dp = req.sched == SGEMM_SCHED_STREAMK ? 0 : (tiles / cap) * cap;
+        int dp = sched == SGEMM_SCHED_STREAMK ? 0 : (tiles / cap) * cap;
         if (dp == cap) {
             // One full wave and a remainder: split everything instead when
             // that ends sooner.  The remainder alone spreads over at most
@@ -408,6 +440,55 @@ int make_plan(const PlanRequest &req, Plan *out) {
     p.workspace_bytes = workspace_bytes(p.sk_grid, p.sk_tiles, p.bm, p.bn);
     *out = p;
     return SGEMM_OK;
+}
+
+// The automatic choice among the direct-to-LDS configurations: the plan of
+// least modelled time (plan_cost) over each configuration's data-parallel
+// and split schedules (only the one asked for when the call fixes the
+// schedule); ties go to the larger tile.
+static int plan_by_cost(const PlanRequest &req, int cus, Plan *out) {
+    static const int kTiled[] = {SGEMM_CFG_DL_256x256x16, SGEMM_CFG_DL_128x128x32, SGEMM_CFG_DL_64x64x64,
+                                 SGEMM_CFG_DL_64x64x32};
+    int scheds[2] = {SGEMM_SCHED_DP, kSchedSplitRest};
+    int n_sched = 2;
+    if (req.sched == SGEMM_SCHED_DP || req.sched == SGEMM_SCHED_STREAMK) {
+        scheds[0] = req.sched;
+        n_sched = 1;
+    }
+    bool have = false;
+    double best = 0.0;
+    for (const int cfg : kTiled) {
+        for (int i = 0; i < n_sched; ++i) {
+            Plan p;
+            if (plan_tiled(req, cfg, scheds[i], cus, &p) != SGEMM_OK) continue;
+            const double t = plan_cost(p, req.M, req.N, cus, occ_of(req, cfg));
+            if (t >= 0.0 && (!have || t < best)) {
+                best = t;
+                *out = p;
+                have = true;
+            }
+        }
+    }
+    return have ? SGEMM_OK : SGEMM_ERR_CONFIG;
+}
+
+int make_plan(const PlanRequest &req, Plan *out) {
+    const int M = req.M, N = req.N, K = req.K;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SHAPE;
+    if (req.config < 0 || req.config >= kNumCfgs) return SGEMM_ERR_CONFIG;
+    if (req.sched < SGEMM_SCHED_AUTO || req.sched > SGEMM_SCHED_FIXED) return SGEMM_ERR_CONFIG;
+    if (req.sched == SGEMM_SCHED_FIXED) return plan_fixed(req, out);
+    const int cus = req.num_cus > 0 ? req.num_cus : 1;
+
+    int cfg = req.config;
+    if (cfg == SGEMM_CFG_AUTO) {
+        cfg = auto_config(req, req.aligned != 0);
+        if (cfg == kTiledChoice) return plan_by_cost(req, cus, out);
+    }
+    const CfgInfo &c = kCfgs[cfg];
+    if (c.kind == kKindSkinny) return plan_skinny(req, cus, out);
+    if (c.kind == kKindRowdot) return plan_rowdot(req, cus, occ_of(req, cfg), out);
+    return plan_tiled(req, cfg, req.sched, cus, out);
 }
 
 }  // namespace sgemm

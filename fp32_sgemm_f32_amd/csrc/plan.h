@@ -90,6 +90,11 @@ extern const int kNumFixedShapes;
 // Returns an SGEMM_* status; fills *out on success.
 int make_plan(const PlanRequest &req, Plan *out);
 
+// Modelled kernel time (microseconds) of a plan of a direct-to-LDS
+// configuration that the automatic choice weighs (negative for any other),
+// on `cus` compute units with `occ` workgroups of it resident per CU.
+double plan_cost(const Plan &p, int M, int N, int cus, int occ);
+
 // The configurations that load tiles straight into LDS address a lane's
 // source as a 32-bit byte offset from the tile's first row (an operand stored
 // k-contiguous: A M x K, B N x K) or the chunk's first k row (stored

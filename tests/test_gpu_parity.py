@@ -935,13 +935,13 @@ def test_graph_capture_of_a_repacked_call(dev):
 # choice for narrow or ragged C: (shape, storage orders, expected
 # configuration, expected tile-row group).  Integer inputs: exact results.
 ROUTE_CASES = {
-    "col_order_3_rows_split": ((192, 8192, 512), (0, 0), "dl_64x64x64", 3),
-    "col_order_3_rows_tt": ((192, 8192, 512), (1, 1), "dl_64x64x64", 3),
+    "col_order_3_rows_split": ((192, 8192, 2048), (0, 0), "dl_64x64x64", 3),
+    "col_order_3_rows_tt": ((192, 8192, 2048), (1, 1), "dl_64x64x64", 3),
     "col_order_5_rows_32deep": ((320, 8192, 384), (0, 0), "dl_64x64x32", 5),
     "row_order_narrow_32deep": ((8192, 320, 512), (0, 0), "dl_64x64x32", 1),
     "row_order_dp_32deep": ((16384, 128, 256), (0, 1), "dl_64x64x32", 1),
-    "coverage_picks_128": ((65536, 128, 32), (0, 0), "dl_128x128x32", 1),
-    "one_wave_split_whole": ((1024, 1028, 512), (1, 0), "dl_64x64x64", None),
+    "coverage_picks_128": ((65536, 128, 256), (0, 0), "dl_128x128x32", 1),
+    "one_wave_split_whole": ((1024, 1028, 2048), (1, 0), "dl_64x64x64", None),
 }
 
 

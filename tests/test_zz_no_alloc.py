@@ -109,7 +109,7 @@ def test_noalloc_split_too_large_runs_whole_tiles(dev):
     beyond the 64 MiB array: the no-allocation call runs whole tiles
     (integer inputs, so both schedules give the exact product), then a
     smaller split call that fits reuses the array."""
-    M, N, K = 4096, 4100, 1024
+    M, N, K = 4096, 4608, 1024
     p = sg.plan(M, N, K)
     assert p["sched"] == sg.SCHED_STREAMK and p["workspace_bytes"] > sg.NOALLOC_SCRATCH_BYTES
     for i, (m, n, k) in enumerate([(M, N, K), (1000, 1028, 1024)]):
