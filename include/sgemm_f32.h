@@ -141,8 +141,10 @@ extern "C" {
  * DL_64x64x64, DL_128x128x32 and DL_256x256x16 also run shapes their tile
  * does not divide and A / B in either storage order (sgemm_f32_gemm), when
  * the stored row lengths of A and B, N and every leading dimension are
- * multiples of 4 and A, B, C are 16-byte aligned; the automatic choice
- * (SGEMM_CFG_AUTO) uses only these four and the general kernel. */
+ * multiples of 4 and A, B, C are 16-byte aligned.  The automatic choice
+ * (SGEMM_CFG_AUTO) uses these four (the one, and the schedule, of least
+ * modelled time), the skinny and row-dot kernels for thin products, and the
+ * general kernel. */
 #define SGEMM_CFG_DL_64x64x32       13 /* 256 threads, 4 waves of 32x32, 4 stages */
 #define SGEMM_CFG_DL_64x64x64_K2    14 /* 512 threads, 2 x 4 waves of 32x32, 3 stages */
 #define SGEMM_CFG_DL_128x128x32     15 /* 256 threads, 4 waves of 64x64, 3 stages */
@@ -178,7 +180,7 @@ extern "C" {
  * their tile divides. */
 
 /* Schedules. */
-#define SGEMM_SCHED_AUTO     0  /* whole tiles in full waves, Stream-K for the rest */
+#define SGEMM_SCHED_AUTO     0  /* the planner's: data-parallel, or whole tiles in full waves and the rest split */
 #define SGEMM_SCHED_DP       1  /* one workgroup per output tile, full K each */
 #define SGEMM_SCHED_STREAMK  2  /* every tile's K range split evenly over a resident grid */
 /* Data-parallel, on the automatic configuration's kernel compiled for this
