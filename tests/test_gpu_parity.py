@@ -792,6 +792,37 @@ def test_random_interface_cases(dev, seed):
     assert np.all(np.isnan(full[:, N:])), "ldc padding was written"
 
 
+# The automatic choice over shapes like those its cost model was fitted on:
+# sides log-uniform in 16..8192, multiples of 16 (of 4 one time in four),
+# every storage order, integer inputs (each partial sum is an integer below
+# 2^24, so every plan, split or whole, must give the exact product).
+@pytest.mark.parametrize("seed", range(96))
+def test_automatic_choice_random_shapes(dev, seed):
+    import math
+    import torch
+    rng = np.random.default_rng(9100 + seed)
+
+    def side():
+        q = 4 if rng.random() < 0.25 else 16
+        return max(q, int(round(math.exp(rng.uniform(math.log(16), math.log(8192))) / q)) * q)
+    while True:
+        M, N, K = side(), side(), side()
+        if 1e6 <= M * N * K <= 1e9:
+            break
+    ta, tb = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+    p = sg.plan(M, N, K, num_cus=torch.cuda.get_device_properties(dev).multi_processor_count, trans_a=ta,
+                trans_b=tb)
+    log(f"case auto random seed={seed}: shape=({M},{N},{K}) ta={ta} tb={tb} config={sg.CFG_NAMES[p['config']]} "
+        f"sched={sg.SCHED_NAMES[p['sched']]} dp={p['dp_tiles']} sk={p['sk_tiles']} repacked={p['repacked']}")
+    A, B = workloads.generate(M, N, K, "int4", 9200 + seed)
+    As, Bs = stored(A, ta), stored(B, tb)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    sg.gemm(to_dev(As, dev), to_dev(Bs, dev), C, 1.0, 0.0, ta, tb)
+    torch.cuda.synchronize()
+    C_ref, _ = oracle.gemm_blas(As, Bs, None, 1.0, 0.0, ta, tb)
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), C_ref), f"auto random {seed}"
+
+
 @pytest.mark.parametrize("views", ["a_t", "b_t", "both_t", "gemm_flip"])
 def test_python_binding_takes_transposed_views(dev, views):
     """Column-major views (X.t() of a row-major X, padded rows included) run
