@@ -121,7 +121,7 @@ class _Plan(ctypes.Structure):
         "config", "sched", "tile_m", "tile_n", "tile_k", "threads", "tiles_m", "tiles_n",
         "iters_per_tile", "dp_tiles", "sk_tiles", "grid", "sk_grid", "xcd_remap", "group_m")] + [
         ("sk_iters", ctypes.c_longlong), ("workspace_bytes", ctypes.c_longlong), ("repacked", ctypes.c_int),
-        ("transposed", ctypes.c_int), ("fixed_shape", ctypes.c_int)]
+        ("transposed", ctypes.c_int), ("fixed_shape", ctypes.c_int), ("model_us", ctypes.c_double)]
 
 
 _lib = None

@@ -620,6 +620,8 @@ static int plan_for(int ta, int tb, int M, int N, int K, int config, int sched, 
     out->sk_iters = p.sk_iters;
     out->workspace_bytes = p.workspace_bytes;
     out->fixed_shape = p.fixed ? 1 : 0;
+    const int occ = occupancy ? occupancy[p.config] : sgemm::kCfgs[p.config].default_occ;   // as make_plan reads it
+    out->model_us = sgemm::plan_cost(p, req.M, req.N, num_cus > 0 ? num_cus : 1, occ);
     return SGEMM_OK;
 }
 

@@ -333,6 +333,11 @@ typedef struct sgemm_f32_plan_t {
                             kernel, few columns with A stored K x M on the
                             skinny kernel); the fields above describe it */
     int fixed_shape;     /* 1: SGEMM_SCHED_FIXED, the kernel compiled for this product */
+    double model_us;     /* the planner's modelled kernel time (microseconds) of this plan,
+                            by which the automatic choice ranks the direct-to-LDS
+                            configurations DL_64x64x32, DL_64x64x64, DL_128x128x32
+                            and DL_256x256x16 and their schedules; -1 for any other
+                            configuration */
 } sgemm_f32_plan_t;
 
 int sgemm_f32_plan(int M, int N, int K, int config, int sched, int num_cus,

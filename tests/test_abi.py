@@ -39,8 +39,8 @@ def test_exports_match_header():
 
 def test_plan_struct_matches_header():
     """The binding's plan structure has the header's fields, in order, with
-    the same C types (int / long long), so the plan query fills it as the
-    library writes it."""
+    the same C types (int / long long / double), so the plan query fills it
+    as the library writes it."""
     import ctypes
     text = open(HEADER).read()
     body = re.search(r"typedef struct sgemm_f32_plan_t \{(.*?)\} sgemm_f32_plan_t;", text, flags=re.S).group(1)
@@ -50,9 +50,9 @@ def test_plan_struct_matches_header():
         decl = decl.strip()
         if not decl:
             continue
-        m = re.match(r"(long long|int)\s+(.*)", decl)
+        m = re.match(r"(long long|int|double)\s+(.*)", decl)
         assert m, decl
-        ctype = ctypes.c_longlong if m.group(1) == "long long" else ctypes.c_int
+        ctype = {"long long": ctypes.c_longlong, "int": ctypes.c_int, "double": ctypes.c_double}[m.group(1)]
         fields += [(name.strip(), ctype) for name in m.group(2).split(",")]
     assert [(n, t) for n, t in sg._Plan._fields_] == fields
 

@@ -9,6 +9,7 @@ numbers for many shapes and grids.
 import os
 from collections import Counter, defaultdict
 
+import numpy as np
 import pytest
 
 import fp32_sgemm_f32_amd as sg
@@ -313,6 +314,33 @@ def test_auto_choices_on_256_cus():
     assert (p["config"], p["repacked"], p["tiles_n"]) == (sg.CFG_DL_128x128x32, 1, 33)
     p = sg.plan(1000, 1001, 1000, sg.CFG_GENERIC_64x64x16, num_cus=256, occupancy=occ)   # forced: as asked
     assert (p["config"], p["repacked"]) == (sg.CFG_GENERIC_64x64x16, 0)
+
+
+def test_automatic_choice_is_the_least_modelled_time():
+    """The automatic choice's modelled time is no more than that of any
+    data-parallel plan of the four configurations it weighs (each is one of
+    its candidates); other configurations report no model (-1)."""
+    occ = OCC
+    tiled = (sg.CFG_DL_256x256x16, sg.CFG_DL_128x128x32, sg.CFG_DL_64x64x64, sg.CFG_DL_64x64x32)
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        M, N, K = (int(x) * 16 for x in rng.integers(1, 513, size=3))
+        ta, tb = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+        p = sg.plan(M, N, K, num_cus=256, occupancy=occ, trans_a=ta, trans_b=tb)
+        if p["config"] not in tiled:
+            assert p["model_us"] == -1.0
+            continue
+        assert p["model_us"] > 0
+        for cfg in tiled:
+            q = sg.plan(M, N, K, cfg, sg.SCHED_DP, num_cus=256, occupancy=occ, trans_a=ta, trans_b=tb)
+            assert q["model_us"] > 0
+            assert p["model_us"] <= q["model_us"] * (1 + 1e-12), ((M, N, K, ta, tb), cfg)
+    # More K costs more; the vector-ALU and general kernels are not modelled.
+    a = sg.plan(1024, 1024, 1024, sg.CFG_DL_64x64x64, sg.SCHED_DP, num_cus=256, occupancy=occ)["model_us"]
+    b = sg.plan(1024, 1024, 2048, sg.CFG_DL_64x64x64, sg.SCHED_DP, num_cus=256, occupancy=occ)["model_us"]
+    assert 0 < a < b
+    for cfg in (sg.CFG_VALU_128x128x8, sg.CFG_GENERIC_64x64x16, sg.CFG_MFMA_256x256x16):
+        assert sg.plan(1024, 1024, 1024, cfg, num_cus=256, occupancy=occ)["model_us"] == -1.0
 
 
 # Configurations that also run A stored K x M and / or B stored N x K.
