@@ -446,9 +446,51 @@ static int plan_tiled(const PlanRequest &req, int cfg, int sched, int cus, Plan 
 // least modelled time (plan_cost) over each configuration's data-parallel
 // and split schedules (only the one asked for when the call fixes the
 // schedule); ties go to the larger tile.
+static const int kTiled[] = {SGEMM_CFG_DL_256x256x16, SGEMM_CFG_DL_128x128x32, SGEMM_CFG_DL_64x64x64,
+                             SGEMM_CFG_DL_64x64x32};
+
+// The inputs of one automatic choice: the request's values (the occupancy of
+// the four configurations, not the pointer to it).
+struct CostKey {
+    int M, N, K, sched, cus, sk_wg_per_cu, aligned, trans_a, trans_b;
+    int occ[4];
+    bool operator==(const CostKey &o) const {
+        return M == o.M && N == o.N && K == o.K && sched == o.sched && cus == o.cus &&
+               sk_wg_per_cu == o.sk_wg_per_cu && aligned == o.aligned && trans_a == o.trans_a &&
+               trans_b == o.trans_b && occ[0] == o.occ[0] && occ[1] == o.occ[1] && occ[2] == o.occ[2] &&
+               occ[3] == o.occ[3];
+    }
+};
+
+static int plan_by_cost_uncached(const PlanRequest &req, int cus, Plan *out);
+
+// The automatic choice weighs eight plans (~0.3 us); calls that repeat a
+// shape take it from a few per-thread entries instead.
 static int plan_by_cost(const PlanRequest &req, int cus, Plan *out) {
-    static const int kTiled[] = {SGEMM_CFG_DL_256x256x16, SGEMM_CFG_DL_128x128x32, SGEMM_CFG_DL_64x64x64,
-                                 SGEMM_CFG_DL_64x64x32};
+    CostKey key{req.M, req.N, req.K, req.sched, cus, req.sk_wg_per_cu, req.aligned, req.trans_a, req.trans_b, {}};
+    for (int i = 0; i < 4; ++i) key.occ[i] = occ_of(req, kTiled[i]);
+    constexpr int kEntries = 4;
+    struct Entry {
+        bool used;
+        CostKey key;
+        Plan plan;
+    };
+    thread_local Entry cache[kEntries] = {};
+    thread_local int next = 0;
+    for (const Entry &e : cache)
+        if (e.used && e.key == key) {
+            *out = e.plan;
+            return SGEMM_OK;
+        }
+    const int st = plan_by_cost_uncached(req, cus, out);
+    if (st == SGEMM_OK) {
+        cache[next] = Entry{true, key, *out};
+        next = (next + 1) % kEntries;
+    }
+    return st;
+}
+
+static int plan_by_cost_uncached(const PlanRequest &req, int cus, Plan *out) {
     int scheds[2] = {SGEMM_SCHED_DP, kSchedSplitRest};
     int n_sched = 2;
     if (req.sched == SGEMM_SCHED_DP || req.sched == SGEMM_SCHED_STREAMK) {

@@ -343,6 +343,30 @@ def test_automatic_choice_is_the_least_modelled_time():
         assert sg.plan(1024, 1024, 1024, cfg, num_cus=256, occupancy=occ)["model_us"] == -1.0
 
 
+def test_automatic_choice_cache_is_keyed_on_the_whole_request():
+    """The per-thread cache of the automatic choice returns what the first
+    call computed for the same request, across more shapes than it holds,
+    and never a plan computed for another occupancy or CU count."""
+    occ = OCC
+    shapes = [(1000, 1028, 1024), (4224, 448, 384), (2688, 1472, 256), (1292, 1292, 1292), (131072, 64, 1024),
+              (4096, 4096, 4096), (512, 512, 512), (3072, 3072, 3072)]
+    first = {s: sg.plan(*s, num_cus=256, occupancy=occ) for s in shapes}
+    for rep in range(3):
+        for s in (shapes if rep % 2 == 0 else shapes[::-1]):
+            assert sg.plan(*s, num_cus=256, occupancy=occ) == first[s], s
+    # 1292^3: 441 64x64 tiles all resident with two workgroups per CU on the
+    # 32-deep kernel; with one, the 64-deep kernel.
+    occ1 = list(occ)
+    occ1[sg.CFG_DL_64x64x32] = 1
+    a = sg.plan(1292, 1292, 1292, num_cus=256, occupancy=occ)
+    b = sg.plan(1292, 1292, 1292, num_cus=256, occupancy=occ1)
+    assert (a["config"], b["config"]) == (sg.CFG_DL_64x64x32, sg.CFG_DL_64x64x64)
+    assert a["model_us"] < b["model_us"]
+    assert sg.plan(1292, 1292, 1292, num_cus=256, occupancy=occ) == a
+    c = sg.plan(4096, 4096, 4096, num_cus=128, occupancy=occ)
+    assert c["model_us"] > 1.9 * first[(4096, 4096, 4096)]["model_us"]
+
+
 # Configurations that also run A stored K x M and / or B stored N x K.
 LAYOUT_CFGS = EDGE_CFGS
 
