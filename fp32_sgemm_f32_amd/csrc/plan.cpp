@@ -153,7 +153,8 @@ static int auto_config(const PlanRequest &r, bool aligned) {
 // fastest candidate (geometric mean per shape), where the earlier fixed
 // rules were 3.6-15% off (worst single shape 1.18x against 3.8x, at small K,
 // where splitting tiles cost more than it balanced).  The values below are
-// the fit to all four.
+// the fit to all four; tuning/fit_cost_model.py reproduces them from the
+// sweeps' timings in tuning/plan_sweeps.csv.
 struct CostCoef {
     int cfg;
     double eff;       // fraction of the matrix-core rate in the K loop

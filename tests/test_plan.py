@@ -343,6 +343,28 @@ def test_automatic_choice_is_the_least_modelled_time():
         assert sg.plan(1024, 1024, 1024, cfg, num_cus=256, occupancy=occ)["model_us"] == -1.0
 
 
+def test_cost_model_coefficients_are_the_committed_fit():
+    """plan.cpp's cost-model coefficients are what the committed fitting
+    script computes from the committed sweep timings."""
+    import re
+    pytest.importorskip("scipy")
+    from fp32_sgemm_f32_amd.tuning import fit_cost_model as fit
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = open(os.path.join(root, "fp32_sgemm_f32_amd", "csrc", "plan.cpp")).read()
+    coef = {m.group(1): (float(m.group(2)), float(m.group(3)))
+            for m in re.finditer(r"\{SGEMM_CFG_(DL_\w+), ([0-9.e+-]+), ([0-9.e+-]+)\}", src)}
+    const = {m.group(1): float(m.group(2))
+             for m in re.finditer(r"constexpr double (k\w+) = ([0-9.e+-]+);", src)}
+    th = fit.fit(fit.load(os.path.join(root, "fp32_sgemm_f32_amd", "tuning", "plan_sweeps.csv")))
+    for i, name in enumerate(fit.NAMES):
+        eff, tile = coef["DL_" + name[3:]]   # dl_256x256x16 -> SGEMM_CFG_DL_256x256x16
+        assert eff == pytest.approx(th[i], rel=1e-3) and tile == pytest.approx(th[4 + i], rel=1e-3), name
+    assert const["kSumLaunchUs"] == pytest.approx(th[9], rel=1e-3)
+    assert const["kSumBytesPerUs"] == pytest.approx(th[10], rel=1e-3)
+    assert const["kStoreBytesPerUs"] == pytest.approx(th[11], rel=1e-3)
+    assert const["kNarrowEff64x64x32"] == pytest.approx(th[12], rel=1e-3)
+
+
 def test_automatic_choice_cache_is_keyed_on_the_whole_request():
     """The per-thread cache of the automatic choice returns what the first
     call computed for the same request, across more shapes than it holds,
