@@ -183,6 +183,11 @@ struct GroupOps<false, F> {
 // (sliced K): with one tile per CU the SIMDs then hold two waves each, one
 // issuing MFMAs while the other waits; the groups' sums are added through
 // LDS at the end of the tile.
+// WS gives every MFMA wave a partner wave that only loads: it issues all of
+// a chunk's LDS-DMA loads at the chunk's start and waits for them, and the
+// MFMA waves only read LDS and multiply (two waves per SIMD).  Measured on
+// the 128x128 tiles: +0.7% at 2048^3 and 2048x4096x2048 (alternating rounds,
+// identical results); level on the 64x64 tiles, which keep one wave.
 // EDGE: the shape need not be a multiple of the tile (the contiguous extent
 // of each operand, and N, multiples of 4): loads through buffer resources
 // with rows / columns / k beyond the matrix masked to zeros, stores masked.
@@ -190,7 +195,7 @@ struct GroupOps<false, F> {
 // SH: the launch geometry, from the arguments or fixed at compile time for
 // one product (gemm_common.h).
 template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int S_, int KSPLIT = 1, int LA_ = 1,
-          bool EDGE = false, bool TA = false, bool TB = false, class SH = RuntimeShape>
+          bool EDGE = false, bool TA = false, bool TB = false, class SH = RuntimeShape, bool WS = false>
 struct MfmaDlCore {
     using Shape = SH;
     static constexpr bool kEdge = EDGE;
@@ -198,8 +203,8 @@ struct MfmaDlCore {
     static constexpr int LA = LA_;                  // groups of operand reads ahead of the MFMAs
     static constexpr int NS = LA == 1 ? 2 : 4;      // operand register sets
     static constexpr int NW_MN = WAVES_M * WAVES_N;   // waves per K group
-    static constexpr int NW = NW_MN * KSPLIT;
-    static constexpr int NT = 64 * NW;
+    static constexpr int NW = NW_MN * KSPLIT;           // waves that issue MFMAs
+    static constexpr int NT = 64 * NW * (WS ? 2 : 1);   // WS: as many more that only load
     static constexpr int NT_MN = 64 * NW_MN;          // threads holding the result
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -233,6 +238,9 @@ struct MfmaDlCore {
     static_assert(LDS_FLOATS * 4 + 16 <= 160 * 1024, "LDS budget");
     static_assert(KSPLIT == 1 || TILE_FLOATS <= LDS_FLOATS, "room to add the K groups' sums");
     static_assert(!SH::kFixed || (!EDGE && !TA && !TB), "a compile-time shape: whole tiles, A M x K, B K x N");
+    static_assert(!WS || KSPLIT == 1, "load waves with one K group");
+    // Roles of a wave: both (not WS), or, with WS, MFMA waves and load waves.
+    static constexpr int kBoth = 0, kMath = 1, kLoad = 2;
 
     floatx16 acc[FM][FN];
     int tiles_started = 0;   // uniform: tiles (or split ranges) this workgroup has begun
@@ -285,6 +293,7 @@ struct MfmaDlCore {
         uint32_t rb[S][BKC ? FN : 1][BKC ? G : 1];
         uint32_t lds;            // uniform: LDS byte address of the ring
         int wave;
+        int dwave;               // uniform: this wave's index among the waves that load
     };
 
     // Source byte offset of this lane's 16 bytes in DMA block blk of an
@@ -319,17 +328,18 @@ struct MfmaDlCore {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        g.dwave = WS ? g.wave % NW : g.wave;
         // EDGE: valid k values in the tile's last chunk (a k-contiguous
         // operand needs K a multiple of 4, so its quads are all in or out).
         const int kt = EDGE ? a.K - (SH::ipt(a) - 1) * BK : BK;
         const int m_lim = a.M - tm * BM, n_lim = a.N - tn * BN;
 #pragma unroll
         for (int u = 0; u < A_PW; ++u)
-            dma_lane<AKC, BM>(g.wave + NW * u, lane, SH::lda(a), m_lim, kt, [](int r) { return r; }, g.va[u],
+            dma_lane<AKC, BM>(g.dwave + NW * u, lane, SH::lda(a), m_lim, kt, [](int r) { return r; }, g.va[u],
                               g.va_t[u]);
 #pragma unroll
         for (int u = 0; u < B_PW; ++u)
-            dma_lane<BKC, BN>(g.wave + NW * u, lane, SH::ldb(a), n_lim, kt, [](int r) { return b_kc_col(r); }, g.vb[u],
+            dma_lane<BKC, BN>(g.dwave + NW * u, lane, SH::ldb(a), n_lim, kt, [](int r) { return b_kc_col(r); }, g.vb[u],
                               g.vb_t[u]);
         if constexpr (AKC) {
             g.ga = (const char *)(a.A + (int64_t)tm * BM * SH::lda(a) + (int64_t)k0 * BK);
@@ -387,7 +397,7 @@ struct MfmaDlCore {
     template <int ST>
     __device__ __forceinline__ static void issue_one(const Geo &g, int d) {
         const uint32_t m0 = g.lds + 4 * (ST * STAGE + (d < A_PW ? 0 : A_STAGE) +
-                                         (g.wave + NW * (d < A_PW ? d : d - A_PW)) * 256);
+                                         (g.dwave + NW * (d < A_PW ? d : d - A_PW)) * 256);
         if constexpr (EDGE) {
             if (d < A_PW) bdma16(g.rsa, g.va[d], m0);
             else bdma16(g.rsb, g.vb[d - A_PW], m0);
@@ -481,7 +491,11 @@ struct MfmaDlCore {
     //     after them.  Issuing an LDS-DMA load holds the wave for a few dozen
     //     cycles; behind the operand reads in one MFMA's shadow it delayed
     //     the next dependent MFMA (3% at one wave per SIMD).
-    template <int ST, int Q>
+    // Loads in flight at a load wave's barrier (WS): S-3 whole chunks and
+    // chunk c+S-1, issued whole at the start of chunk c.
+    static constexpr int VM_AT_BARRIER_LOAD = L * (S - 2);
+
+    template <int ROLE, int ST, int Q>
     __device__ __forceinline__ void group(Geo &g, int c, int nch, int tail_ch, AOps (&av)[NS], BOps (&bv)[NS]) {
         // Whether this chunk still loads (c <= nch - S), computed afresh in a
         // scalar register at every test: one boolean shared by the group's
@@ -490,6 +504,27 @@ struct MfmaDlCore {
 #define SGEMM_DL_STEADY (steady_now(c, nch) != 0)
         constexpr int cs = Q % NS, TQ = Q + LA, ts = TQ % NS;
         constexpr int NXT = (ST + 1) % S, PRV = (ST + S - 1) % S;
+        if constexpr (ROLE == kLoad) {
+            // A load wave: the whole of chunk c+S-1 at the chunk's start,
+            // then, in the group of the chunk's barrier, the wait for chunk
+            // c+1 and the barrier, the same one the MFMA waves reach.
+            if constexpr (Q == 0) {
+                if (SGEMM_DL_STEADY) {
+                    if constexpr (EDGE) {
+                        if (scalar_eq(c + S - 1, tail_ch)) mask_k_tail(g);
+                    }
+#pragma unroll
+                    for (int d = 0; d < L; ++d) issue_one<PRV>(g, d);
+                    advance(g);
+                }
+            }
+            if constexpr (TQ == G) {
+                if (SGEMM_DL_STEADY) wait_counts<VM_AT_BARRIER_LOAD, 0>();
+                else wait_counts<0, 0>();
+                lds_barrier();
+            }
+            return;
+        }
         wait_counts<63, (LA - 1) * R>();
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(av[cs], bv[cs], 0);
@@ -507,24 +542,28 @@ struct MfmaDlCore {
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(av[cs], bv[cs], 1);
         __builtin_amdgcn_sched_barrier(0);
-        if (SGEMM_DL_STEADY) {
-            if constexpr (EDGE && Q == 0) {
-                if (scalar_eq(c + S - 1, tail_ch)) mask_k_tail(g);
+        if constexpr (ROLE == kBoth) {
+            if (SGEMM_DL_STEADY) {
+                if constexpr (EDGE && Q == 0) {
+                    if (scalar_eq(c + S - 1, tail_ch)) mask_k_tail(g);
+                }
+                dma_slot<PRV, Q, 0>(g);
             }
-            dma_slot<PRV, Q, 0>(g);
         }
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(av[cs], bv[cs], 2);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (dma_lo(Q + 1) - dma_lo(Q) > 1) {
+        if constexpr (ROLE == kBoth && dma_lo(Q + 1) - dma_lo(Q) > 1) {
             if (SGEMM_DL_STEADY) dma_slot<PRV, Q, 1>(g);
         }
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(av[cs], bv[cs], 3);
         __builtin_amdgcn_sched_barrier(0);
-        if (SGEMM_DL_STEADY) {
-            if constexpr (dma_lo(Q + 1) - dma_lo(Q) > 2) dma_slot<PRV, Q, 2>(g);
-            if constexpr (Q == G - 1) advance(g);
+        if constexpr (ROLE == kBoth) {
+            if (SGEMM_DL_STEADY) {
+                if constexpr (dma_lo(Q + 1) - dma_lo(Q) > 2) dma_slot<PRV, Q, 2>(g);
+                if constexpr (Q == G - 1) advance(g);
+            }
         }
 #undef SGEMM_DL_STEADY
         __builtin_amdgcn_sched_barrier(0);
@@ -540,20 +579,20 @@ struct MfmaDlCore {
             if ((d - dma_lo(Q)) % 3 == SLOT) issue_one<PRV>(g, d);
     }
 
-    template <int ST, int... Qs>
+    template <int ROLE, int ST, int... Qs>
     __device__ __forceinline__ void chunk_groups(std::integer_sequence<int, Qs...>, Geo &g, int c, int nch,
                                                  int tail_ch, AOps (&av)[NS], BOps (&bv)[NS]) {
-        (group<ST, Qs>(g, c, nch, tail_ch, av, bv), ...);
+        (group<ROLE, ST, Qs>(g, c, nch, tail_ch, av, bv), ...);
     }
 
     // Chunks ST, ST+1, ... of the ring from chunk c on; true once chunk
     // nch-1 is done.  Chunk c loads chunk c+S-1 while c <= nch-S.
-    template <int ST>
+    template <int ROLE, int ST>
     __device__ __forceinline__ bool chunks_from(int &c, int nch, int tail_ch, Geo &g, AOps (&av)[NS],
                                                 BOps (&bv)[NS]) {
-        chunk_groups<ST>(std::make_integer_sequence<int, G>{}, g, c, nch, tail_ch, av, bv);
+        chunk_groups<ROLE, ST>(std::make_integer_sequence<int, G>{}, g, c, nch, tail_ch, av, bv);
         if (++c >= nch) return true;
-        if constexpr (ST + 1 < S) return chunks_from<ST + 1>(c, nch, tail_ch, g, av, bv);
+        if constexpr (ST + 1 < S) return chunks_from<ROLE, ST + 1>(c, nch, tail_ch, g, av, bv);
         else return false;
     }
 
@@ -573,6 +612,19 @@ struct MfmaDlCore {
     }
 
     __device__ __forceinline__ void mainloop(const KernelArgs &a, float *lds, int tm, int tn, int k0, int k1) {
+        if constexpr (WS) {
+            if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= NW) mainloop_role<kLoad>(a, lds, tm, tn, k0, k1);
+            else mainloop_role<kMath>(a, lds, tm, tn, k0, k1);
+        } else {
+            mainloop_role<kBoth>(a, lds, tm, tn, k0, k1);
+        }
+    }
+
+    // One role's part of the tile's K range.  Every barrier of it is in code
+    // the roles share (the ring's start, one per chunk, one per later tile),
+    // so the waves of a workgroup meet the same barriers in the same order.
+    template <int ROLE>
+    __device__ __forceinline__ void mainloop_role(const KernelArgs &a, float *lds, int tm, int tn, int k0, int k1) {
         Geo g;
         setup(g, a, lds, tm, tn, k0);
         int nch = k1 - k0;
@@ -597,26 +649,30 @@ struct MfmaDlCore {
         }
         // Chunks 0 .. S-2 up front (stage = chunk); chunk c+S-1 is loaded
         // during chunk c.
-        issue_prologue<0>(g, nch, tail_ch);
+        if constexpr (ROLE != kMath) issue_prologue<0>(g, nch, tail_ch);
         if (nch >= S - 1) wait_counts<L * (S - 2), 0>();
         else wait_counts<0, 0>();
         lds_barrier();
 
         AOps av[NS];
         BOps bv[NS];
-        read_group<0, 0>(g, av[0], bv[0]);
-        if constexpr (LA == 2) read_group<0, 1>(g, av[1], bv[1]);
+        if constexpr (ROLE != kLoad) {
+            read_group<0, 0>(g, av[0], bv[0]);
+            if constexpr (LA == 2) read_group<0, 1>(g, av[1], bv[1]);
+        }
 
         int c = 0;
-        while (!chunks_from<0>(c, nch, tail_ch, g, av, bv)) {
+        while (!chunks_from<ROLE, 0>(c, nch, tail_ch, g, av, bv)) {
         }
         // The last groups read operands of a chunk that does not exist; the
         // registers must not be reused before those reads have returned.
         wait_counts<0, 0>();
+        if constexpr (ROLE != kLoad) {
 #pragma unroll
-        for (int v = 0; v < NS; ++v) {
-            av[v].keep();
-            bv[v].keep();
+            for (int v = 0; v < NS; ++v) {
+                av[v].keep();
+                bv[v].keep();
+            }
         }
 
         if constexpr (KSPLIT == 2) {
@@ -655,7 +711,7 @@ struct MfmaDlCore {
     // adjacent columns are all in or all out).
     __device__ __forceinline__ void store_c(const KernelArgs &a, int tm, int tn) {
         const int tid = threadIdx.x;
-        if (KSPLIT > 1 && tid >= NT_MN) return;
+        if ((KSPLIT > 1 || WS) && tid >= NT_MN) return;
         const int wave = tid >> 6, lane = tid & 63;
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
         const int lr = lane & 31, lh = lane >> 5;
@@ -705,7 +761,7 @@ struct MfmaDlCore {
     // partial sum; whole tile, no masking, no epilogue).
     __device__ __forceinline__ void store_tile(float *p) {
         const int tid = threadIdx.x;
-        if (KSPLIT > 1 && tid >= NT_MN) return;
+        if ((KSPLIT > 1 || WS) && tid >= NT_MN) return;
         const int wave = tid >> 6, lane = tid & 63;
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
         const int lr = lane & 31, lh = lane >> 5;
@@ -747,7 +803,7 @@ __global__ __launch_bounds__(Core::NT) void sgemm_mfma_dl_kernel(KernelArgs a) {
 
 using Dl64x64x32 = MfmaDlCore<64, 64, 32, 2, 2, 4, 1, 2>;
 using Dl64x64x64K2 = MfmaDlCore<64, 64, 64, 2, 2, 3, 2, 2>;
-using Dl128x128x32 = MfmaDlCore<128, 128, 32, 2, 2, 3, 1, 2>;
+using Dl128x128x32 = MfmaDlCore<128, 128, 32, 2, 2, 3, 1, 2, false, false, false, RuntimeShape, true>;
 using Dl256x256x16 = MfmaDlCore<256, 256, 16, 4, 2, 3>;
 using Dl64x64x32K2 = MfmaDlCore<64, 64, 32, 2, 2, 4, 2>;
 using Dl128x128x32K2 = MfmaDlCore<128, 128, 32, 2, 2, 3, 2>;
@@ -757,18 +813,18 @@ using Dl256x128x16 = MfmaDlCore<256, 128, 16, 2, 2, 3>;
 // The configurations the automatic choice uses, for each storage order of A
 // and B (NN, TN, NT, TT): whole-tile variants (the NN one is defined above)
 // and edge-masking ones.
-#define SGEMM_DL_LAYOUT_CORES(name, BM, BN, BK, WM, WN, S, KS, LA)                  \
-    using name##TN = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, false, true>;        \
-    using name##NT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, false, false, true>; \
-    using name##TT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, false, true, true>;  \
-    using name##E = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true>;                \
-    using name##ETN = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, true>;        \
-    using name##ENT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, false, true>; \
-    using name##ETT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, true, true>;
-SGEMM_DL_LAYOUT_CORES(Dl64x64x32, 64, 64, 32, 2, 2, 4, 1, 2)
-SGEMM_DL_LAYOUT_CORES(Dl64x64x64, 64, 64, 64, 2, 2, 3, 1, 2)
-SGEMM_DL_LAYOUT_CORES(Dl128x128x32, 128, 128, 32, 2, 2, 3, 1, 2)
-SGEMM_DL_LAYOUT_CORES(Dl256x256x16, 256, 256, 16, 4, 2, 3, 1, 1)
+#define SGEMM_DL_LAYOUT_CORES(name, BM, BN, BK, WM, WN, S, KS, LA, WS)                                  \
+    using name##TN = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, false, true, false, RuntimeShape, WS>;  \
+    using name##NT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, false, false, true, RuntimeShape, WS>;  \
+    using name##TT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, false, true, true, RuntimeShape, WS>;   \
+    using name##E = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, false, false, RuntimeShape, WS>;   \
+    using name##ETN = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, true, false, RuntimeShape, WS>;  \
+    using name##ENT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, false, true, RuntimeShape, WS>;  \
+    using name##ETT = MfmaDlCore<BM, BN, BK, WM, WN, S, KS, LA, true, true, true, RuntimeShape, WS>;
+SGEMM_DL_LAYOUT_CORES(Dl64x64x32, 64, 64, 32, 2, 2, 4, 1, 2, false)
+SGEMM_DL_LAYOUT_CORES(Dl64x64x64, 64, 64, 64, 2, 2, 3, 1, 2, false)
+SGEMM_DL_LAYOUT_CORES(Dl128x128x32, 128, 128, 32, 2, 2, 3, 1, 2, true)
+SGEMM_DL_LAYOUT_CORES(Dl256x256x16, 256, 256, 16, 4, 2, 3, 1, 1, false)
 #undef SGEMM_DL_LAYOUT_CORES
 
 // Kernels compiled for one product each (SGEMM_SCHED_FIXED): the automatic
@@ -777,7 +833,7 @@ SGEMM_DL_LAYOUT_CORES(Dl256x256x16, 256, 256, 16, 4, 2, 3, 1, 1)
 using DlFixed4096 = MfmaDlCore<256, 256, 16, 4, 2, 3, 1, 1, false, false, false,
                                FixedShape<4096, 4096, 4096, 256, 256, 16, 4>>;
 using DlFixed2048 = MfmaDlCore<128, 128, 32, 2, 2, 3, 1, 2, false, false, false,
-                               FixedShape<2048, 2048, 2048, 128, 128, 32, 4>>;
+                               FixedShape<2048, 2048, 2048, 128, 128, 32, 4>, true>;
 using DlFixed1024 = MfmaDlCore<64, 64, 64, 2, 2, 3, 1, 2, false, false, false,
                                FixedShape<1024, 1024, 1024, 64, 64, 64, 4>>;
 using DlFixed1024x16384 = MfmaDlCore<64, 64, 64, 2, 2, 3, 1, 2, false, false, false,

@@ -30,7 +30,7 @@ const CfgInfo kCfgs[] = {
     {SGEMM_CFG_MFMA_64x64x128, 64, 64, 128, 256, kKindMfma, 1, false, false, "mfma_64x64x128"},
     {SGEMM_CFG_DL_64x64x32, 64, 64, 32, 256, kKindMfmaDl, 2, true, true, "dl_64x64x32"},
     {SGEMM_CFG_DL_64x64x64_K2, 64, 64, 64, 512, kKindMfmaDl, 1, false, false, "dl_64x64x64_k2"},
-    {SGEMM_CFG_DL_128x128x32, 128, 128, 32, 256, kKindMfmaDl, 1, true, true, "dl_128x128x32"},
+    {SGEMM_CFG_DL_128x128x32, 128, 128, 32, 512, kKindMfmaDl, 1, true, true, "dl_128x128x32"},
     {SGEMM_CFG_DL_256x256x16, 256, 256, 16, 512, kKindMfmaDl, 1, true, true, "dl_256x256x16"},
     {SGEMM_CFG_DL_64x64x32_K2, 64, 64, 32, 512, kKindMfmaDl, 2, false, false, "dl_64x64x32_k2"},
     {SGEMM_CFG_DL_128x128x32_K2, 128, 128, 32, 512, kKindMfmaDl, 1, false, false, "dl_128x128x32_k2"},

@@ -147,7 +147,7 @@ extern "C" {
  * general kernel. */
 #define SGEMM_CFG_DL_64x64x32       13 /* 256 threads, 4 waves of 32x32, 4 stages */
 #define SGEMM_CFG_DL_64x64x64_K2    14 /* 512 threads, 2 x 4 waves of 32x32, 3 stages */
-#define SGEMM_CFG_DL_128x128x32     15 /* 256 threads, 4 waves of 64x64, 3 stages */
+#define SGEMM_CFG_DL_128x128x32     15 /* 512 threads, 4 waves of 64x64 and 4 that load, 3 stages */
 #define SGEMM_CFG_DL_256x256x16     16 /* 512 threads, 8 waves of 64x128, 3 stages */
 #define SGEMM_CFG_DL_64x64x32_K2    17 /* 512 threads, 2 x 4 waves of 32x32, 4 stages */
 #define SGEMM_CFG_DL_128x128x32_K2  18 /* 512 threads, 2 x 4 waves of 64x64, 3 stages */
