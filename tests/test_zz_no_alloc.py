@@ -141,6 +141,71 @@ def test_noalloc_refuses_copies_beyond_the_array(dev):
     assert np.array_equal(noalloc.astype(np.float64), exact)
 
 
+# Seeded sweep: (seed, draws, smallest and largest side, most multiply-adds).
+NOALLOC_SWEEPS = {"small": (21, 400, 1, 4096, 4e9), "large": (23, 150, 128, 8192, 2e10)}
+
+
+def noalloc_draws(seed, count, lo, hi, max_macs):
+    """Random products (host only): shape (any side, or multiples of 4, 16 or
+    64), storage orders, a padded ldc now and then, alpha and beta."""
+    import math
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        def side():
+            v = int(math.exp(rng.uniform(math.log(lo), math.log(hi))))
+            q = int(rng.choice([1, 4, 16, 64]))
+            return max(1, v // q * q)
+        M, N, K = side(), side(), side()
+        if M * N * K > max_macs:
+            continue
+        out.append((M, N, K, int(rng.integers(2)), int(rng.integers(2)), int(rng.choice([0, 0, 3, 8])),
+                    float(rng.choice([1.0, 2.0, -1.0])), float(rng.choice([0.0, 0.0, 1.0, -2.0])),
+                    int(rng.integers(2 ** 31))))
+    return out
+
+
+@pytest.mark.parametrize("name", list(NOALLOC_SWEEPS))
+def test_noalloc_integer_sweep(dev, name):
+    """Random products through sgemm_f32_gemm_noalloc on integer inputs in
+    {-4..4}: every partial sum is an integer below 2^24 (K < 2^19), so the
+    result must equal the exact product (float64 matmul on the device) bit
+    for bit, whatever plan the call ran.  A call whose repacked copies exceed
+    the scratch array must be refused with SGEMM_ERR_SCRATCH and leave C as
+    it was."""
+    import torch
+    seed, count, lo, hi, max_macs = NOALLOC_SWEEPS[name]
+    ran = refused = 0
+    for i, (M, N, K, ta, tb, pad, alpha, beta, s) in enumerate(noalloc_draws(seed, count, lo, hi, max_macs)):
+        assert 2 * 16 * K + 8 < 2 ** 24
+        g = np.random.default_rng(s)
+        As = g.integers(-4, 5, size=(K, M) if ta else (M, K)).astype(np.float32)
+        Bs = g.integers(-4, 5, size=(N, K) if tb else (K, N)).astype(np.float32)
+        C0 = g.integers(-4, 5, size=(M, N)).astype(np.float32)
+        log(f"noalloc sweep {name} #{i}: ({M},{N},{K}) ta={ta} tb={tb} ldc={N + pad} alpha={alpha} beta={beta}")
+        Ad, Bd = torch.from_numpy(As).to(dev), torch.from_numpy(Bs).to(dev)
+        Cbuf = torch.full((M, N + pad), float("nan"), dtype=torch.float32, device=dev)
+        Cbuf[:, :N] = torch.from_numpy(C0).to(dev)
+        st = sg.gemm_noalloc_raw(ta, tb, M, N, K, alpha, Ad.data_ptr(), As.shape[1], Bd.data_ptr(), Bs.shape[1],
+                                 beta, Cbuf.data_ptr(), N + pad, torch.cuda.current_stream(dev).cuda_stream)
+        torch.cuda.synchronize()
+        C = Cbuf.cpu().numpy()
+        assert np.all(np.isnan(C[:, N:])), "ldc padding was written"
+        if st == sg.ERR_SCRATCH:
+            assert np.array_equal(C[:, :N], C0), "a refused call wrote C"
+            refused += 1
+            continue
+        assert st == sg.OK, (st, sg.status_string(st))
+        opA = Ad.t() if ta else Ad
+        opB = Bd.t() if tb else Bd
+        ref = (alpha * (opA.double() @ opB.double()) + beta * torch.from_numpy(C0).to(dev).double()).cpu().numpy()
+        wrong = int(np.sum(C[:, :N].astype(np.float64) != ref))
+        assert wrong == 0, f"#{i}: {wrong} elements differ from the exact product"
+        ran += 1
+    log(f"noalloc sweep {name}: {ran} ran, {refused} refused (scratch), all exact")
+    assert ran >= count // 2
+
+
 def test_noalloc_calls_from_two_threads_on_one_stream(dev):
     """Two host threads make no-allocation calls on ONE stream with no host
     synchronisation: repacked products (copies in the shared scratch array)
